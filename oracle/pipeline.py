@@ -1,0 +1,66 @@
+"""End-to-end oracle of the online path: rotate+quant, weight prep, W4A4, KV.
+
+* Activations ("QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs",
+  paper-graph-ui summary, section 3.4 Stage 1b and Stage 2b): rotate each
+  token by R, then per-token symmetric INT4, then pack.
+* Weights (same page, Stage 1a "fuse Q into the weights" and Stage 2a; "QuaRot
+  Guide", step 1 of "Deep Dive"): the same R is applied to each output
+  channel's row of W [n_out x d] (W~ = W R^T), so X~ W~^T = X W^T; then one
+  symmetric scale per output channel (max/7, round to nearest) and pack.
+* KV cache (same page, Stage 1d "online head-wise rotation after RoPE" and
+  Stage 2c; "QuaRot Guide", step 4 of "Deep Dive"): each (batch, head,
+  position) vector of head_dim values is rotated by the head-wise Hadamard and
+  quantised as one group.  This module implements the symmetric per-group
+  variant (fp16 scale, no zero point).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .gemm import w4a4_reference
+from .quant import pack_int4, quantize_rows
+from .rotate import rotate_rows
+
+__all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant"]
+
+
+def had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0):
+    """Rotate+quant rows of x.
+
+    Returns dict(x_rot float64, codes int8, packed uint8 [rows x d/2], scales fp16).
+    """
+    x_rot = rotate_rows(x, signs, m)
+    codes, scales = quantize_rows(x_rot, clip_ratio)
+    return {"x_rot": x_rot, "codes": codes, "packed": pack_int4(codes), "scales": scales}
+
+
+def prep_weights(w: np.ndarray, signs: np.ndarray, m: int = 1):
+    """Offline weight prep: W~ = W R^T, per-output-channel max/7 RTN, pack."""
+    return had_quant(w, signs, m, clip_ratio=1.0)
+
+
+def w4a4_linear(x: np.ndarray, w: np.ndarray, signs: np.ndarray, m: int = 1,
+                clip_ratio: float = 1.0):
+    """The whole quantised linear layer: returns acts, weights, acc and y."""
+    a = had_quant(x, signs, m, clip_ratio)
+    b = prep_weights(w, signs, m)
+    acc, y = w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
+    return {"act": a, "wgt": b, "acc": acc, "y": y}
+
+
+def kv_had_quant(t: np.ndarray, signs: np.ndarray, clip_ratio: float = 1.0):
+    """Symmetric per-(b, h, s) group quantisation of a [B, H, S, D] tensor.
+
+    Returns dict(x_rot [B,H,S,D] float64, codes int8, packed uint8 [B,H,S,D/2],
+    scales fp16 [B,H,S]).
+    """
+    t = np.asarray(t)
+    b, h, s, d = t.shape
+    r = had_quant(t.reshape(-1, d), signs, 1, clip_ratio)
+    return {
+        "x_rot": r["x_rot"].reshape(b, h, s, d),
+        "codes": r["codes"].reshape(b, h, s, d),
+        "packed": r["packed"].reshape(b, h, s, d // 2),
+        "scales": r["scales"].reshape(b, h, s),
+    }
