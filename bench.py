@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated W4A4 hot path on one MI355X.
+
+One step = one pass of the online path over one batch of synthetic input:
+rotate+quant of the activations X (fused randomized Hadamard + per-token INT4,
+``quarot_had_quant``) followed by the W4A4 GEMM with dequant
+(``quarot_w4a4_gemm``) against weights prepared offline (untimed) by the same
+rotate+quant kernel.  Default workload: X fp16 [2048 x 4096] with 0.1%
+outlier channels, random-sign H_4096, W int4 [4096 x 4096].
+
+Inputs are resident in HBM before timing starts.  To keep the 256 MB
+Infinity Cache from serving repeated reads, the step cycles over enough
+independent buffer sets (inputs, weights and outputs) to exceed 1 GiB.
+
+Prints ONE JSON line:
+  value            rotate+quant algorithmic GB/s (fp16 read + int4 codes and
+                   fp16 scales written), from HIP events around that kernel
+  value_gemm_tops  GEMM algorithmic TOPS (2 M N K per launch)
+  roofline         the dominant kernel (the GEMM) against INT8 MFMA peak
+  roofline_rotate_quant  rotate+quant against HBM peak
+  cpu_baseline     the CPU oracle timed on this host on the same workload
+Extra workloads for profiling: --workload NAME, --kv (the K/V cache write).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+CACHE_DEFEAT_BYTES = 1 << 30
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama7b_proj", choices=sorted(workloads.ACT_CONFIGS))
+    p.add_argument("--kv", action="store_true", help="benchmark the K/V cache write instead")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for 1 GiB)")
+    return p.parse_args()
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline_act(cfg, inp) -> dict:
+    """The oracle, as it stands, on the full step of this workload."""
+    import oracle
+
+    t0 = time.perf_counter()
+    a = oracle.had_quant(inp["x"], inp["signs"], cfg.m)
+    t1 = time.perf_counter()
+    b = oracle.prep_weights(inp["w"], inp["signs"], cfg.m)  # offline, not counted
+    t2 = time.perf_counter()
+    acc, y = oracle.w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
+    t3 = time.perf_counter()
+    T, d, N = inp["x"].shape[0], cfg.d, inp["w"].shape[0]
+    rq_bytes = 2 * T * d + T * d // 2 + 2 * T
+    return {
+        "value": rq_bytes / (t1 - t0) / 1e9,
+        "unit": "GB/s",
+        "gemm_tops": 2.0 * T * N * d / (t3 - t2) / 1e12,
+        "seconds_rotate_quant": t1 - t0,
+        "seconds_gemm_dequant": t3 - t2,
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"full {cfg.name} step: rotate+quant of X [{T} x {d}] (float64 dense "
+                  f"factored rotation) and the exact integer GEMM [{T} x {N} x {d}] + dequant "
+                  f"(float64 BLAS); weight prep excluded",
+    }
+
+
+def bench_act(args, torch, qr) -> dict:
+    cfg = workloads.ACT_CONFIGS[args.workload]
+    log(f"workload {cfg.name}: generating inputs")
+    inp = workloads.make_act_inputs(cfg)
+    T, d, N = inp["x"].shape[0], cfg.d, inp["w"].shape[0]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    signs = dev(inp["signs"])
+    x0 = dev(inp["x"])
+    w0 = dev(inp["w"])
+    # offline weight prep (same kernel, untimed)
+    qw0, sw0 = qr.had_quant(w0, signs, cfg.m)
+    del w0
+    per_set = T * d * 2 + T * d // 2 + 2 * T + N * d // 2 + 2 * N + T * N * 2
+    nsets = args.sets or max(1, -(-CACHE_DEFEAT_BYTES // per_set))
+    log(f"{nsets} buffer sets of {per_set / 2**20:.1f} MiB")
+    sets = []
+    for _ in range(nsets):
+        sets.append({
+            "x": x0.clone(),
+            "qx": torch.empty((T, d // 2), dtype=torch.uint8, device="cuda"),
+            "sx": torch.empty((T,), dtype=torch.float16, device="cuda"),
+            "qw": qw0.clone(),
+            "sw": sw0.clone(),
+            "y": torch.empty((T, N), dtype=torch.float16, device="cuda"),
+        })
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        qr.w4a4_gemm(s["qx"], s["sx"], s["qw"], s["sw"], d, out=s["y"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    rq_bytes = 2 * T * d + T * d // 2 + 2 * T
+    gemm_ops = 2.0 * T * N * d
+    rq_gbs = rq_bytes / (rq_ms * 1e-3) / 1e9
+    tops = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    log(f"rotate+quant {rq_ms * 1e3:.2f} us ({rq_gbs:.0f} GB/s); gemm {gemm_ms * 1e3:.2f} us "
+        f"({tops:.0f} TOPS); wall/step {wall / args.steps * 1e3:.4f} ms")
+    out = {
+        "metric": "rotate+quant GB/s (% HBM peak); W4A4 GEMM TOPS (% INT8 MFMA peak)",
+        "value": round(rq_gbs, 2),
+        "unit": "GB/s",
+        "value_gemm_tops": round(tops, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 rotate / int8 MFMA (int4 codes, int32 acc)",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: X fp16 [{T} x {d}] with {cfg.outlier_count} outlier "
+                        f"channels, rotation H_{d // cfg.m}" + (f" (x) H_{cfg.m}" if cfg.m > 1 else "")
+                        + f" with random signs, W int4 [{N} x {d}], Y fp16 [{T} x {N}]",
+            "tokens": T, "d": d, "n_out": N, "buffer_sets": nsets,
+        },
+        "kernels_us": {"had_quant": round(rq_ms * 1e3, 3), "w4a4_gemm": round(gemm_ms * 1e3, 3)},
+        "roofline": {
+            "kernel": "w4a4_gemm",
+            "bound": "mfma",
+            "achieved": round(tops, 2),
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tops / INT8_PEAK_TOPS, 4),
+            "traffic": None,
+            "note": "integer ops (TOPS) against the dense INT8 MFMA peak; 2*M*N*K per launch",
+        },
+        "roofline_rotate_quant": {
+            "kernel": "had_quant",
+            "bound": "hbm",
+            "achieved": round(rq_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": rq_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (baseline)")
+        out["cpu_baseline"] = cpu_baseline_act(cfg, inp)
+    return out
+
+
+def bench_kv(args, torch, qr) -> dict:
+    cfg = workloads.KV_CONFIG
+    log(f"kv workload {cfg.name}: generating inputs")
+    inp = workloads.make_kv_inputs(cfg)
+    B, H, S, D = inp["k"].shape
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    signs = dev(inp["signs"])
+    k0, v0 = dev(inp["k"]), dev(inp["v"])
+    per_set = 2 * (B * H * S * D * 2 + B * H * S * D // 2 + B * H * S * 2)
+    nsets = args.sets or max(2, -(-CACHE_DEFEAT_BYTES // per_set))
+    sets = []
+    for i in range(nsets):
+        sets.append({
+            "k": k0 if i == 0 else k0.clone(), "v": v0 if i == 0 else v0.clone(),
+            "kq": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda"),
+            "vq": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda"),
+            "ks": torch.empty((B, H, S), dtype=torch.float16, device="cuda"),
+            "vs": torch.empty((B, H, S), dtype=torch.float16, device="cuda"),
+        })
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = sets[i % nsets]
+        qr.kv_had_quant(s["k"], s["v"], signs, s["kq"], s["ks"], s["vq"], s["vs"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = per_set
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"kv {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
+    return {
+        "metric": "KV rotate+quant GB/s (% HBM peak)", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32 rotate / int4 codes",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: K and V fp16 [{B} x {H} x {S} x {D}], "
+                               f"H_{D} with random signs", "buffer_sets": nsets},
+        "roofline": {"kernel": "kv_had_quant", "bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes},
+    }
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path has no cross-GPU exchange; see the sharding notes)", file=sys.stderr)
+        return 2
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import rotated_w4a4_amd as qr
+
+    qr.lib()
+    torch.cuda.set_device(0)
+    out = bench_kv(args, torch, qr) if args.kv else bench_act(args, torch, qr)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,179 @@
+/*
+ * quarot.h -- C ABI of the rotated W4A4 hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages (titles, with the section each call
+ * follows):
+ *   [S] "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs"
+ *       (paper-graph-ui summary of arXiv 2404.00456)
+ *   [G] "QuaRot Guide: Outlier-Free 4-Bit W4A4 LLM Quantization" (aifetchly blog)
+ *   [V] the QuaRot paper-viz explainer (romaanj.github.io)
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *     allocated and owned by the caller.  The library allocates nothing,
+ *     frees nothing and keeps no reference after returning.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and the call returns without synchronising.  A kernel
+ *     fault surfaces at the caller's next synchronisation.
+ *   - fp16 means IEEE binary16 (stored as 16-bit words).  int4 codes are
+ *     packed two per byte: element 2k in the low nibble of byte k, element
+ *     2k+1 in the high nibble, each the 4-bit two's complement of a value
+ *     in [-8, 7].
+ *   - Return value: QUAROT_OK (0) or a negative status.  All argument checks
+ *     run on the host before any HIP call, so a rejected call touches
+ *     neither the GPU nor the stream.  quarot_last_error() returns a
+ *     thread-local text with the detail of the last failure on this thread.
+ *   - Calls are re-entrant; the library holds no mutable global state apart
+ *     from a once-initialised per-device property cache.
+ */
+#ifndef QUAROT_H
+#define QUAROT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QUAROT_OK = 0,
+  QUAROT_ERR_INVALID = -1,     /* null required pointer, bad size, bad stride, bad clip */
+  QUAROT_ERR_UNSUPPORTED = -2, /* shape or mode outside what the kernels implement */
+  QUAROT_ERR_MISALIGNED = -3,  /* pointer or stride alignment requirement violated */
+  QUAROT_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * Fused randomized Hadamard rotation + per-token symmetric INT4 quantisation.
+ *
+ * Follows [S] section 3.4 Stage 1a (randomized Hadamard R = H diag(s), and
+ * H_d = H_{2^n} (x) H_m when d is not a power of two), Stage 1b (online
+ * Hadamard before the down-projection), Stage 2b (per-token symmetric scale
+ * clip * max|x| / 7) and "Kernel Implementation and Hardware Efficiency"
+ * (quantise per token, pack two INT4 per byte); [G] section "2. Why
+ * Randomized Walsh-Hadamard Transforms" and step 2 of "Deep Dive" (round to
+ * nearest, clip to [-8, 7]).
+ *
+ * For every row r of x (fp16 [rows x d], row stride ld_x elements):
+ *   x~      = (H_{2^n} (x) H_m) diag(signs) x_r / sqrt(d)      (fp32 arithmetic)
+ *   S_r     = fp16(clip_ratio * max(max_j |x~_j|, 1e-5) / 7)
+ *   q_j     = clamp(rint(x~_j / S_r), -8, 7)                     (ties to even)
+ * and writes q packed into q_out (uint8 [rows x d/2], row stride ld_q bytes)
+ * and S_r into scale_out (fp16 [rows]).  The Kronecker index of element j
+ * is j = a*m + b: H_m mixes the contiguous group b, H_{2^n} mixes a.
+ *
+ * Arguments:
+ *   x          fp16 [rows x d], 16-byte aligned, ld_x >= d, ld_x % 8 == 0.
+ *   signs      int8 [d] of +1/-1, or NULL for all +1.
+ *   m          1, 12 or 28: the size of the small Hadamard factor, taken
+ *              from the library's built-in Paley type-I matrices
+ *              (quarot_hadamard_factor() returns them); d = 2^n * m.
+ *   clip_ratio in (0, 1].  1.0 gives S = max|x~| / 7.
+ *   q_out      uint8 [rows x ld_q], 16-byte aligned, ld_q >= d/2, ld_q % 16 == 0.
+ *   scale_out  fp16 [rows], 2-byte aligned.
+ *   x_rot_out  optional fp32 [rows x d] (dense) receiving x~ for inspection;
+ *              NULL in production (it adds 4*d bytes of traffic per row).
+ * Supported: rows >= 0 (0 is a no-op), d = 2^n * m with d % 32 == 0 and
+ * d <= 32768.  Non-finite inputs are outside the contract.
+ */
+int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
+                     const int8_t* signs, int32_t m, float clip_ratio,
+                     uint8_t* q_out, int64_t ld_q, void* scale_out,
+                     float* x_rot_out, void* stream);
+
+/*
+ * W4A4 GEMM with INT32 accumulation and the per-token x per-channel dequant.
+ *
+ * Follows [S] section 3.4 Stage 2b (dequantised output
+ * Y_ij = acc_ij * scale_x[i] * scale_w[j]) and "Kernel Implementation and
+ * Hardware Efficiency" (INT4 x INT4 GEMM of packed activations against
+ * offline-packed weights, INT32 accumulator, dequant to FP16); [G] step 3
+ * of "Deep Dive".
+ *
+ *   acc[i][j] = sum_k a[i][k] * b[j][k]           exact, int32
+ *   c[i][j]   = fp16(float(acc[i][j]) * a_scale[i] * b_scale[j])
+ * (computed in fp32, then rounded to fp16 with ties to even;
+ * beyond the fp16 range it saturates to +-inf).
+ *
+ * Arguments:
+ *   a_q        packed int4 activations, uint8 [M x lda], K-contiguous rows,
+ *              16-byte aligned, lda >= K/2, lda % 16 == 0.
+ *   a_scale    fp16 [M] per-token scales.
+ *   b_q        packed int4 weights, uint8 [N x ldb] (one row per output
+ *              channel), same alignment rules as a_q.
+ *   b_scale    fp16 [N] per-output-channel scales.
+ *   c          fp16 [M x ldc] output, ldc >= N, 4-byte aligned, ldc % 2 == 0.
+ *   acc_out    optional int32 [M x ld_acc] receiving acc (ld_acc >= N);
+ *              NULL in production.
+ * Supported: M, N >= 0 (0 is a no-op), K > 0 with K % 32 == 0 and
+ * K <= 65536 (so 256 * |acc| <= 256 * 64 K fits in int32).
+ */
+int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
+                     const uint8_t* b_q, int64_t ldb, const void* b_scale,
+                     int64_t M, int64_t N, int64_t K,
+                     void* c, int64_t ldc, int32_t* acc_out, int64_t ld_acc,
+                     void* stream);
+
+/*
+ * Head-wise Hadamard rotation + INT4 quantisation of K and V into the cache.
+ *
+ * Follows [S] section 3.4 Stage 1d (keys rotated head-wise by
+ * I_{n_h} (x) H_{d_h} after RoPE, post-RoPE caching), Stage 1c (values
+ * rotated head-wise), Stage 2c (one quantisation group per head vector of
+ * 128 values) and the "Append" routine of "Kernel Implementation and
+ * Hardware Efficiency" (quantise the new keys/values and append them to the
+ * cache); [G] step 4 of "Deep Dive".
+ *
+ * For every (b, h, s) with 0 <= s < S, the D values
+ * t[b][h][s][:] (element (b,h,s,i) at t + b*stride_b + h*stride_h +
+ * s*stride_s + i) are rotated by diag(signs_h) then the Sylvester H_D / sqrt(D),
+ * and quantised as one group exactly like quarot_had_quant (mode 0), with
+ * the code row written to cache position p = pos0 + s:
+ *   t_q    [B x H x S_cache x D/2] uint8, contiguous, row (b,h,p)
+ *   t_scale[B x H x S_cache]       fp16, contiguous.
+ *
+ * Arguments:
+ *   k, v         fp16 inputs; either may be NULL (that tensor is skipped),
+ *                not both.  16-byte aligned; strides in elements, each a
+ *                multiple of 8 and >= 0.
+ *   D            head dimension: 32, 64, 128 or 256.
+ *   signs        int8 +1/-1; head h uses signs + h*signs_stride_h (stride 0:
+ *                one vector shared by all heads).  NULL = all +1.
+ *   mode         0 = symmetric (scale only).  1 = asymmetric with zero point
+ *                (reserved; returns QUAROT_ERR_UNSUPPORTED).
+ *   clip_ratio   in (0, 1].
+ *   k_q/v_q      16-byte aligned cache code buffers; k_scale/v_scale fp16.
+ *   k_zero/v_zero  reserved for mode 1; ignored in mode 0.
+ *   S_cache, pos0  cache length and first position written;
+ *                0 <= pos0 and pos0 + S <= S_cache.
+ */
+int quarot_kv_had_quant(const void* k, const void* v,
+                        int64_t B, int64_t H, int64_t S, int64_t D,
+                        int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                        const int8_t* signs, int64_t signs_stride_h,
+                        int32_t mode, float clip_ratio,
+                        uint8_t* k_q, void* k_scale, void* k_zero,
+                        uint8_t* v_q, void* v_scale, void* v_zero,
+                        int64_t S_cache, int64_t pos0, void* stream);
+
+/*
+ * Host-only: copy the built-in small Hadamard factor H_m (entries +1/-1,
+ * row-major int8 [m x m], HOST memory of m*m bytes) that quarot_had_quant
+ * uses for d = 2^n * m.  m = 1 gives [1]; 12 and 28 give the Paley type-I
+ * matrices for q = 11 and q = 27 ([S] Stage 1a: "a known Hadamard matrix of
+ * size m"; [V]: a Paley block of size 12 for width 12288).  Offline weight
+ * preparation must use the same matrix.  Makes no HIP call.
+ */
+int quarot_hadamard_factor(int32_t m, int8_t* out_host);
+
+/* Static text for a status code (never NULL). */
+const char* quarot_status_string(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* quarot_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUAROT_H */

@@ -1,0 +1,24 @@
+"""rotated_w4a4_amd -- MI355X (gfx950) HIP kernels for QuaRot's online W4A4 path.
+
+Python binding of the C ABI declared in ``include/quarot.h`` (library
+``libquarot.so`` next to this file).  The binding only marshals arguments:
+it checks dtypes, devices and shapes, passes raw device pointers and the
+current HIP stream, and turns a negative status into an exception.  Every
+step of the computation runs in the HIP kernels; there is no fallback.
+
+Calls (same names as the C entry points, without the ``quarot_`` prefix):
+
+* ``had_quant(x, signs, m, clip_ratio)``   -> (codes uint8 [rows, d/2], scales fp16 [rows])
+* ``w4a4_gemm(a_q, a_scale, b_q, b_scale, k)`` -> fp16 [M, N]
+* ``kv_had_quant(k, v, signs, k_cache, k_scale, v_cache, v_scale, pos0)``
+* ``hadamard_factor(m)``                  -> the built-in H_m (numpy int8)
+
+Tensors are torch tensors on the current HIP device; torch provides device
+memory and streams only.
+"""
+
+from ._lib import (QuarotError, had_quant, hadamard_factor, kv_had_quant, lib,
+                   library_path, w4a4_gemm)
+
+__all__ = ["QuarotError", "had_quant", "hadamard_factor", "kv_had_quant", "lib",
+           "library_path", "w4a4_gemm"]

@@ -1,0 +1,208 @@
+"""ctypes binding of libquarot (argument marshalling only)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libquarot.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+
+_SIGNATURES = {
+    "quarot_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _f32,
+                                        _vp, _i64, _vp, _vp, _vp]),
+    "quarot_w4a4_gemm": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
+                                        _vp, _i64, _vp, _i64, _vp]),
+    "quarot_kv_had_quant": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                           _vp, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _i64, _i64, _vp]),
+    "quarot_hadamard_factor": (ctypes.c_int, [_i32, _vp]),
+    "quarot_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "quarot_last_error": (ctypes.c_char_p, []),
+}
+
+
+class QuarotError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libquarot.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m rotated_w4a4_amd.build` "
+                "(there is no fallback implementation)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        detail = lib().quarot_last_error().decode(errors="replace")
+        raise QuarotError(fn, status, detail)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t, dtype, name: str, ndim: Optional[int] = None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def hadamard_factor(m: int) -> np.ndarray:
+    """The built-in H_m the kernels use (int8 [m, m], +-1)."""
+    out = np.zeros((m, m), dtype=np.int8)
+    _check("quarot_hadamard_factor",
+           lib().quarot_hadamard_factor(m, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def had_quant(x, signs=None, m: int = 1, clip_ratio: float = 1.0, q_out=None, scale_out=None,
+              x_rot_out=None, stream=None):
+    """Rotate+quant rows of fp16 x [rows, d]; returns (codes, scales)."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    rows, d = x.shape
+    if signs is not None:
+        _need(signs, torch.int8, "signs", 1)
+        if signs.numel() != d or not signs.is_contiguous():
+            raise ValueError("signs must be a contiguous int8 vector of length d")
+    if q_out is None:
+        q_out = torch.empty((rows, d // 2), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((rows,), dtype=torch.float16, device=x.device)
+    _need(q_out, torch.uint8, "q_out", 2)
+    _need(scale_out, torch.float16, "scale_out", 1)
+    if x_rot_out is not None:
+        _need(x_rot_out, torch.float32, "x_rot_out", 2)
+        if not x_rot_out.is_contiguous() or tuple(x_rot_out.shape) != (rows, d):
+            raise ValueError("x_rot_out must be contiguous float32 [rows, d]")
+    if q_out.stride(1) != 1 or q_out.shape[0] != rows or scale_out.shape[0] != rows:
+        raise ValueError("bad output shapes")
+    st = lib().quarot_had_quant(_ptr(x), rows, d, x.stride(0), _ptr(signs), m,
+                                float(clip_ratio), _ptr(q_out), q_out.stride(0),
+                                _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
+    _check("quarot_had_quant", st)
+    return q_out, scale_out
+
+
+def w4a4_gemm(a_q, a_scale, b_q, b_scale, k: int, out=None, acc_out=None, stream=None):
+    """fp16 [M, N] = dequant(int4 a_q [M, k/2] x int4 b_q [N, k/2]^T)."""
+    torch = _torch()
+    _need(a_q, torch.uint8, "a_q", 2)
+    _need(b_q, torch.uint8, "b_q", 2)
+    _need(a_scale, torch.float16, "a_scale", 1)
+    _need(b_scale, torch.float16, "b_scale", 1)
+    if a_q.stride(1) != 1 or b_q.stride(1) != 1:
+        raise ValueError("a_q/b_q rows must be contiguous")
+    M, N = a_q.shape[0], b_q.shape[0]
+    if a_scale.numel() != M or b_scale.numel() != N:
+        raise ValueError("scale lengths must match M and N")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a_q.device)
+    _need(out, torch.float16, "out", 2)
+    if out.stride(1) != 1 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N] with contiguous rows")
+    ld_acc = 0
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out", 2)
+        if acc_out.stride(1) != 1 or tuple(acc_out.shape) != (M, N):
+            raise ValueError("acc_out must be [M, N] with contiguous rows")
+        ld_acc = acc_out.stride(0)
+    st = lib().quarot_w4a4_gemm(_ptr(a_q), a_q.stride(0), _ptr(a_scale), _ptr(b_q),
+                                b_q.stride(0), _ptr(b_scale), M, N, int(k), _ptr(out),
+                                out.stride(0), _ptr(acc_out), ld_acc, _stream(stream))
+    _check("quarot_w4a4_gemm", st)
+    return out
+
+
+def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0: int = 0,
+                 signs_stride_h: int = 0, clip_ratio: float = 1.0, mode: int = 0, stream=None):
+    """Quantise K (and V) [B, H, S, D] into caches [B, H, S_cache, D/2] at pos0."""
+    torch = _torch()
+    ref = k if k is not None else v
+    _need(ref, torch.float16, "k/v", 4)
+    B, H, S, D = ref.shape
+    for name, t in (("k", k), ("v", v)):
+        if t is None:
+            continue
+        _need(t, torch.float16, name, 4)
+        if tuple(t.shape) != (B, H, S, D) or t.stride(3) != 1:
+            raise ValueError(f"{name} must be [B, H, S, D] with contiguous D")
+        if t.stride() != ref.stride():
+            raise ValueError("k and v must share strides")
+    caches = [(k, k_cache, k_scale, "k"), (v, v_cache, v_scale, "v")]
+    S_cache = None
+    for t, cq, cs, name in caches:
+        if t is None:
+            continue
+        _need(cq, torch.uint8, f"{name}_cache", 4)
+        _need(cs, torch.float16, f"{name}_scale", 3)
+        if not cq.is_contiguous() or not cs.is_contiguous():
+            raise ValueError("caches must be contiguous")
+        if cq.shape[0] != B or cq.shape[1] != H or cq.shape[3] != D // 2:
+            raise ValueError(f"{name}_cache must be [B, H, S_cache, D/2]")
+        if tuple(cs.shape) != tuple(cq.shape[:3]):
+            raise ValueError(f"{name}_scale must be [B, H, S_cache]")
+        if S_cache is None:
+            S_cache = cq.shape[2]
+        elif cq.shape[2] != S_cache:
+            raise ValueError("k and v caches must have the same length")
+    if signs is not None:
+        _need(signs, torch.int8, "signs")
+    sb, sh, ss, _ = ref.stride()
+    st = lib().quarot_kv_had_quant(_ptr(k), _ptr(v), B, H, S, D, sb, sh, ss, _ptr(signs),
+                                   int(signs_stride_h), int(mode), float(clip_ratio),
+                                   _ptr(k_cache) if k is not None else None,
+                                   _ptr(k_scale) if k is not None else None, None,
+                                   _ptr(v_cache) if v is not None else None,
+                                   _ptr(v_scale) if v is not None else None, None,
+                                   S_cache, int(pos0), _stream(stream))
+    _check("quarot_kv_had_quant", st)
+    return k_cache, k_scale, v_cache, v_scale

@@ -1,0 +1,186 @@
+// C ABI of libquarot: argument validation, status strings, and dispatch to
+// the kernel launchers.  Every check here runs on the host before any HIP
+// call, so a rejected call never touches the device or the stream.
+#include <cstring>
+
+#include "common.h"
+
+namespace quarot {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return QUAROT_ERR_HIP;
+  }
+  return QUAROT_OK;
+}
+
+namespace {
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int log2_exact(int64_t v) {
+  int n = 0;
+  while ((int64_t(1) << n) < v) ++n;
+  return n;
+}
+
+bool clip_ok(float c) { return c > 0.0f && c <= 1.0f; }  // also rejects NaN
+
+}  // namespace
+}  // namespace quarot
+
+using namespace quarot;
+
+extern "C" {
+
+const char* quarot_status_string(int status) {
+  switch (status) {
+    case QUAROT_OK: return "ok";
+    case QUAROT_ERR_INVALID: return "invalid argument";
+    case QUAROT_ERR_UNSUPPORTED: return "unsupported shape or mode";
+    case QUAROT_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case QUAROT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* quarot_last_error(void) { return g_last_error; }
+
+int quarot_hadamard_factor(int32_t m, int8_t* out_host) {
+  clear_error();
+  QR_CHECK_ARG(out_host != nullptr, QUAROT_ERR_INVALID, "out_host is NULL");
+  switch (m) {
+    case 1: out_host[0] = 1; return QUAROT_OK;
+    case 12: std::memcpy(out_host, HadTable<12>::value.v, 12 * 12); return QUAROT_OK;
+    case 28: std::memcpy(out_host, HadTable<28>::value.v, 28 * 28); return QUAROT_OK;
+    default:
+      set_error("no built-in Hadamard factor of order %d (have 1, 12, 28)", m);
+      return QUAROT_ERR_UNSUPPORTED;
+  }
+}
+
+int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
+                     const int8_t* signs, int32_t m, float clip_ratio,
+                     uint8_t* q_out, int64_t ld_q, void* scale_out,
+                     float* x_rot_out, void* stream) {
+  clear_error();
+  QR_CHECK_ARG(rows >= 0, QUAROT_ERR_INVALID, "rows = %lld < 0", (long long)rows);
+  QR_CHECK_ARG(d > 0, QUAROT_ERR_INVALID, "d = %lld <= 0", (long long)d);
+  QR_CHECK_ARG(clip_ok(clip_ratio), QUAROT_ERR_INVALID, "clip_ratio must be in (0, 1]");
+  QR_CHECK_ARG(m == 1 || m == 12 || m == 28, QUAROT_ERR_UNSUPPORTED,
+               "m = %d: built-in Hadamard factors are 1, 12, 28", m);
+  QR_CHECK_ARG(d % m == 0 && is_pow2(d / m), QUAROT_ERR_UNSUPPORTED,
+               "d = %lld is not 2^n * %d", (long long)d, m);
+  QR_CHECK_ARG(d % 32 == 0 && d <= 32768, QUAROT_ERR_UNSUPPORTED,
+               "d = %lld: need d %% 32 == 0 and d <= 32768", (long long)d);
+  QR_CHECK_ARG(ld_x >= d, QUAROT_ERR_INVALID, "ld_x = %lld < d", (long long)ld_x);
+  QR_CHECK_ARG(ld_q >= d / 2, QUAROT_ERR_INVALID, "ld_q = %lld < d/2", (long long)ld_q);
+  if (rows == 0) return QUAROT_OK;
+  QR_CHECK_ARG(x && q_out && scale_out, QUAROT_ERR_INVALID, "x, q_out and scale_out are required");
+  QR_CHECK_ARG(aligned(x, 16) && ld_x % 8 == 0, QUAROT_ERR_MISALIGNED,
+               "x must be 16-byte aligned with ld_x %% 8 == 0");
+  QR_CHECK_ARG(aligned(q_out, 16) && ld_q % 16 == 0, QUAROT_ERR_MISALIGNED,
+               "q_out must be 16-byte aligned with ld_q %% 16 == 0");
+  QR_CHECK_ARG(aligned(scale_out, 2), QUAROT_ERR_MISALIGNED, "scale_out must be 2-byte aligned");
+  QR_CHECK_ARG(x_rot_out == nullptr || aligned(x_rot_out, 16), QUAROT_ERR_MISALIGNED,
+               "x_rot_out must be 16-byte aligned");
+  QR_CHECK_ARG(rows <= (int64_t(1) << 31) - 1, QUAROT_ERR_UNSUPPORTED, "rows too large");
+  const int n = log2_exact(d / m);
+  return launch_had_quant(static_cast<const __half*>(x), rows, int(d), n, m, ld_x, signs,
+                          clip_ratio, q_out, ld_q, static_cast<__half*>(scale_out), x_rot_out,
+                          static_cast<hipStream_t>(stream));
+}
+
+int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
+                     const uint8_t* b_q, int64_t ldb, const void* b_scale,
+                     int64_t M, int64_t N, int64_t K,
+                     void* c, int64_t ldc, int32_t* acc_out, int64_t ld_acc,
+                     void* stream) {
+  clear_error();
+  QR_CHECK_ARG(M >= 0 && N >= 0, QUAROT_ERR_INVALID, "M, N must be >= 0");
+  QR_CHECK_ARG(K > 0, QUAROT_ERR_INVALID, "K must be > 0");
+  QR_CHECK_ARG(K % 32 == 0, QUAROT_ERR_UNSUPPORTED, "K = %lld: need K %% 32 == 0", (long long)K);
+  QR_CHECK_ARG(K <= 65536, QUAROT_ERR_UNSUPPORTED, "K = %lld > 65536", (long long)K);
+  QR_CHECK_ARG(lda >= K / 2 && ldb >= K / 2, QUAROT_ERR_INVALID, "lda, ldb must be >= K/2");
+  QR_CHECK_ARG(ldc >= N, QUAROT_ERR_INVALID, "ldc must be >= N");
+  QR_CHECK_ARG(acc_out == nullptr || ld_acc >= N, QUAROT_ERR_INVALID, "ld_acc must be >= N");
+  if (M == 0 || N == 0) return QUAROT_OK;
+  QR_CHECK_ARG(a_q && a_scale && b_q && b_scale && c, QUAROT_ERR_INVALID,
+               "a_q, a_scale, b_q, b_scale and c are required");
+  QR_CHECK_ARG(aligned(a_q, 16) && aligned(b_q, 16) && lda % 16 == 0 && ldb % 16 == 0,
+               QUAROT_ERR_MISALIGNED, "a_q/b_q must be 16-byte aligned with lda, ldb %% 16 == 0");
+  QR_CHECK_ARG(aligned(a_scale, 2) && aligned(b_scale, 2), QUAROT_ERR_MISALIGNED,
+               "scales must be 2-byte aligned");
+  QR_CHECK_ARG(aligned(c, 4) && ldc % 2 == 0, QUAROT_ERR_MISALIGNED,
+               "c must be 4-byte aligned with ldc %% 2 == 0");
+  QR_CHECK_ARG(acc_out == nullptr || aligned(acc_out, 4), QUAROT_ERR_MISALIGNED,
+               "acc_out must be 4-byte aligned");
+  QR_CHECK_ARG(M < (int64_t(1) << 31) && N < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED,
+               "M, N too large");
+  return launch_w4a4_gemm(a_q, lda, static_cast<const __half*>(a_scale), b_q, ldb,
+                          static_cast<const __half*>(b_scale), M, N, K,
+                          static_cast<__half*>(c), ldc, acc_out, ld_acc,
+                          static_cast<hipStream_t>(stream));
+}
+
+int quarot_kv_had_quant(const void* k, const void* v,
+                        int64_t B, int64_t H, int64_t S, int64_t D,
+                        int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                        const int8_t* signs, int64_t signs_stride_h,
+                        int32_t mode, float clip_ratio,
+                        uint8_t* k_q, void* k_scale, void* k_zero,
+                        uint8_t* v_q, void* v_scale, void* v_zero,
+                        int64_t S_cache, int64_t pos0, void* stream) {
+  clear_error();
+  (void)k_zero;
+  (void)v_zero;
+  QR_CHECK_ARG(B >= 0 && H >= 0 && S >= 0, QUAROT_ERR_INVALID, "B, H, S must be >= 0");
+  QR_CHECK_ARG(D == 32 || D == 64 || D == 128 || D == 256, QUAROT_ERR_UNSUPPORTED,
+               "D = %lld: supported head dims are 32, 64, 128, 256", (long long)D);
+  QR_CHECK_ARG(mode == 0 || mode == 1, QUAROT_ERR_INVALID, "mode must be 0 or 1");
+  QR_CHECK_ARG(mode == 0, QUAROT_ERR_UNSUPPORTED, "mode 1 (asymmetric) is not implemented");
+  QR_CHECK_ARG(clip_ok(clip_ratio), QUAROT_ERR_INVALID, "clip_ratio must be in (0, 1]");
+  QR_CHECK_ARG(stride_b >= 0 && stride_h >= 0 && stride_s >= 0 && signs_stride_h >= 0,
+               QUAROT_ERR_INVALID, "strides must be >= 0");
+  QR_CHECK_ARG(pos0 >= 0 && S_cache >= 0 && pos0 + S <= S_cache, QUAROT_ERR_INVALID,
+               "need 0 <= pos0 and pos0 + S <= S_cache");
+  QR_CHECK_ARG(k != nullptr || v != nullptr, QUAROT_ERR_INVALID, "k and v are both NULL");
+  if (B == 0 || H == 0 || S == 0) return QUAROT_OK;
+  QR_CHECK_ARG(stride_b % 8 == 0 && stride_h % 8 == 0 && stride_s % 8 == 0, QUAROT_ERR_MISALIGNED,
+               "strides must be multiples of 8 elements");
+  KvTensorArgs t[2];
+  int nt = 0;
+  const void* srcs[2] = {k, v};
+  uint8_t* qs[2] = {k_q, v_q};
+  void* ss[2] = {k_scale, v_scale};
+  for (int i = 0; i < 2; ++i) {
+    if (!srcs[i]) continue;
+    QR_CHECK_ARG(qs[i] && ss[i], QUAROT_ERR_INVALID, "%s_q and %s_scale are required",
+                 i ? "v" : "k", i ? "v" : "k");
+    QR_CHECK_ARG(aligned(srcs[i], 16) && aligned(qs[i], 16) && aligned(ss[i], 2),
+                 QUAROT_ERR_MISALIGNED, "inputs and code buffers must be 16-byte aligned");
+    t[nt++] = KvTensorArgs{static_cast<const __half*>(srcs[i]), qs[i],
+                           static_cast<__half*>(ss[i])};
+  }
+  QR_CHECK_ARG(B * H * S < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED, "too many groups");
+  return launch_kv_had_quant(t, nt, B, H, S, int(D), stride_b, stride_h, stride_s, signs,
+                             signs_stride_h, clip_ratio, S_cache, pos0,
+                             static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

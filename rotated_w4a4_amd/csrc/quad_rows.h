@@ -1,0 +1,135 @@
+// Rotate+quant of short rows (d = 32 .. 256, a power of two): four lanes of
+// a wave own one row.  Used for the per-head K/V groups and for short
+// activation rows.
+//
+// "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
+// summary), section 3.4 Stage 1d (head-wise Hadamard on keys after RoPE) and
+// Stage 2c (one quantisation group per head vector); "QuaRot Guide",
+// section 3 of "The Architecture" (fast Walsh-Hadamard transform: d log d
+// additions and subtractions, no multiplies).
+//
+// Layout.  Lane q (0..3) of a quad owns the 16-byte chunks c = q + 4j of the
+// row, j = 0..D/32-1, so element e = 8q + 32j + i (i = 0..7) sits in register
+// r = 8j + i.  Element bits 0-2 and 5.. are register bits (butterflies
+// inside a lane); element bits 3 and 4 are lane bits 0 and 1 of the quad
+// (butterflies through DPP quad permutations).  Loads are 16 contiguous bytes
+// per lane, four lanes cover 64 contiguous bytes; each chunk's eight codes
+// pack into one 32-bit word.
+#pragma once
+
+#include "quant_common.h"
+
+namespace quarot {
+
+// One DPP butterfly across lanes: the partner is lane ^ (1 << LB) inside the
+// quad.  The low lane keeps a + b, the high lane keeps a - b.
+template <int LB>
+__device__ __forceinline__ float quad_butterfly(float v, float sgn) {
+  constexpr int ctrl = (LB == 0) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const float p = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+  return fmaf(v, sgn, p);
+}
+
+template <int LB>
+__device__ __forceinline__ float quad_max(float v) {
+  constexpr int ctrl = (LB == 0) ? 0xB1 : 0x4E;
+  const float p = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+  return fmaxf(v, p);
+}
+
+// Build the XOR masks that flip fp16 sign bits for this lane's elements.
+template <int NC>
+__device__ __forceinline__ void load_sign_masks(const int8_t* sg, int q, uint32_t (&mask)[NC][4]) {
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t mk = 0;
+      if (sg) {
+        const int e = 8 * (q + 4 * j) + 2 * p;
+        mk = (sg[e] < 0 ? 0x8000u : 0u) | (sg[e + 1] < 0 ? 0x80000000u : 0u);
+      }
+      mask[j][p] = mk;
+    }
+  }
+}
+
+// Process one row held by a quad.  src: fp16 row; qrow: code row (D/2
+// bytes); scale: where the fp16 scale goes; xrot: optional fp32 row.
+template <int D>
+__device__ __forceinline__ void quad_row(const __half* __restrict__ src, uint8_t* __restrict__ qrow,
+                                         __half* __restrict__ scale, float* __restrict__ xrot,
+                                         const uint32_t (&mask)[D / 32][4], int q,
+                                         float clip_ratio, bool active) {
+  constexpr int NC = D / 32;  // chunks per lane
+  constexpr int E = 8 * NC;   // elements per lane
+  float v[E];
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * (q + 4 * j));
+      raw.x ^= mask[j][0];
+      raw.y ^= mask[j][1];
+      raw.z ^= mask[j][2];
+      raw.w ^= mask[j][3];
+      unpack_half8(raw, &v[8 * j]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = 0.0f;
+  }
+  // register-bit butterflies
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      if ((r & h) == 0) {
+        const float a = v[r], b = v[r + h];
+        v[r] = a + b;
+        v[r + h] = a - b;
+      }
+    }
+  }
+  // lane-bit butterflies (element bits 3 and 4); every lane of the wave takes
+  // part so the DPP sources are always defined
+  const float s0 = (q & 1) ? -1.0f : 1.0f;
+  const float s1 = (q & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int r = 0; r < E; ++r) v[r] = quad_butterfly<0>(v[r], s0);
+#pragma unroll
+  for (int r = 0; r < E; ++r) v[r] = quad_butterfly<1>(v[r], s1);
+
+  constexpr float kNorm = 1.0f / (D == 32 ? 5.656854249492380f
+                                  : D == 64 ? 8.0f
+                                  : D == 128 ? 11.313708498984761f
+                                             : 16.0f);
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    v[r] *= kNorm;
+    amax = fmaxf(amax, fabsf(v[r]));
+  }
+  amax = quad_max<0>(amax);
+  amax = quad_max<1>(amax);
+  const __half s16 = row_scale_fp16(amax, clip_ratio);
+  const float k = inv_scale(s16);
+  if (!active) return;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const uint32_t w = pack8(&v[8 * j], k);
+    *reinterpret_cast<uint32_t*>(qrow + 4 * (q + 4 * j)) = w;
+  }
+  if (q == 0) *scale = s16;
+  if (xrot) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      float4* dst = reinterpret_cast<float4*>(xrot + 8 * (q + 4 * j));
+      dst[0] = make_float4(v[8 * j + 0], v[8 * j + 1], v[8 * j + 2], v[8 * j + 3]);
+      dst[1] = make_float4(v[8 * j + 4], v[8 * j + 5], v[8 * j + 6], v[8 * j + 7]);
+    }
+  }
+}
+
+}  // namespace quarot

@@ -1,0 +1,81 @@
+"""Comparison rules between the HIP path and the CPU oracle.
+
+Tolerances (from the stated targets; readings explained where the targets
+leave the semantics open):
+
+* rotated values: |gpu - ref| <= 1e-5 * max_j |ref_row_j| per row ("within
+  1e-5 relative"; taken relative to the row's largest entry, since an
+  elementwise relative error is meaningless near zero);
+* scales (fp16): equal, or one fp16 ulp apart (the fp32 absolute maximum can
+  sit on the other side of an fp16 rounding boundary than the fp64 one);
+* int4 codes: |gpu - ref| <= 1 everywhere and nonzero on at most 0.1% of the
+  elements (rounding-boundary ties);
+* int32 accumulators fed the oracle's codes: bit-exact;
+* fp16 GEMM output fed the oracle's codes: |gpu - ref| <= 1e-3 * |ref| or
+  within one fp16 ulp of ref;
+* fp16 output end to end: ||gpu - ref||_F / ||ref||_F <= 1e-3, plus the
+  elementwise rule above wherever the row's and the column's codes match.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ROT_TOL = 1e-5
+CODE_FRAC = 1e-3
+Y_REL = 1e-3
+
+
+def check_rot(gpu: np.ndarray, ref: np.ndarray, tol: float = ROT_TOL) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rowmax = np.abs(ref).max(axis=1, keepdims=True)
+    rowmax = np.maximum(rowmax, 1e-30)
+    err = (np.abs(gpu - ref) / rowmax).max()
+    assert err <= tol, f"rotated values: max row-relative error {err:.3e} > {tol:.1e}"
+    return float(err)
+
+
+def check_scales(gpu16: np.ndarray, ref16: np.ndarray) -> int:
+    g = np.asarray(gpu16, dtype=np.float16).view(np.uint16).astype(np.int64)
+    r = np.asarray(ref16, dtype=np.float16).view(np.uint16).astype(np.int64)
+    d = np.abs(g - r)
+    assert d.max() <= 1, f"scales differ by {d.max()} fp16 ulps"
+    return int((d > 0).sum())
+
+
+def check_codes(gpu: np.ndarray, ref: np.ndarray, frac: float = CODE_FRAC) -> float:
+    g = np.asarray(gpu, dtype=np.int64)
+    r = np.asarray(ref, dtype=np.int64)
+    d = np.abs(g - r)
+    assert d.max() <= 1, f"codes differ by up to {d.max()}"
+    f = float((d > 0).mean())
+    assert f <= frac, f"{f:.2e} of the codes differ (> {frac:.0e})"
+    return f
+
+
+def fp16_ulp(ref16: np.ndarray) -> np.ndarray:
+    r = np.abs(np.asarray(ref16, dtype=np.float16))
+    return np.spacing(r).astype(np.float64)
+
+
+def check_y_elementwise(gpu16: np.ndarray, ref16: np.ndarray, mask=None) -> float:
+    g = np.asarray(gpu16, dtype=np.float16).astype(np.float64)
+    r = np.asarray(ref16, dtype=np.float16).astype(np.float64)
+    both_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
+    diff = np.where(both_inf, 0.0, np.abs(g - r))
+    ok = (diff <= Y_REL * np.abs(r)) | (diff <= fp16_ulp(ref16))
+    if mask is not None:
+        ok = ok | ~mask
+    bad = int((~ok).sum())
+    assert bad == 0, f"{bad} fp16 outputs outside 1e-3 relative / 1 ulp"
+    rel = diff / np.maximum(np.abs(r), 1e-30)
+    return float(rel[mask].max() if mask is not None and mask.any() else rel.max())
+
+
+def check_y_frobenius(gpu16: np.ndarray, ref16: np.ndarray, tol: float = Y_REL) -> float:
+    g = np.asarray(gpu16, dtype=np.float16).astype(np.float64)
+    r = np.asarray(ref16, dtype=np.float16).astype(np.float64)
+    e = np.linalg.norm(g - r) / np.linalg.norm(r)
+    assert e <= tol, f"end-to-end Frobenius relative error {e:.3e} > {tol:.0e}"
+    return float(e)

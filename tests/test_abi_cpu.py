@@ -1,0 +1,164 @@
+"""Host-side checks of libquarot (no GPU needed).
+
+* the library loads and exports every function declared in include/quarot.h;
+* its built-in Paley factors equal the oracle's (two independent
+  constructions of the same published definition);
+* invalid arguments are rejected with the documented status before any HIP
+  call (no call here reaches the device: each one fails validation).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import rotated_w4a4_amd as qr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, MISALIGNED, HIPERR = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qr.library_path()):
+        pytest.skip("libquarot.so not built")
+    return qr.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    with open(os.path.join(ROOT, "include", "quarot.h")) as f:
+        text = f.read()
+    names = set(re.findall(r"\b(quarot_[a-z0-9_]+)\s*\(", text))
+    assert {"quarot_had_quant", "quarot_w4a4_gemm", "quarot_kv_had_quant"} <= names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("m", [1, 12, 28])
+def test_builtin_factor_matches_oracle(lib, m):
+    np.testing.assert_array_equal(qr.hadamard_factor(m), oracle.hadamard_m(m))
+
+
+def test_factor_unsupported(lib):
+    out = np.zeros(64, np.int8)
+    assert lib.quarot_hadamard_factor(20, out.ctypes.data_as(ctypes.c_void_p)) == UNSUPPORTED
+    assert lib.quarot_hadamard_factor(12, None) == INVALID
+
+
+def test_status_strings(lib):
+    for s in (OK, INVALID, UNSUPPORTED, MISALIGNED, HIPERR, 7):
+        assert lib.quarot_status_string(s)
+
+
+FAKE = 0x10000  # 64 KiB-aligned host address never dereferenced by a failing call
+
+
+def _hq(lib, **kw):
+    a = dict(x=FAKE, rows=4, d=256, ld_x=256, signs=None, m=1, clip=1.0, q=FAKE, ld_q=128,
+             scale=FAKE, xrot=None, stream=None)
+    a.update(kw)
+    return lib.quarot_had_quant(a["x"], a["rows"], a["d"], a["ld_x"], a["signs"], a["m"],
+                                a["clip"], a["q"], a["ld_q"], a["scale"], a["xrot"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), INVALID),
+    (dict(d=0), INVALID),
+    (dict(clip=0.0), INVALID),
+    (dict(clip=1.5), INVALID),
+    (dict(clip=float("nan")), INVALID),
+    (dict(m=20), UNSUPPORTED),
+    (dict(d=384, ld_x=384, ld_q=192), UNSUPPORTED),  # 384 = 3 * 128, not 2^n * 1
+    (dict(d=48, m=12, ld_x=48, ld_q=32), UNSUPPORTED),  # d % 32 != 0
+    (dict(d=65536, ld_x=65536, ld_q=32768), UNSUPPORTED),
+    (dict(ld_x=128), INVALID),
+    (dict(ld_q=64), INVALID),
+    (dict(x=None), INVALID),
+    (dict(q=None), INVALID),
+    (dict(scale=None), INVALID),
+    (dict(x=FAKE + 8), MISALIGNED),
+    (dict(ld_x=260), MISALIGNED),
+    (dict(q=FAKE + 4), MISALIGNED),
+    (dict(ld_q=136), MISALIGNED),
+    (dict(scale=FAKE + 1), MISALIGNED),
+    (dict(xrot=FAKE + 4), MISALIGNED),
+])
+def test_had_quant_rejects(lib, kw, status):
+    assert _hq(lib, **kw) == status
+    assert lib.quarot_last_error()
+
+
+def test_had_quant_zero_rows_is_noop(lib):
+    assert _hq(lib, rows=0, x=None, q=None, scale=None) == OK
+
+
+def _gemm(lib, **kw):
+    a = dict(a=FAKE, lda=64, sa=FAKE, b=FAKE, ldb=64, sb=FAKE, M=16, N=16, K=128, c=FAKE,
+             ldc=16, acc=None, ld_acc=0)
+    a.update(kw)
+    return lib.quarot_w4a4_gemm(a["a"], a["lda"], a["sa"], a["b"], a["ldb"], a["sb"], a["M"],
+                                a["N"], a["K"], a["c"], a["ldc"], a["acc"], a["ld_acc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID),
+    (dict(K=0), INVALID),
+    (dict(K=48), UNSUPPORTED),
+    (dict(K=65568, lda=32784, ldb=32784), UNSUPPORTED),
+    (dict(lda=32), INVALID),
+    (dict(ldc=8), INVALID),
+    (dict(acc=FAKE, ld_acc=8), INVALID),
+    (dict(a=None), INVALID),
+    (dict(sb=None), INVALID),
+    (dict(c=None), INVALID),
+    (dict(a=FAKE + 8), MISALIGNED),
+    (dict(lda=72), MISALIGNED),
+    (dict(sa=FAKE + 1), MISALIGNED),
+    (dict(c=FAKE + 2), MISALIGNED),
+    (dict(ldc=17), MISALIGNED),
+    (dict(acc=FAKE + 2, ld_acc=16), MISALIGNED),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert _gemm(lib, **kw) == status
+
+
+def test_gemm_empty_is_noop(lib):
+    assert _gemm(lib, M=0, a=None, c=None) == OK
+
+
+def _kv(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, B=2, H=2, S=4, D=128, sb=1024, sh=512, ss=128, signs=None,
+             ssh=0, mode=0, clip=1.0, kq=FAKE, ks=FAKE, vq=FAKE, vs=FAKE, S_cache=8, pos0=0)
+    a.update(kw)
+    return lib.quarot_kv_had_quant(a["k"], a["v"], a["B"], a["H"], a["S"], a["D"], a["sb"],
+                                   a["sh"], a["ss"], a["signs"], a["ssh"], a["mode"], a["clip"],
+                                   a["kq"], a["ks"], None, a["vq"], a["vs"], None, a["S_cache"],
+                                   a["pos0"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(D=512), UNSUPPORTED),
+    (dict(mode=2), INVALID),
+    (dict(mode=1), UNSUPPORTED),
+    (dict(clip=0.0), INVALID),
+    (dict(pos0=5), INVALID),
+    (dict(pos0=-1), INVALID),
+    (dict(k=None, v=None), INVALID),
+    (dict(kq=None), INVALID),
+    (dict(vs=None), INVALID),
+    (dict(ss=100), MISALIGNED),
+    (dict(k=FAKE + 2), MISALIGNED),
+    (dict(vq=FAKE + 4), MISALIGNED),
+    (dict(ssh=-1), INVALID),
+])
+def test_kv_rejects(lib, kw, status):
+    assert _kv(lib, **kw) == status
+
+
+def test_kv_empty_is_noop(lib):
+    assert _kv(lib, S=0, k=None) == OK

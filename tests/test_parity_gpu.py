@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Every case prints its name and shape before touching the GPU.  Inputs come
+from the seeded generators in ``workloads``; expected values only from
+``oracle``.  Comparison rules are in ``parity.py``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import (check_codes, check_rot, check_scales, check_y_elementwise,
+                    check_y_frobenius)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import rotated_w4a4_amd as qr  # noqa: E402
+
+
+def say(msg: str) -> None:
+    print(f"[parity] {msg}", flush=True)
+
+
+def dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_had_quant(x16: np.ndarray, signs, m: int, clip: float = 1.0, with_rot: bool = True):
+    x = dev(x16)
+    rows, d = x16.shape
+    xr = torch.empty((rows, d), dtype=torch.float32, device="cuda") if with_rot else None
+    q, s = qr.had_quant(x, dev(signs) if signs is not None else None, m, clip, x_rot_out=xr)
+    return host(q), host(s), (host(xr) if with_rot else None)
+
+
+_CACHE = {}
+
+
+def act_inputs(name: str) -> dict:
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = workloads.make_act_inputs(workloads.ACT_CONFIGS[name])
+    return _CACHE[name]
+
+
+# ---------------------------------------------------------------------------
+# Fast transform against the dense matrix on small d
+# ---------------------------------------------------------------------------
+SMALL_D = [(32, 1), (64, 1), (128, 1), (256, 1), (512, 1), (1024, 1), (2048, 1), (4096, 1),
+           (96, 12), (192, 12), (384, 12), (768, 12), (224, 28), (448, 28), (896, 28)]
+
+
+@pytest.mark.parametrize("d,m", SMALL_D)
+def test_rotation_equals_dense_hadamard(d, m):
+    rng = np.random.default_rng(d + m)
+    rows = 37
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    x[:, rng.integers(0, d)] *= 40.0
+    x16 = x.astype(np.float16)
+    signs = (1 - 2 * rng.integers(0, 2, d)).astype(np.int8)
+    say(f"dense check d={d} m={m} rows={rows}")
+    q, s, xr = gpu_had_quant(x16, signs, m)
+    dense = oracle.dense_rotation(d, signs, m)
+    ref = x16.astype(np.float64) @ dense.T
+    check_rot(xr, ref, 1e-6)
+    ref_q = oracle.had_quant(x16, signs, m)
+    check_scales(s, ref_q["scales"])
+    check_codes(oracle.unpack_int4(q), ref_q["codes"], frac=1e-2)
+
+
+# ---------------------------------------------------------------------------
+# Rotate+quant on the configured workloads
+# ---------------------------------------------------------------------------
+ACT_SAMPLE = {"tiny": None, "llama7b_proj": 256, "down_12288": 64, "llama70b_down": 24}
+
+
+@pytest.mark.parametrize("name", list(ACT_SAMPLE))
+def test_had_quant_workload(name):
+    cfg = workloads.ACT_CONFIGS[name]
+    inp = act_inputs(name)
+    x16 = inp["x"]
+    say(f"had_quant {name}: x {x16.shape} m={cfg.m}")
+    q, s, xr = gpu_had_quant(x16, inp["signs"], cfg.m)
+    n = ACT_SAMPLE[name]
+    rows = np.arange(x16.shape[0]) if n is None else np.unique(
+        np.r_[0, x16.shape[0] - 1, np.random.default_rng(7).choice(x16.shape[0], n, replace=False)])
+    ref = oracle.had_quant(x16[rows], inp["signs"], cfg.m)
+    e = check_rot(xr[rows], ref["x_rot"])
+    ns = check_scales(s[rows], ref["scales"])
+    f = check_codes(oracle.unpack_int4(q[rows]), ref["codes"])
+    np.testing.assert_array_equal(oracle.pack_int4(oracle.unpack_int4(q[rows])), q[rows])
+    say(f"  rows checked {len(rows)}: rot err {e:.2e}, scale ulps {ns}, code diff frac {f:.2e}")
+
+
+def test_had_quant_weights_workload():
+    # offline weight prep uses the same kernel on W's rows
+    cfg = workloads.ACT_CONFIGS["llama7b_proj"]
+    inp = act_inputs("llama7b_proj")
+    w16 = inp["w"]
+    say(f"had_quant weights: w {w16.shape}")
+    q, s, xr = gpu_had_quant(w16, inp["signs"], cfg.m)
+    rows = np.random.default_rng(11).choice(w16.shape[0], 128, replace=False)
+    ref = oracle.prep_weights(w16[rows], inp["signs"], cfg.m)
+    check_rot(xr[rows], ref["x_rot"])
+    check_scales(s[rows], ref["scales"])
+    check_codes(oracle.unpack_int4(q[rows]), ref["codes"])
+
+
+# ---------------------------------------------------------------------------
+# GEMM fed the oracle's codes: bit-exact accumulators
+# ---------------------------------------------------------------------------
+GEMM_FED = [  # (workload, rows of X, rows of W)
+    ("tiny", 16, 256),
+    ("llama7b_proj", 200, 300),
+    ("down_12288", 130, 260),
+    ("llama70b_down", 72, 136),
+]
+
+
+@pytest.mark.parametrize("name,mr,nr", GEMM_FED)
+def test_gemm_fed_oracle_codes(name, mr, nr):
+    cfg = workloads.ACT_CONFIGS[name]
+    inp = act_inputs(name)
+    a = oracle.had_quant(inp["x"][:mr], inp["signs"], cfg.m)
+    b = oracle.prep_weights(inp["w"][:nr], inp["signs"], cfg.m)
+    acc_ref, y_ref = oracle.w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
+    say(f"gemm fed oracle codes {name}: M={mr} N={nr} K={cfg.d}")
+    acc = torch.empty((mr, nr), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(dev(a["packed"]), dev(a["scales"]), dev(b["packed"]), dev(b["scales"]),
+                     cfg.d, acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    check_y_elementwise(host(y), y_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 65, 96), (129, 257, 160), (256, 512, 384),
+                                   (300, 700, 1056)])
+def test_gemm_ragged_shapes(M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = (rng.uniform(0.01, 2.0, M)).astype(np.float16)
+    sb = (rng.uniform(0.001, 0.1, N)).astype(np.float16)
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    say(f"gemm ragged M={M} N={N} K={K}")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(sa), dev(oracle.pack_int4(qb)), dev(sb), K,
+                     acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    check_y_elementwise(host(y), y_ref)
+
+
+def test_gemm_extreme_codes():
+    # all -8 x all -8 at K = 28672: acc = 64 K = 1835008 per output
+    M, N, K = 64, 64, 28672
+    qa = np.full((M, K), -8, np.int8)
+    say("gemm extreme codes")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ones = np.ones(M, np.float16)
+    qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(ones), dev(oracle.pack_int4(qa)), dev(ones), K,
+                 acc_out=acc)
+    assert np.all(host(acc) == 64 * K)
+
+
+# ---------------------------------------------------------------------------
+# Full-size pipelines, sampled: rotate X and W on the GPU, GEMM on the GPU
+# ---------------------------------------------------------------------------
+FULL = {"llama7b_proj": (48, 64), "down_12288": (24, 48), "llama70b_down": (12, 24)}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_pipeline_sampled(name):
+    cfg = workloads.ACT_CONFIGS[name]
+    inp = act_inputs(name)
+    x16, w16, signs = inp["x"], inp["w"], inp["signs"]
+    say(f"full pipeline {name}: X {x16.shape} W {w16.shape}")
+    xs = dev(signs)
+    qx, sx = qr.had_quant(dev(x16), xs, cfg.m)
+    qw, sw = qr.had_quant(dev(w16), xs, cfg.m)
+    acc = torch.empty((x16.shape[0], w16.shape[0]), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(qx, sx, qw, sw, cfg.d, acc_out=acc)
+    acc_h, y_h = host(acc), host(y)
+    qx_h, sx_h, qw_h, sw_h = host(qx), host(sx), host(qw), host(sw)
+    nr, nc = FULL[name]
+    rng = np.random.default_rng(5)
+    ri = np.unique(np.r_[0, x16.shape[0] - 1, rng.choice(x16.shape[0], nr, replace=False)])
+    ci = np.unique(np.r_[0, w16.shape[0] - 1, rng.choice(w16.shape[0], nc, replace=False)])
+    # the GEMM is exact on whatever codes it was given
+    cx = oracle.unpack_int4(qx_h[ri])
+    cw = oracle.unpack_int4(qw_h[ci])
+    np.testing.assert_array_equal(acc_h[np.ix_(ri, ci)], oracle.int_gemm_exact(cx, cw))
+    # end to end against the oracle pipeline on the sampled rows and columns
+    a = oracle.had_quant(x16[ri], signs, cfg.m)
+    b = oracle.prep_weights(w16[ci], signs, cfg.m)
+    check_scales(sx_h[ri], a["scales"])
+    check_scales(sw_h[ci], b["scales"])
+    check_codes(cx, a["codes"])
+    check_codes(cw, b["codes"])
+    _, y_ref = oracle.w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
+    ys = y_h[np.ix_(ri, ci)]
+    e = check_y_frobenius(ys, y_ref)
+    same = (np.all(cx == a["codes"], axis=1)[:, None] & np.all(cw == b["codes"], axis=1)[None, :]
+            & (sx_h[ri][:, None] == a["scales"][:, None]) & (sw_h[ci][None, :] == b["scales"][None, :]))
+    check_y_elementwise(ys, y_ref, mask=same)
+    say(f"  sampled {len(ri)}x{len(ci)}: frobenius {e:.2e}, exact-code cells {same.mean():.3f}")
+
+
+# ---------------------------------------------------------------------------
+# KV cache path
+# ---------------------------------------------------------------------------
+def test_kv_workload():
+    cfg = workloads.KV_CONFIG
+    inp = workloads.make_kv_inputs(cfg)
+    k16, v16, signs = inp["k"], inp["v"], inp["signs"]
+    B, H, S, D = k16.shape
+    say(f"kv {cfg.name}: K/V {k16.shape}")
+    kq = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda")
+    vq = torch.empty_like(kq)
+    ks = torch.empty((B, H, S), dtype=torch.float16, device="cuda")
+    vs = torch.empty_like(ks)
+    qr.kv_had_quant(dev(k16), dev(v16), dev(signs), kq, ks, vq, vs, pos0=0)
+    kq_h, vq_h, ks_h, vs_h = host(kq), host(vq), host(ks), host(vs)
+    rng = np.random.default_rng(3)
+    flat = rng.choice(B * H * S, 4096, replace=False)
+    for t16, q_h, s_h, nm in ((k16, kq_h, ks_h, "K"), (v16, vq_h, vs_h, "V")):
+        rows = t16.reshape(-1, D)[flat]
+        ref = oracle.had_quant(rows, signs, 1)
+        check_scales(s_h.reshape(-1)[flat], ref["scales"])
+        f = check_codes(oracle.unpack_int4(q_h.reshape(-1, D // 2)[flat]), ref["codes"])
+        say(f"  {nm}: 4096 groups sampled, code diff frac {f:.2e}")
+
+
+def test_kv_positions_strides_and_per_head_signs():
+    rng = np.random.default_rng(21)
+    B, H, S, D, S_cache, pos0 = 3, 4, 37, 128, 64, 19
+    # K stored as [B, S, H, D] and viewed as [B, H, S, D] (non-contiguous)
+    k_bshd = rng.standard_normal((B, S, H, D)).astype(np.float16)
+    v_bshd = rng.standard_normal((B, S, H, D)).astype(np.float16)
+    signs = (1 - 2 * rng.integers(0, 2, (H, D))).astype(np.int8)
+    say("kv positions/strides/per-head signs")
+    k_t = dev(k_bshd).permute(0, 2, 1, 3)
+    v_t = dev(v_bshd).permute(0, 2, 1, 3)
+    kq = torch.full((B, H, S_cache, D // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    vq = torch.full_like(kq, 0xCD)
+    ks = torch.full((B, H, S_cache), -1.0, dtype=torch.float16, device="cuda")
+    vs = torch.full_like(ks, -2.0)
+    qr.kv_had_quant(k_t, v_t, dev(signs), kq, ks, vq, vs, pos0=pos0, signs_stride_h=D)
+    kq_h, vq_h, ks_h, vs_h = host(kq), host(vq), host(ks), host(vs)
+    for src, q_h, s_h, fill_q, fill_s in ((k_bshd, kq_h, ks_h, 0xAB, -1.0),
+                                          (v_bshd, vq_h, vs_h, 0xCD, -2.0)):
+        for h in range(H):
+            rows = src[:, :, h, :].reshape(-1, D)
+            ref = oracle.had_quant(rows, signs[h], 1)
+            got_q = q_h[:, h, pos0:pos0 + S].reshape(-1, D // 2)
+            got_s = s_h[:, h, pos0:pos0 + S].reshape(-1)
+            check_scales(got_s, ref["scales"])
+            check_codes(oracle.unpack_int4(got_q), ref["codes"], frac=1e-2)
+        # cache entries outside [pos0, pos0 + S) untouched
+        assert np.all(q_h[:, :, :pos0] == fill_q) and np.all(q_h[:, :, pos0 + S:] == fill_q)
+        assert np.all(s_h[:, :, :pos0] == fill_s) and np.all(s_h[:, :, pos0 + S:] == fill_s)
+
+
+def test_kv_single_tensor_and_head_dims():
+    rng = np.random.default_rng(4)
+    for D in (32, 64, 128, 256):
+        B, H, S = 2, 3, 11
+        v16 = rng.standard_normal((B, H, S, D)).astype(np.float16)
+        signs = (1 - 2 * rng.integers(0, 2, D)).astype(np.int8)
+        say(f"kv V only D={D}")
+        vq = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda")
+        vs = torch.empty((B, H, S), dtype=torch.float16, device="cuda")
+        qr.kv_had_quant(None, dev(v16), dev(signs), None, None, vq, vs)
+        ref = oracle.had_quant(v16.reshape(-1, D), signs, 1)
+        check_scales(host(vs).reshape(-1), ref["scales"])
+        check_codes(oracle.unpack_int4(host(vq).reshape(-1, D // 2)), ref["codes"], frac=1e-2)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases of rotate+quant
+# ---------------------------------------------------------------------------
+def test_had_quant_strided_rows_clip_and_zero_rows():
+    rng = np.random.default_rng(9)
+    rows, d, ld = 45, 4096, 4096 + 64
+    buf = rng.standard_normal((rows, ld)).astype(np.float16)
+    buf[3] = 0  # an all-zero row
+    signs = (1 - 2 * rng.integers(0, 2, d)).astype(np.int8)
+    say("had_quant strided rows, clip 0.9, zero row")
+    xt = dev(buf)[:, :d]
+    qbuf = torch.full((rows, d // 2 + 32), 0x5A, dtype=torch.uint8, device="cuda")
+    q_view = qbuf[:, : d // 2]
+    s = torch.empty(rows, dtype=torch.float16, device="cuda")
+    qr.had_quant(xt, dev(signs), 1, 0.9, q_out=q_view, scale_out=s)
+    ref = oracle.had_quant(buf[:, :d], signs, 1, 0.9)
+    qh = host(qbuf)
+    assert np.all(qh[:, d // 2:] == 0x5A)
+    check_scales(host(s), ref["scales"])
+    check_codes(oracle.unpack_int4(qh[:, : d // 2]), ref["codes"])
+    assert np.all(qh[3, : d // 2] == 0)
+
+
+def test_had_quant_no_signs_single_row_and_determinism():
+    rng = np.random.default_rng(12)
+    for d, m in ((256, 1), (4096, 1), (12288, 12), (28672, 28)):
+        x16 = rng.standard_normal((1, d)).astype(np.float16)
+        say(f"had_quant single row no signs d={d}")
+        q1, s1, _ = gpu_had_quant(x16, None, m, with_rot=False)
+        q2, s2, _ = gpu_had_quant(x16, None, m, with_rot=False)
+        np.testing.assert_array_equal(q1, q2)
+        np.testing.assert_array_equal(s1, s2)
+        ref = oracle.had_quant(x16, np.ones(d, np.int8), m)
+        check_scales(s1, ref["scales"])
+        check_codes(oracle.unpack_int4(q1), ref["codes"], frac=1e-2)
