@@ -102,7 +102,7 @@ int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
  *   b_q        packed int4 weights, uint8 [N x ldb] (one row per output
  *              channel), same alignment rules as a_q.
  *   b_scale    fp16 [N] per-output-channel scales.
- *   c          fp16 [M x ldc] output, ldc >= N, 4-byte aligned, ldc % 2 == 0.
+ *   c          fp16 [M x ldc] output, ldc >= N, 2-byte aligned.
  *   acc_out    optional int32 [M x ld_acc] receiving acc (ld_acc >= N);
  *              NULL in production.
  * Supported: M, N >= 0 (0 is a no-op), K > 0 with K % 32 == 0 and

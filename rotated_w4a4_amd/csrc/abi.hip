@@ -126,8 +126,7 @@ int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
                QUAROT_ERR_MISALIGNED, "a_q/b_q must be 16-byte aligned with lda, ldb %% 16 == 0");
   QR_CHECK_ARG(aligned(a_scale, 2) && aligned(b_scale, 2), QUAROT_ERR_MISALIGNED,
                "scales must be 2-byte aligned");
-  QR_CHECK_ARG(aligned(c, 4) && ldc % 2 == 0, QUAROT_ERR_MISALIGNED,
-               "c must be 4-byte aligned with ldc %% 2 == 0");
+  QR_CHECK_ARG(aligned(c, 2), QUAROT_ERR_MISALIGNED, "c must be 2-byte aligned");
   QR_CHECK_ARG(acc_out == nullptr || aligned(acc_out, 4), QUAROT_ERR_MISALIGNED,
                "acc_out must be 4-byte aligned");
   QR_CHECK_ARG(M < (int64_t(1) << 31) && N < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED,

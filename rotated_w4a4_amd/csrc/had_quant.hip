@@ -11,11 +11,14 @@
 //
 // Kernels:
 //   * had_quant_quad<D>   d = 32..256: a quad of lanes per row (quad_rows.h).
+//   * had_quant_4096      d = 4096: a wave per row, one LDS exchange
+//                         (wave_rows.h).
 //   * had_quant_lds<M>    any supported d (<= 32768): one workgroup per row,
 //                         the row staged in LDS as fp32; H_m applied per
 //                         contiguous group, then radix-32 FWHT passes over
 //                         the power-of-two index.
 #include "quad_rows.h"
+#include "wave_rows.h"
 
 namespace quarot {
 
@@ -204,6 +207,20 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
       default: hipLaunchKernelGGL(had_quant_quad<256>, grid, block, 0, stream, x, rows, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out); break;
     }
     return check_launch("had_quant_quad");
+  }
+  if (m == 1 && d == 4096) {
+    const int64_t rpb = kWaveRowsBlock / 64;
+    int64_t blocks = (rows + rpb - 1) / rpb;
+    const int64_t cap = int64_t(cus) * 2;  // 64 KiB LDS per block: two blocks per CU
+    if (blocks > cap) blocks = cap;
+    const dim3 grid{unsigned(blocks)}, block{unsigned(kWaveRowsBlock)};
+    if (clip_ratio == 1.0f)
+      hipLaunchKernelGGL(had_quant_4096<false>, grid, block, 0, stream, x, rows, ld_x, signs,
+                         clip_ratio, q_out, ld_q, scale_out, x_rot_out);
+    else
+      hipLaunchKernelGGL(had_quant_4096<true>, grid, block, 0, stream, x, rows, ld_x, signs,
+                         clip_ratio, q_out, ld_q, scale_out, x_rot_out);
+    return check_launch("had_quant_4096");
   }
   const size_t lds = size_t(d + d / 32) * sizeof(float);
   // rows above 16K elements need more than the default 64 KiB of dynamic LDS

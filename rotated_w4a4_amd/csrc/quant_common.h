@@ -54,3 +54,40 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 }  // namespace quarot
+
+namespace quarot {
+
+// Round to nearest integer by the float "magic number" addition: for
+// |v| < 2^22, fma(y, k, 1.5 * 2^23 + 8) rounds y * k to the nearest integer
+// q (ties to even, the current rounding mode) and leaves q + 8 in the low
+// bits of the result, so byte 0 of its bit pattern is q + 8 in [0, 15]
+// whenever q is in [-8, 7].
+constexpr float kMagic8 = 12582912.0f + 8.0f;
+
+// q + 8 in byte 0 of the returned float's bits; CLAMP limits q to [-8, 7].
+template <bool CLAMP>
+__device__ __forceinline__ float magic_code(float y, float k) {
+  float t = fmaf(y, k, kMagic8);
+  if (CLAMP) t = fminf(fmaxf(t, kMagic8 - 8.0f), kMagic8 + 7.0f);
+  return t;
+}
+
+// Byte 0 of four words, gathered into one word (a in byte 0 ... d in byte 3).
+__device__ __forceinline__ uint32_t gather_byte0(float a, float b, float c, float d) {
+  const uint32_t ab = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b),
+                                            __builtin_bit_cast(uint32_t, a), 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d),
+                                            __builtin_bit_cast(uint32_t, c), 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Eight magic_code results (element i in t[i]) -> one word, code i in nibble i
+// as 4-bit two's complement: evens fill the low nibbles of each byte, odds
+// the high nibbles, and xor 8 turns the q + 8 offset into two's complement.
+__device__ __forceinline__ uint32_t pack8_magic(const float* t) {
+  const uint32_t ev = gather_byte0(t[0], t[2], t[4], t[6]);
+  const uint32_t od = gather_byte0(t[1], t[3], t[5], t[7]);
+  return ((od << 4) | ev) ^ 0x88888888u;
+}
+
+}  // namespace quarot

@@ -117,8 +117,7 @@ def _gemm(lib, **kw):
     (dict(a=FAKE + 8), MISALIGNED),
     (dict(lda=72), MISALIGNED),
     (dict(sa=FAKE + 1), MISALIGNED),
-    (dict(c=FAKE + 2), MISALIGNED),
-    (dict(ldc=17), MISALIGNED),
+    (dict(c=FAKE + 1), MISALIGNED),
     (dict(acc=FAKE + 2, ld_acc=16), MISALIGNED),
 ])
 def test_gemm_rejects(lib, kw, status):
