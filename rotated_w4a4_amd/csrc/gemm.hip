@@ -19,11 +19,12 @@
 //
 // Tiling.  Workgroup tile 128 (M) x 256 (N) x 128 (K), 4 waves of 64 x 128,
 // each wave 2 x 4 blocks of v_mfma_i32_32x32x32_i8.  Packed tiles are staged
-// in LDS (double buffered, rows padded to 80 bytes).  Each lane reads 16
-// packed bytes per block and K-pair: the first 8 feed one MFMA, the last 8
-// the next, so lane half h covers K offsets [32h, 32h + 32) of a 64-wide
-// K-pair.  Tiles are assigned XCD-major: consecutive tile ids go to the same
-// XCD so neighbouring tiles share its L2.
+// in LDS (two buffers, 16-byte chunks XOR-swizzled per row); a third tile
+// waits in registers, so global loads are issued two tiles ahead of use.
+// Each lane reads 16 packed bytes per block and K-pair: the first 8 feed
+// one MFMA, the last 8 the next, so lane half h covers K offsets
+// [32h, 32h + 32) of a 64-wide K-pair.  Tiles are assigned XCD-major:
+// consecutive tile ids go to the same XCD so neighbouring tiles share its L2.
 #include "common.h"
 
 namespace quarot {
@@ -36,14 +37,22 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = 128;             // int4 elements per K tile
-constexpr int BKB = BK / 2;         // bytes per row per K tile (64)
-constexpr int LDS_STRIDE = 80;      // padded row stride in bytes
+constexpr int BKB = BK / 2;         // bytes per row per K tile (64 = four 16-byte chunks)
 constexpr int kThreads = 256;
 constexpr int A_CHUNKS = BM * BKB / 16 / kThreads;  // 16-byte loads per thread: 2
 constexpr int B_CHUNKS = BN * BKB / 16 / kThreads;  // 4
 constexpr int WM = 64, WN = 128;    // wave tile
 constexpr int FM = WM / 32, FN = WN / 32;  // MFMA blocks per wave: 2 x 4
 constexpr int GROUP_M = 4;
+constexpr int STAGE_BYTES = (BM + BN) * BKB;  // one K tile of A and B in LDS
+
+// LDS rows are 64 bytes (no padding); 16-byte chunk c of row r lives at
+// chunk slot c ^ swz(r).  Sixteen consecutive rows reading the same logical
+// chunk then hit sixteen different 16-byte bank groups (and eight
+// consecutive rows eight different groups), and a row's four chunks stay
+// inside its own 64 bytes, so the cooperative stores are conflict-free too.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BKB + ((c ^ swz(r)) << 4); }
 
 __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
   lo[0] = int((p.x << 4) & 0xF0F0F0F0u);
@@ -56,12 +65,49 @@ __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
   hi[3] = int(p.w & 0xF0F0F0F0u);
 }
 
+// One K tile of a thread's share: two 16-byte chunks of A, four of B.
+struct TileRegs {
+  uint4 a0, a1, b0, b1, b2, b3;
+};
+static_assert(A_CHUNKS == 2 && B_CHUNKS == 4, "TileRegs holds 2 + 4 chunks");
+
+// Per-thread global row pointers (rows lrow + 64 i of the A and B tiles).
+struct TilePtrs {
+  const uint8_t *a0, *a1, *b0, *b1, *b2, *b3;
+};
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void load_tile(const TilePtrs& p, int kb0, TileRegs& r) {
+  r.a0 = ld16(p.a0 + kb0);
+  r.a1 = ld16(p.a1 + kb0);
+  r.b0 = ld16(p.b0 + kb0);
+  r.b1 = ld16(p.b1 + kb0);
+  r.b2 = ld16(p.b2 + kb0);
+  r.b3 = ld16(p.b3 + kb0);
+}
+
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4& v) {
+  return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_tile(uint8_t* st, int lrow, int lchunk, const TileRegs& r) {
+  *reinterpret_cast<uint4*>(st + lds_off(lrow, lchunk)) = r.a0;
+  *reinterpret_cast<uint4*>(st + lds_off(lrow + 64, lchunk)) = r.a1;
+  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow, lchunk)) = r.b0;
+  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow + 64, lchunk)) = r.b1;
+  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow + 128, lchunk)) = r.b2;
+  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow + 192, lchunk)) = r.b3;
+}
+
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ a_q, int64_t lda, const __half* __restrict__ a_scale,
     const uint8_t* __restrict__ b_q, int64_t ldb, const __half* __restrict__ b_scale,
     int M, int N, int K, __half* __restrict__ c, int64_t ldc, int32_t* __restrict__ acc_out,
     int64_t ld_acc, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][STAGE_BYTES];
 
   // --- tile assignment: XCD-major, then grouped along M -------------------
   const int total = tiles_m * tiles_n;
@@ -81,45 +127,18 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
   const int wn = (wave & 1) * WN;   // wave col offset inside the tile
   const int kbytes = K >> 1;
 
-  // global -> register staging of one K tile
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-  auto load_tile = [&](int kt) {
-    const int kb0 = kt * BKB;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx >> 2, col = (cidx & 3) * 16;
-      const int gr = min(m0 + row, M - 1);
-      if (kb0 + col < kbytes)
-        ra[i] = *reinterpret_cast<const uint4*>(a_q + int64_t(gr) * lda + kb0 + col);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx >> 2, col = (cidx & 3) * 16;
-      const int gr = min(n0 + row, N - 1);
-      if (kb0 + col < kbytes)
-        rb[i] = *reinterpret_cast<const uint4*>(b_q + int64_t(gr) * ldb + kb0 + col);
-      else
-        rb[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx >> 2, col = (cidx & 3) * 16;
-      *reinterpret_cast<uint4*>(&smem[buf][row * LDS_STRIDE + col]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int row = cidx >> 2, col = (cidx & 3) * 16;
-      *reinterpret_cast<uint4*>(&smem[buf][(BM + row) * LDS_STRIDE + col]) = rb[i];
-    }
-  };
+  // each thread moves chunk (tid & 3) of rows tid/4 + 64 i; rows past the
+  // matrix edge re-read the last row (their results are never stored)
+  const int lrow = tid >> 2, lchunk = tid & 3;
+  TilePtrs tp;
+  tp.a0 = a_q + int64_t(min(m0 + lrow, M - 1)) * lda + 16 * lchunk;
+  tp.a1 = a_q + int64_t(min(m0 + lrow + 64, M - 1)) * lda + 16 * lchunk;
+  tp.b0 = b_q + int64_t(min(n0 + lrow, N - 1)) * ldb + 16 * lchunk;
+  tp.b1 = b_q + int64_t(min(n0 + lrow + 64, N - 1)) * ldb + 16 * lchunk;
+  tp.b2 = b_q + int64_t(min(n0 + lrow + 128, N - 1)) * ldb + 16 * lchunk;
+  tp.b3 = b_q + int64_t(min(n0 + lrow + 192, N - 1)) * ldb + 16 * lchunk;
+  const int kfull = kbytes / BKB;  // tiles entirely inside K
+  const bool has_tail = (kbytes % BKB) != 0;
 
   v16i acc[FM][FN];
 #pragma unroll
@@ -127,32 +146,22 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
-  const int ktiles = (K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  const int frow = lane & 31;       // row (A) / column (B) of the fragment
-  const int fcol = (lane >> 5) * 16;  // byte offset of this lane half in a K-pair
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ktiles) load_tile(kt + 1);
-    const uint8_t* sa = &smem[buf][0];
-    const uint8_t* sb = &smem[buf][BM * LDS_STRIDE];
+  const int frow = lane & 31;   // row (A) / column (B) of the fragment
+  const int fhalf = lane >> 5;  // which 16-byte chunk of a 32-byte K-pair
+  auto compute_tile = [&](int buf) {
+    const uint8_t* sa = smem[buf];
+    const uint8_t* sb = smem[buf] + BM * BKB;
 #pragma unroll
     for (int kp = 0; kp < BKB / 32; ++kp) {  // two 64-wide K-pairs per tile
       v4i alo[FM], ahi[FM], blo[FN], bhi[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint4 p = *reinterpret_cast<const uint4*>(
-            sa + (wm + i * 32 + frow) * LDS_STRIDE + kp * 32 + fcol);
+        const uint4 p = *reinterpret_cast<const uint4*>(sa + lds_off(wm + i * 32 + frow, 2 * kp + fhalf));
         widen(p, alo[i], ahi[i]);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const uint4 p = *reinterpret_cast<const uint4*>(
-            sb + (wn + j * 32 + frow) * LDS_STRIDE + kp * 32 + fcol);
+        const uint4 p = *reinterpret_cast<const uint4*>(sb + lds_off(wn + j * 32 + frow, 2 * kp + fhalf));
         widen(p, blo[j], bhi[j]);
       }
 #pragma unroll
@@ -163,8 +172,52 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[i], bhi[j], acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < ktiles) store_tile(buf ^ 1);
+  };
+
+  // Pipeline over the full tiles: tile kt is computed from LDS while tile
+  // kt+1 waits in registers and tile kt+2 is in flight from memory.  The
+  // loop is unrolled by two so each register set keeps a fixed role, and
+  // loads are issued every step (past the end they re-read the last full
+  // tile) so every path through the loop has the same wait counts.
+  TileRegs r0, r1;
+  if (kfull > 0) {
+    load_tile(tp, 0, r0);
+    load_tile(tp, min(1, kfull - 1) * BKB, r1);
+    store_tile(smem[0], lrow, lchunk, r0);
     __syncthreads();
+    int kt = 0;
+    // sched_barrier keeps the compiler from sinking the loads below the
+    // MFMAs (which would shorten the time they have to arrive)
+    for (; kt + 2 <= kfull; kt += 2) {
+      load_tile(tp, min(kt + 2, kfull - 1) * BKB, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(0);                        // tile kt
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(smem[1], lrow, lchunk, r1);  // tile kt+1
+      __syncthreads();
+      load_tile(tp, min(kt + 3, kfull - 1) * BKB, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(1);                        // tile kt+1
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(smem[0], lrow, lchunk, r0);  // tile kt+2 (a harmless repeat past the end)
+      __syncthreads();
+    }
+    if (kt < kfull) compute_tile(0);  // odd count: the last full tile is in buffer 0
+  }
+  if (has_tail) {  // the partial tile at the end of K: chunks past K read as zero
+    __syncthreads();
+    const int kb0 = kfull * BKB;
+    const bool ok = kb0 + 16 * lchunk < kbytes;
+    load_tile(tp, ok ? kb0 : 0, r0);
+    r0.a0 = keep_if(ok, r0.a0);
+    r0.a1 = keep_if(ok, r0.a1);
+    r0.b0 = keep_if(ok, r0.b0);
+    r0.b1 = keep_if(ok, r0.b1);
+    r0.b2 = keep_if(ok, r0.b2);
+    r0.b3 = keep_if(ok, r0.b3);
+    store_tile(smem[1], lrow, lchunk, r0);
+    __syncthreads();
+    compute_tile(1);
   }
 
   // --- epilogue: acc / 256 -> fp32 * scale_x * scale_w -> fp16 -----------
