@@ -41,6 +41,7 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 CACHE_DEFEAT_BYTES = 1 << 30
+SPIN_CYCLES = 200_000_000  # ~0.1 s of GPU spin before event-timed launches
 
 
 def log(msg: str) -> None:
@@ -140,13 +141,21 @@ def bench_act(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     log(f"warmup done; timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # (1) the timed region: exactly K steps between two synchronisations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # (2) per-kernel durations from HIP events on the launch stream.  A spin
+    # kernel keeps the GPU busy while the host enqueues every step, so the
+    # events see back-to-back GPU work and no host launch latency.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda._sleep(SPIN_CYCLES)
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     rq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     rq_bytes = 2 * T * d + T * d // 2 + 2 * T
@@ -231,14 +240,18 @@ def bench_kv(args, torch, qr) -> dict:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda._sleep(SPIN_CYCLES)
     for i in range(args.steps):
         evs[i][0].record(stream)
         step(i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     nbytes = per_set
     gbs = nbytes / (ms * 1e-3) / 1e9

@@ -17,14 +17,16 @@
 // accumulator holds 256 * acc exactly (256 * 64 * K <= 2^30 for K <= 65536)
 // and the epilogue shifts it right by 8.
 //
-// Tiling.  Workgroup tile 128 (M) x 256 (N) x 128 (K), 4 waves of 64 x 128,
-// each wave 2 x 4 blocks of v_mfma_i32_32x32x32_i8.  Packed tiles are staged
-// in LDS (two buffers, 16-byte chunks XOR-swizzled per row); a third tile
-// waits in registers, so global loads are issued two tiles ahead of use.
-// Each lane reads 16 packed bytes per block and K-pair: the first 8 feed
-// one MFMA, the last 8 the next, so lane half h covers K offsets
+// Tiling.  Workgroup tile BM x BN x 128 (K), waves of WM x WN, each wave
+// (WM/32) x (WN/32) blocks of v_mfma_i32_32x32x32_i8.  Packed tiles are
+// staged in LDS (two buffers, 16-byte chunks XOR-swizzled per row); a third
+// tile waits in registers, so global loads are issued two tiles ahead of
+// use.  Each lane reads 16 packed bytes per block and K-pair: the first 8
+// feed one MFMA, the last 8 the next, so lane half h covers K offsets
 // [32h, 32h + 32) of a 64-wide K-pair.  Tiles are assigned XCD-major:
 // consecutive tile ids go to the same XCD so neighbouring tiles share its L2.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace quarot {
@@ -34,17 +36,9 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;
-constexpr int BN = 256;
-constexpr int BK = 128;             // int4 elements per K tile
-constexpr int BKB = BK / 2;         // bytes per row per K tile (64 = four 16-byte chunks)
-constexpr int kThreads = 256;
-constexpr int A_CHUNKS = BM * BKB / 16 / kThreads;  // 16-byte loads per thread: 2
-constexpr int B_CHUNKS = BN * BKB / 16 / kThreads;  // 4
-constexpr int WM = 64, WN = 128;    // wave tile
-constexpr int FM = WM / 32, FN = WN / 32;  // MFMA blocks per wave: 2 x 4
+constexpr int BK = 128;      // int4 elements per K tile
+constexpr int BKB = BK / 2;  // bytes per row per K tile (64 = four 16-byte chunks)
 constexpr int GROUP_M = 4;
-constexpr int STAGE_BYTES = (BM + BN) * BKB;  // one K tile of A and B in LDS
 
 // LDS rows are 64 bytes (no padding); 16-byte chunk c of row r lives at
 // chunk slot c ^ swz(r).  Sixteen consecutive rows reading the same logical
@@ -65,49 +59,36 @@ __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
   hi[3] = int(p.w & 0xF0F0F0F0u);
 }
 
-// One K tile of a thread's share: two 16-byte chunks of A, four of B.
-struct TileRegs {
-  uint4 a0, a1, b0, b1, b2, b3;
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <int WAVES_M_, int WAVES_N_, int WM_, int WN_>
+struct GemmCfg {
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int ROWS = BM + BN;            // A rows then B rows of a tile
+  static constexpr int CH = ROWS * 4 / THREADS;   // 16-byte chunks per thread per tile
+  static constexpr int ROWS_PER_PASS = THREADS / 4;
+  static constexpr int STAGE = ROWS * BKB;
+  static_assert(ROWS * 4 % THREADS == 0, "tile rows must split evenly over threads");
+  static_assert(BM % ROWS_PER_PASS == 0, "a load pass must not straddle A and B");
 };
-static_assert(A_CHUNKS == 2 && B_CHUNKS == 4, "TileRegs holds 2 + 4 chunks");
 
-// Per-thread global row pointers (rows lrow + 64 i of the A and B tiles).
-struct TilePtrs {
-  const uint8_t *a0, *a1, *b0, *b1, *b2, *b3;
-};
+// 4 waves of 64 x 128: BM = 128, BN = 256, one wave per SIMD.
+using Cfg4 = GemmCfg<2, 2, 64, 128>;
+// 8 waves of 64 x 64: BM = 128, BN = 256, two waves per SIMD.
+using Cfg8 = GemmCfg<2, 4, 64, 64>;
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-__device__ __forceinline__ void load_tile(const TilePtrs& p, int kb0, TileRegs& r) {
-  r.a0 = ld16(p.a0 + kb0);
-  r.a1 = ld16(p.a1 + kb0);
-  r.b0 = ld16(p.b0 + kb0);
-  r.b1 = ld16(p.b1 + kb0);
-  r.b2 = ld16(p.b2 + kb0);
-  r.b3 = ld16(p.b3 + kb0);
-}
-
-__device__ __forceinline__ uint4 keep_if(bool ok, const uint4& v) {
-  return ok ? v : make_uint4(0, 0, 0, 0);
-}
-
-__device__ __forceinline__ void store_tile(uint8_t* st, int lrow, int lchunk, const TileRegs& r) {
-  *reinterpret_cast<uint4*>(st + lds_off(lrow, lchunk)) = r.a0;
-  *reinterpret_cast<uint4*>(st + lds_off(lrow + 64, lchunk)) = r.a1;
-  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow, lchunk)) = r.b0;
-  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow + 64, lchunk)) = r.b1;
-  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow + 128, lchunk)) = r.b2;
-  *reinterpret_cast<uint4*>(st + BM * BKB + lds_off(lrow + 192, lchunk)) = r.b3;
-}
-
-__global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ a_q, int64_t lda, const __half* __restrict__ a_scale,
     const uint8_t* __restrict__ b_q, int64_t ldb, const __half* __restrict__ b_scale,
     int M, int N, int K, __half* __restrict__ c, int64_t ldc, int32_t* __restrict__ acc_out,
     int64_t ld_acc, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][STAGE_BYTES];
+  constexpr int FM = C::FM, FN = C::FN, CH = C::CH, BM = C::BM, BN = C::BN;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][C::STAGE];
 
   // --- tile assignment: XCD-major, then grouped along M -------------------
   const int total = tiles_m * tiles_n;
@@ -123,20 +104,21 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = (wave >> 1) * WM;  // wave row offset inside the tile
-  const int wn = (wave & 1) * WN;   // wave col offset inside the tile
+  const int wm = (wave / C::WAVES_N) * C::WM;  // wave row offset inside the tile
+  const int wn = (wave % C::WAVES_N) * C::WN;  // wave col offset inside the tile
   const int kbytes = K >> 1;
 
-  // each thread moves chunk (tid & 3) of rows tid/4 + 64 i; rows past the
-  // matrix edge re-read the last row (their results are never stored)
+  // Thread tid moves chunk (tid & 3) of tile rows tid/4 + ROWS_PER_PASS * i
+  // (A rows first, then B rows); rows past the matrix edge re-read the last
+  // row (their results are never stored).
   const int lrow = tid >> 2, lchunk = tid & 3;
-  TilePtrs tp;
-  tp.a0 = a_q + int64_t(min(m0 + lrow, M - 1)) * lda + 16 * lchunk;
-  tp.a1 = a_q + int64_t(min(m0 + lrow + 64, M - 1)) * lda + 16 * lchunk;
-  tp.b0 = b_q + int64_t(min(n0 + lrow, N - 1)) * ldb + 16 * lchunk;
-  tp.b1 = b_q + int64_t(min(n0 + lrow + 64, N - 1)) * ldb + 16 * lchunk;
-  tp.b2 = b_q + int64_t(min(n0 + lrow + 128, N - 1)) * ldb + 16 * lchunk;
-  tp.b3 = b_q + int64_t(min(n0 + lrow + 192, N - 1)) * ldb + 16 * lchunk;
+  const uint8_t* src[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int r = lrow + C::ROWS_PER_PASS * i;
+    src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * lchunk
+                      : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb + 16 * lchunk;
+  }
   const int kfull = kbytes / BKB;  // tiles entirely inside K
   const bool has_tail = (kbytes % BKB) != 0;
 
@@ -155,15 +137,11 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
     for (int kp = 0; kp < BKB / 32; ++kp) {  // two 64-wide K-pairs per tile
       v4i alo[FM], ahi[FM], blo[FN], bhi[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint4 p = *reinterpret_cast<const uint4*>(sa + lds_off(wm + i * 32 + frow, 2 * kp + fhalf));
-        widen(p, alo[i], ahi[i]);
-      }
+      for (int i = 0; i < FM; ++i)
+        widen(ld16(sa + lds_off(wm + i * 32 + frow, 2 * kp + fhalf)), alo[i], ahi[i]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint4 p = *reinterpret_cast<const uint4*>(sb + lds_off(wn + j * 32 + frow, 2 * kp + fhalf));
-        widen(p, blo[j], bhi[j]);
-      }
+      for (int j = 0; j < FN; ++j)
+        widen(ld16(sb + lds_off(wn + j * 32 + frow, 2 * kp + fhalf)), blo[j], bhi[j]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -179,27 +157,32 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
   // loop is unrolled by two so each register set keeps a fixed role, and
   // loads are issued every step (past the end they re-read the last full
   // tile) so every path through the loop has the same wait counts.
-  TileRegs r0, r1;
+  uint4 r0[CH], r1[CH];
+#define QR_LOAD(r, kb0)                                          \
+  _Pragma("unroll") for (int i = 0; i < CH; ++i) r[i] = ld16(src[i] + (kb0))
+#define QR_STORE(buf, r)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < CH; ++i) *reinterpret_cast<uint4*>(               \
+      smem[buf] + lds_off(lrow + C::ROWS_PER_PASS * i, lchunk)) = r[i]
   if (kfull > 0) {
-    load_tile(tp, 0, r0);
-    load_tile(tp, min(1, kfull - 1) * BKB, r1);
-    store_tile(smem[0], lrow, lchunk, r0);
+    QR_LOAD(r0, 0);
+    QR_LOAD(r1, min(1, kfull - 1) * BKB);
+    QR_STORE(0, r0);
     __syncthreads();
     int kt = 0;
     // sched_barrier keeps the compiler from sinking the loads below the
     // MFMAs (which would shorten the time they have to arrive)
     for (; kt + 2 <= kfull; kt += 2) {
-      load_tile(tp, min(kt + 2, kfull - 1) * BKB, r0);
+      QR_LOAD(r0, min(kt + 2, kfull - 1) * BKB);
       __builtin_amdgcn_sched_barrier(0);
-      compute_tile(0);                        // tile kt
+      compute_tile(0);  // tile kt
       __builtin_amdgcn_sched_barrier(0);
-      store_tile(smem[1], lrow, lchunk, r1);  // tile kt+1
+      QR_STORE(1, r1);  // tile kt+1
       __syncthreads();
-      load_tile(tp, min(kt + 3, kfull - 1) * BKB, r1);
+      QR_LOAD(r1, min(kt + 3, kfull - 1) * BKB);
       __builtin_amdgcn_sched_barrier(0);
-      compute_tile(1);                        // tile kt+1
+      compute_tile(1);  // tile kt+1
       __builtin_amdgcn_sched_barrier(0);
-      store_tile(smem[0], lrow, lchunk, r0);  // tile kt+2 (a harmless repeat past the end)
+      QR_STORE(0, r0);  // tile kt+2 (a harmless repeat past the end)
       __syncthreads();
     }
     if (kt < kfull) compute_tile(0);  // odd count: the last full tile is in buffer 0
@@ -208,26 +191,32 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
     __syncthreads();
     const int kb0 = kfull * BKB;
     const bool ok = kb0 + 16 * lchunk < kbytes;
-    load_tile(tp, ok ? kb0 : 0, r0);
-    r0.a0 = keep_if(ok, r0.a0);
-    r0.a1 = keep_if(ok, r0.a1);
-    r0.b0 = keep_if(ok, r0.b0);
-    r0.b1 = keep_if(ok, r0.b1);
-    r0.b2 = keep_if(ok, r0.b2);
-    r0.b3 = keep_if(ok, r0.b3);
-    store_tile(smem[1], lrow, lchunk, r0);
+    QR_LOAD(r0, ok ? kb0 : 0);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) r0[i] = ok ? r0[i] : make_uint4(0, 0, 0, 0);
+    QR_STORE(1, r0);
     __syncthreads();
     compute_tile(1);
   }
+#undef QR_LOAD
+#undef QR_STORE
 
   // --- epilogue: acc / 256 -> fp32 * scale_x * scale_w -> fp16 -----------
   // 32x32 block layout: lane holds column (lane & 31); register r holds row
   // 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
+  float sx[FM][16];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      sx[i][r] = __half2float(a_scale[min(row, M - 1)]);
+    }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int col = n0 + wn + j * 32 + (lane & 31);
     const bool col_ok = col < N;
-    const float sw = col_ok ? __half2float(b_scale[col]) : 0.0f;
+    const float sw = __half2float(b_scale[min(col, N - 1)]);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -235,12 +224,28 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(
         const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (!col_ok || row >= M) continue;
         const int32_t v = acc[i][j][r] >> 8;
-        const float sx = __half2float(a_scale[row]);
-        c[int64_t(row) * ldc + col] = __float2half_rn((float(v) * sx) * sw);
+        c[int64_t(row) * ldc + col] = __float2half_rn((float(v) * sx[i][r]) * sw);
         if (acc_out) acc_out[int64_t(row) * ld_acc + col] = v;
       }
     }
   }
+}
+
+template <class C>
+int launch_cfg(const uint8_t* a_q, int64_t lda, const __half* a_scale, const uint8_t* b_q,
+               int64_t ldb, const __half* b_scale, int64_t M, int64_t N, int64_t K, __half* c,
+               int64_t ldc, int32_t* acc_out, int64_t ld_acc, hipStream_t stream) {
+  const int tiles_m = int((M + C::BM - 1) / C::BM);
+  const int tiles_n = int((N + C::BN - 1) / C::BN);
+  const int64_t total = int64_t(tiles_m) * tiles_n;
+  if (total > 0x7fffffff) {
+    set_error("too many tiles");
+    return QUAROT_ERR_UNSUPPORTED;
+  }
+  hipLaunchKernelGGL(w4a4_gemm_kernel<C>, dim3(unsigned(total)), dim3(C::THREADS), 0, stream,
+                     a_q, lda, a_scale, b_q, ldb, b_scale, int(M), int(N), int(K), c, ldc,
+                     acc_out, ld_acc, tiles_m, tiles_n);
+  return check_launch("w4a4_gemm");
 }
 
 }  // namespace
@@ -249,17 +254,15 @@ int launch_w4a4_gemm(const uint8_t* a_q, int64_t lda, const __half* a_scale,
                      const uint8_t* b_q, int64_t ldb, const __half* b_scale,
                      int64_t M, int64_t N, int64_t K, __half* c, int64_t ldc,
                      int32_t* acc_out, int64_t ld_acc, hipStream_t stream) {
-  const int tiles_m = int((M + BM - 1) / BM);
-  const int tiles_n = int((N + BN - 1) / BN);
-  const int64_t total = int64_t(tiles_m) * tiles_n;
-  if (total > 0x7fffffff) {
-    set_error("too many tiles");
-    return QUAROT_ERR_UNSUPPORTED;
-  }
-  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3(unsigned(total)), dim3(kThreads), 0, stream, a_q,
-                     lda, a_scale, b_q, ldb, b_scale, int(M), int(N), int(K), c, ldc, acc_out,
-                     ld_acc, tiles_m, tiles_n);
-  return check_launch("w4a4_gemm");
+  static const int variant = [] {
+    const char* e = getenv("QUAROT_GEMM_VARIANT");
+    return e ? atoi(e) : 8;
+  }();
+  if (variant == 4)
+    return launch_cfg<Cfg4>(a_q, lda, a_scale, b_q, ldb, b_scale, M, N, K, c, ldc, acc_out,
+                            ld_acc, stream);
+  return launch_cfg<Cfg8>(a_q, lda, a_scale, b_q, ldb, b_scale, M, N, K, c, ldc, acc_out,
+                          ld_acc, stream);
 }
 
 }  // namespace quarot
