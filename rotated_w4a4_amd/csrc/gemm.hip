@@ -19,14 +19,13 @@
 //
 // Tiling.  Workgroup tile BM x BN x 128 (K), waves of WM x WN, each wave
 // (WM/32) x (WN/32) blocks of v_mfma_i32_32x32x32_i8.  Packed tiles are
-// staged in LDS (two buffers, 16-byte chunks XOR-swizzled per row); a third
-// tile waits in registers, so global loads are issued two tiles ahead of
-// use.  Each lane reads 16 packed bytes per block and K-pair: the first 8
-// feed one MFMA, the last 8 the next, so lane half h covers K offsets
-// [32h, 32h + 32) of a 64-wide K-pair.  Tiles are assigned XCD-major:
+// staged in LDS (two buffers, 16-byte chunks XOR-swizzled per row); two more
+// tiles are in flight into registers, so global loads are issued two tiles
+// ahead of use and each K step has a single barrier.  Each lane reads 16
+// packed bytes per block and K-pair: the first 8 feed one MFMA, the last 8
+// the next, so lane half h covers K offsets [32h, 32h + 32) of a 64-wide
+// K-pair.  Tiles are assigned XCD-major:
 // consecutive tile ids go to the same XCD so neighbouring tiles share its L2.
-#include <cstdlib>
-
 #include "common.h"
 
 namespace quarot {
@@ -36,17 +35,22 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 128;      // int4 elements per K tile
-constexpr int BKB = BK / 2;  // bytes per row per K tile (64 = four 16-byte chunks)
 constexpr int GROUP_M = 4;
 
-// LDS rows are 64 bytes (no padding); 16-byte chunk c of row r lives at
-// chunk slot c ^ swz(r).  Sixteen consecutive rows reading the same logical
-// chunk then hit sixteen different 16-byte bank groups (and eight
-// consecutive rows eight different groups), and a row's four chunks stay
-// inside its own 64 bytes, so the cooperative stores are conflict-free too.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BKB + ((c ^ swz(r)) << 4); }
+// LDS holds one K tile per buffer, row-major with BKB-byte rows (no
+// padding).  The LDS has 64 four-byte banks and serves a 128-bit read for 16
+// lanes per cycle, so the 16 rows a fragment read touches (same logical
+// 16-byte chunk) must land in 16 different 16-byte slots of a 256-byte bank
+// period.  Chunk c of row r is stored at chunk slot c ^ swz(r); with 64-byte
+// rows (4 chunks) swz(r) = ((r >> 1) ^ (r >> 3)) & 3, with 128-byte rows
+// (8 chunks) swz(r) = (r >> 1) & 7.  The cooperative stores write whole rows
+// and stay conflict-free.
+template <int BKB>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  constexpr int CPR = BKB / 16;
+  const int sw = (CPR == 4) ? (((r >> 1) ^ (r >> 3)) & 3) : ((r >> 1) & (CPR - 1));
+  return r * BKB + ((c ^ sw) << 4);
+}
 
 __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
   lo[0] = int((p.x << 4) & 0xF0F0F0F0u);
@@ -61,25 +65,26 @@ __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <int WAVES_M_, int WAVES_N_, int WM_, int WN_>
+template <int WAVES_M_, int WAVES_N_, int WM_, int WN_, int BK_>
 struct GemmCfg {
+  static constexpr int BK = BK_;                  // int4 elements per K tile
+  static constexpr int BKB = BK / 2;              // bytes per row per K tile
+  static constexpr int CPR = BKB / 16;            // 16-byte chunks per row
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int ROWS = BM + BN;            // A rows then B rows of a tile
-  static constexpr int CH = ROWS * 4 / THREADS;   // 16-byte chunks per thread per tile
-  static constexpr int ROWS_PER_PASS = THREADS / 4;
+  static constexpr int CH = ROWS * CPR / THREADS;  // 16-byte chunks per thread per tile
+  static constexpr int ROWS_PER_PASS = THREADS / CPR;
   static constexpr int STAGE = ROWS * BKB;
-  static_assert(ROWS * 4 % THREADS == 0, "tile rows must split evenly over threads");
+  static_assert(ROWS * CPR % THREADS == 0, "tile rows must split evenly over threads");
   static_assert(BM % ROWS_PER_PASS == 0, "a load pass must not straddle A and B");
 };
 
-// 4 waves of 64 x 128: BM = 128, BN = 256, one wave per SIMD.
-using Cfg4 = GemmCfg<2, 2, 64, 128>;
-// 8 waves of 64 x 64: BM = 128, BN = 256, two waves per SIMD.
-using Cfg8 = GemmCfg<2, 4, 64, 64>;
+// 8 waves of 64 x 64: BM = 128, BN = 256, two waves per SIMD; K tile 256.
+using Cfg8 = GemmCfg<2, 4, 64, 64, 256>;
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
@@ -88,6 +93,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     int M, int N, int K, __half* __restrict__ c, int64_t ldc, int32_t* __restrict__ acc_out,
     int64_t ld_acc, int tiles_m, int tiles_n) {
   constexpr int FM = C::FM, FN = C::FN, CH = C::CH, BM = C::BM, BN = C::BN;
+  constexpr int BKB = C::BKB, CPR = C::CPR;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][C::STAGE];
 
   // --- tile assignment: XCD-major, then grouped along M -------------------
@@ -108,10 +114,10 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   const int wn = (wave % C::WAVES_N) * C::WN;  // wave col offset inside the tile
   const int kbytes = K >> 1;
 
-  // Thread tid moves chunk (tid & 3) of tile rows tid/4 + ROWS_PER_PASS * i
-  // (A rows first, then B rows); rows past the matrix edge re-read the last
-  // row (their results are never stored).
-  const int lrow = tid >> 2, lchunk = tid & 3;
+  // Thread tid moves chunk (tid % CPR) of tile rows tid / CPR +
+  // ROWS_PER_PASS * i (A rows first, then B rows); rows past the matrix edge
+  // re-read the last row (their results are never stored).
+  const int lrow = tid / CPR, lchunk = tid % CPR;
   const uint8_t* src[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -130,18 +136,27 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
 
   const int frow = lane & 31;   // row (A) / column (B) of the fragment
   const int fhalf = lane >> 5;  // which 16-byte chunk of a 32-byte K-pair
+  // All fragment reads of a tile are issued before its MFMAs so the LDS
+  // latency overlaps the first MFMAs instead of stalling each K-pair.
+  constexpr int KP = BKB / 32;  // 64-wide K-pairs per tile
   auto compute_tile = [&](int buf) {
     const uint8_t* sa = smem[buf];
     const uint8_t* sb = smem[buf] + BM * BKB;
+    uint4 fa[KP][FM], fb[KP][FN];
 #pragma unroll
-    for (int kp = 0; kp < BKB / 32; ++kp) {  // two 64-wide K-pairs per tile
+    for (int kp = 0; kp < KP; ++kp) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[kp][i] = ld16(sa + lds_off<BKB>(wm + i * 32 + frow, 2 * kp + fhalf));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[kp][j] = ld16(sb + lds_off<BKB>(wn + j * 32 + frow, 2 * kp + fhalf));
+    }
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
       v4i alo[FM], ahi[FM], blo[FN], bhi[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        widen(ld16(sa + lds_off(wm + i * 32 + frow, 2 * kp + fhalf)), alo[i], ahi[i]);
+      for (int i = 0; i < FM; ++i) widen(fa[kp][i], alo[i], ahi[i]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        widen(ld16(sb + lds_off(wn + j * 32 + frow, 2 * kp + fhalf)), blo[j], bhi[j]);
+      for (int j = 0; j < FN; ++j) widen(fb[kp][j], blo[j], bhi[j]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -152,37 +167,38 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     }
   };
 
-  // Pipeline over the full tiles: tile kt is computed from LDS while tile
-  // kt+1 waits in registers and tile kt+2 is in flight from memory.  The
-  // loop is unrolled by two so each register set keeps a fixed role, and
-  // loads are issued every step (past the end they re-read the last full
-  // tile) so every path through the loop has the same wait counts.
+  // Pipeline over the full tiles: tile kt is computed from one LDS buffer,
+  // then tile kt+1 goes from registers into the other buffer while tiles
+  // kt+2 and kt+3 are in flight from memory.  The loop is unrolled by two
+  // so each register set keeps a fixed role, and loads are issued every step
+  // (past the end they re-read the last full tile) so every path through the
+  // loop has the same wait counts.
   uint4 r0[CH], r1[CH];
 #define QR_LOAD(r, kb0)                                          \
   _Pragma("unroll") for (int i = 0; i < CH; ++i) r[i] = ld16(src[i] + (kb0))
 #define QR_STORE(buf, r)                                                                  \
   _Pragma("unroll") for (int i = 0; i < CH; ++i) *reinterpret_cast<uint4*>(               \
-      smem[buf] + lds_off(lrow + C::ROWS_PER_PASS * i, lchunk)) = r[i]
+      smem[buf] + lds_off<BKB>(lrow + C::ROWS_PER_PASS * i, lchunk)) = r[i]
   if (kfull > 0) {
+    // Step i: compute tile i from buffer i % 2, store tile i+1 (in registers
+    // since step i-2) into the other buffer, issue the loads of tile i+3 into
+    // the registers just freed, one barrier.  sched_barrier keeps that order.
     QR_LOAD(r0, 0);
     QR_LOAD(r1, min(1, kfull - 1) * BKB);
     QR_STORE(0, r0);
+    QR_LOAD(r0, min(2, kfull - 1) * BKB);
     __syncthreads();
     int kt = 0;
-    // sched_barrier keeps the compiler from sinking the loads below the
-    // MFMAs (which would shorten the time they have to arrive)
     for (; kt + 2 <= kfull; kt += 2) {
-      QR_LOAD(r0, min(kt + 2, kfull - 1) * BKB);
-      __builtin_amdgcn_sched_barrier(0);
       compute_tile(0);  // tile kt
       __builtin_amdgcn_sched_barrier(0);
       QR_STORE(1, r1);  // tile kt+1
-      __syncthreads();
       QR_LOAD(r1, min(kt + 3, kfull - 1) * BKB);
-      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
       compute_tile(1);  // tile kt+1
       __builtin_amdgcn_sched_barrier(0);
       QR_STORE(0, r0);  // tile kt+2 (a harmless repeat past the end)
+      QR_LOAD(r0, min(kt + 4, kfull - 1) * BKB);
       __syncthreads();
     }
     if (kt < kfull) compute_tile(0);  // odd count: the last full tile is in buffer 0
@@ -254,13 +270,6 @@ int launch_w4a4_gemm(const uint8_t* a_q, int64_t lda, const __half* a_scale,
                      const uint8_t* b_q, int64_t ldb, const __half* b_scale,
                      int64_t M, int64_t N, int64_t K, __half* c, int64_t ldc,
                      int32_t* acc_out, int64_t ld_acc, hipStream_t stream) {
-  static const int variant = [] {
-    const char* e = getenv("QUAROT_GEMM_VARIANT");
-    return e ? atoi(e) : 8;
-  }();
-  if (variant == 4)
-    return launch_cfg<Cfg4>(a_q, lda, a_scale, b_q, ldb, b_scale, M, N, K, c, ldc, acc_out,
-                            ld_acc, stream);
   return launch_cfg<Cfg8>(a_q, lda, a_scale, b_q, ldb, b_scale, M, N, K, c, ldc, acc_out,
                           ld_acc, stream);
 }

@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kQuadBlock = 256;  // 64 rows per block iteration
 
-template <int D>
+template <int D, bool CLAMP>
 __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     const int64_t r = base + (threadIdx.x >> 2);
     const bool active = r < rows;
     const int64_t rr = active ? r : 0;
-    quad_row<D>(x + rr * ld_x, q_out + rr * ld_q, scale_out + rr,
+    quad_row<D, CLAMP>(x + rr * ld_x, q_out + rr * ld_q, scale_out + rr,
                 x_rot ? x_rot + rr * D : nullptr, mask, lane_q, clip_ratio, active);
   }
 }
@@ -200,12 +200,17 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
     const int64_t cap = int64_t(cus) * 8;
     if (blocks > cap) blocks = cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kQuadBlock)};
+#define QR_QUAD(DD, CL)                                                                 \
+  hipLaunchKernelGGL((had_quant_quad<DD, CL>), grid, block, 0, stream, x, rows, ld_x, signs, \
+                     clip_ratio, q_out, ld_q, scale_out, x_rot_out)
+    const bool clamp = clip_ratio != 1.0f;
     switch (d) {
-      case 32: hipLaunchKernelGGL(had_quant_quad<32>, grid, block, 0, stream, x, rows, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out); break;
-      case 64: hipLaunchKernelGGL(had_quant_quad<64>, grid, block, 0, stream, x, rows, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out); break;
-      case 128: hipLaunchKernelGGL(had_quant_quad<128>, grid, block, 0, stream, x, rows, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out); break;
-      default: hipLaunchKernelGGL(had_quant_quad<256>, grid, block, 0, stream, x, rows, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out); break;
+      case 32: if (clamp) QR_QUAD(32, true); else QR_QUAD(32, false); break;
+      case 64: if (clamp) QR_QUAD(64, true); else QR_QUAD(64, false); break;
+      case 128: if (clamp) QR_QUAD(128, true); else QR_QUAD(128, false); break;
+      default: if (clamp) QR_QUAD(256, true); else QR_QUAD(256, false); break;
     }
+#undef QR_QUAD
     return check_launch("had_quant_quad");
   }
   if (m == 1 && d == 4096) {

@@ -27,7 +27,7 @@ struct KvLaunch {
   int64_t S_cache, pos0;
 };
 
-template <int D>
+template <int D, bool CLAMP>
 __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
   constexpr int NC = D / 32;
   const KvTensorArgs t = blockIdx.y ? p.t[1] : p.t[0];
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
     }
     const __half* src = t.src + b * p.stride_b + h * p.stride_h + s * p.stride_s;
     const int64_t slot = bh * p.S_cache + p.pos0 + s;
-    quad_row<D>(src, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
+    quad_row<D, CLAMP>(src, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
                 p.clip_ratio, active);
   }
 }
@@ -87,12 +87,15 @@ int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t
   const int64_t cap = int64_t(cus > 0 ? cus : 256) * 8 / n_tensors;
   if (blocks > cap) blocks = cap;
   const dim3 grid{unsigned(blocks), unsigned(n_tensors)}, block{unsigned(kBlock)};
+#define QR_KV(DD, CL) hipLaunchKernelGGL((kv_had_quant_kernel<DD, CL>), grid, block, 0, stream, p)
+  const bool clamp = clip_ratio != 1.0f;
   switch (D) {
-    case 32: hipLaunchKernelGGL(kv_had_quant_kernel<32>, grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(kv_had_quant_kernel<64>, grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(kv_had_quant_kernel<128>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(kv_had_quant_kernel<256>, grid, block, 0, stream, p); break;
+    case 32: if (clamp) QR_KV(32, true); else QR_KV(32, false); break;
+    case 64: if (clamp) QR_KV(64, true); else QR_KV(64, false); break;
+    case 128: if (clamp) QR_KV(128, true); else QR_KV(128, false); break;
+    default: if (clamp) QR_KV(256, true); else QR_KV(256, false); break;
   }
+#undef QR_KV
   return check_launch("kv_had_quant");
 }
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ void load_sign_masks(const int8_t* sg, int q, uint32_
 
 // Process one row held by a quad.  src: fp16 row; qrow: code row (D/2
 // bytes); scale: where the fp16 scale goes; xrot: optional fp32 row.
-template <int D>
+template <int D, bool CLAMP>
 __device__ __forceinline__ void quad_row(const __half* __restrict__ src, uint8_t* __restrict__ qrow,
                                          __half* __restrict__ scale, float* __restrict__ xrot,
                                          const uint32_t (&mask)[D / 32][4], int q,
@@ -105,29 +105,36 @@ __device__ __forceinline__ void quad_row(const __half* __restrict__ src, uint8_t
                                   : D == 64 ? 8.0f
                                   : D == 128 ? 11.313708498984761f
                                              : 16.0f);
+  // the transform is unnormalised: max|x~| = max|v| / sqrt(D)
   float amax = 0.0f;
 #pragma unroll
-  for (int r = 0; r < E; ++r) {
-    v[r] *= kNorm;
-    amax = fmaxf(amax, fabsf(v[r]));
-  }
+  for (int r = 0; r < E; ++r) amax = fmaxf(amax, fabsf(v[r]));
   amax = quad_max<0>(amax);
   amax = quad_max<1>(amax);
-  const __half s16 = row_scale_fp16(amax, clip_ratio);
-  const float k = inv_scale(s16);
+  const __half s16 = row_scale_fp16(amax * kNorm, clip_ratio);
   if (!active) return;
+  const float kq = inv_scale(s16) * kNorm;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const uint32_t w = pack8(&v[8 * j], k);
-    *reinterpret_cast<uint32_t*>(qrow + 4 * (q + 4 * j)) = w;
+    float t8[8];
+    if (CLAMP) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = magic_code<true>(v[8 * j + i], kq);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = magic_code<false>(v[8 * j + i], kq);
+    }
+    *reinterpret_cast<uint32_t*>(qrow + 4 * (q + 4 * j)) = pack8_magic(t8);
   }
   if (q == 0) *scale = s16;
   if (xrot) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       float4* dst = reinterpret_cast<float4*>(xrot + 8 * (q + 4 * j));
-      dst[0] = make_float4(v[8 * j + 0], v[8 * j + 1], v[8 * j + 2], v[8 * j + 3]);
-      dst[1] = make_float4(v[8 * j + 4], v[8 * j + 5], v[8 * j + 6], v[8 * j + 7]);
+      dst[0] = make_float4(v[8 * j + 0] * kNorm, v[8 * j + 1] * kNorm, v[8 * j + 2] * kNorm,
+                           v[8 * j + 3] * kNorm);
+      dst[1] = make_float4(v[8 * j + 4] * kNorm, v[8 * j + 5] * kNorm, v[8 * j + 6] * kNorm,
+                           v[8 * j + 7] * kNorm);
     }
   }
 }
