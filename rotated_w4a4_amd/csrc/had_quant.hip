@@ -13,12 +13,15 @@
 //   * had_quant_quad<D>   d = 32..256: a quad of lanes per row (quad_rows.h).
 //   * had_quant_4096      d = 4096: a wave per row, one LDS exchange
 //                         (wave_rows.h).
+//   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
+//                         on the matrix cores, one LDS exchange (kron_rows.h).
 //   * had_quant_lds<M>    any supported d (<= 32768): one workgroup per row,
 //                         the row staged in LDS as fp32; H_m applied per
 //                         contiguous group, then radix-32 FWHT passes over
 //                         the power-of-two index.
 #include "quad_rows.h"
 #include "wave_rows.h"
+#include "kron_rows.h"
 
 namespace quarot {
 
@@ -226,6 +229,44 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
       hipLaunchKernelGGL(had_quant_4096<true>, grid, block, 0, stream, x, rows, ld_x, signs,
                          clip_ratio, q_out, ld_q, scale_out, x_rot_out);
     return check_launch("had_quant_4096");
+  }
+  if ((m == 12 || m == 28) && d == 1024 * m) {
+    static const bool kron_attr_ok = [] {
+      bool ok = true;
+      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<12, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                KronCfg<12>::LDS_BYTES) == hipSuccess;
+      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<12, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                KronCfg<12>::LDS_BYTES) == hipSuccess;
+      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<28, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                KronCfg<28>::LDS_BYTES) == hipSuccess;
+      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<28, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                KronCfg<28>::LDS_BYTES) == hipSuccess;
+      return ok;
+    }();
+    if (!kron_attr_ok) {
+      set_error("could not raise the dynamic LDS limit for d = %d", d);
+      return QUAROT_ERR_HIP;
+    }
+    const size_t lds = m == 12 ? KronCfg<12>::LDS_BYTES : KronCfg<28>::LDS_BYTES;
+    const int64_t cap = cus;  // about 210-255 VGPRs: one 512-thread block per CU
+    const int64_t blocks = rows < cap ? rows : cap;
+    const dim3 grid{unsigned(blocks)}, block{unsigned(kKronBlock)};
+    const float norm = 1.0f / sqrtf(float(d));
+    const bool clamp = clip_ratio != 1.0f;
+#define QR_KRON(MM, CL)                                                                      \
+  hipLaunchKernelGGL((had_quant_kron<MM, CL>), grid, block, lds, stream, x, rows, ld_x, signs, \
+                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm)
+    if (m == 12) {
+      if (clamp) QR_KRON(12, true); else QR_KRON(12, false);
+    } else {
+      if (clamp) QR_KRON(28, true); else QR_KRON(28, false);
+    }
+#undef QR_KRON
+    return check_launch("had_quant_kron");
   }
   const size_t lds = size_t(d + d / 32) * sizeof(float);
   // rows above 16K elements need more than the default 64 KiB of dynamic LDS

@@ -1,0 +1,278 @@
+// Rotate+quant of rows of d = 1024 * m, m = 12 or 28 (H_1024 (x) H_m):
+// one 512-thread workgroup owns one row.
+//
+// "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
+// summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
+// H_{2^n} (x) H_m with a known H_m, computable in O(d (m + n)); Stage 1b:
+// the online Hadamard before the down-projection (d = 28672 is the
+// LLaMA2-70B down-projection input, d = 12288 the Qwen3-8B one, which the
+// QuaRot paper-viz explainer builds with a Paley-12 block).
+//
+// Element e = a * m + b, a = 0..1023 (the power-of-two index), b = 0..m-1.
+//   phase 1  wave w (0..7), lane l = n + 16 g, tile t = 0..7 hold group
+//            a = 128 w + 16 t + n.  The lane loads elements b = 8 g .. 8 g + 7
+//            of its group (zero past m): the B operand of
+//            v_mfma_f32_16x16x32_f16.  H_m (rows 0-15 and, for m = 28,
+//            16-31; zero padded to 32 x 32) is the A operand, so the dense
+//            H_m factor runs on the matrix cores on the raw sign-flipped fp16
+//            input (products with +-1 are exact, sums fp32).  The output
+//            lands as b = 4 g + (0..3) and 16 + 4 g + (0..3).  Butterflies
+//            over a4-a6 (tile t) run in registers, over a0, a1, a3 (lane bits
+//            0, 1, 3) through DPP.  Valid outputs go to LDS as fp32.
+//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of four
+//            consecutive b.  The task reads the 16 values of a2, a7, a8, a9
+//            (float4 each), runs those four butterfly stages in registers,
+//            joins the workgroup maximum, quantises and writes 16-bit code
+//            units to LDS; the row's codes then leave in 16-byte stores.
+#pragma once
+
+#include "wave_rows.h"
+
+namespace quarot {
+
+constexpr int kKronBlock = 512;
+
+// H_m as bit masks over columns, rows and columns padded to 32 with zeros:
+// row r has entry -1 where bit c of neg[r] is set, +1 where only bit c of
+// nz[r] is set, 0 where neither is.
+struct HadMasks {
+  uint32_t neg[32];
+  uint32_t nz[32];
+};
+
+template <int M>
+constexpr HadMasks make_had_masks() {
+  constexpr HadFactor<M> h = make_had_factor<M>();
+  HadMasks r{};
+  for (int i = 0; i < M; ++i)
+    for (int j = 0; j < M; ++j) {
+      r.nz[i] |= 1u << j;
+      if (h.v[i][j] < 0) r.neg[i] |= 1u << j;
+    }
+  return r;
+}
+
+__constant__ HadMasks kHadMasks12 = make_had_masks<12>();
+__constant__ HadMasks kHadMasks28 = make_had_masks<28>();
+
+template <int M>
+__device__ __forceinline__ const HadMasks& kron_masks() {
+  static_assert(M == 12 || M == 28, "Paley factors of order 12 and 28");
+  if constexpr (M == 12) return kHadMasks12;
+  else return kHadMasks28;
+}
+
+// Entry c of a mask row (already shifted to the lane's first column).
+__device__ __forceinline__ _Float16 had_entry(uint32_t nz, uint32_t neg, int c) {
+  if (!((nz >> c) & 1u)) return _Float16(0.0f);
+  return ((neg >> c) & 1u) ? _Float16(-1.0f) : _Float16(1.0f);
+}
+
+template <int M>
+struct KronCfg {
+  static constexpr int D = 1024 * M;
+  static constexpr int UNITS = M / 4;       // runs of 4 consecutive b per group
+  static constexpr int TASKS = 64 * UNITS;  // phase-2 tasks per row
+  static constexpr int HALVES = (M > 16) ? 2 : 1;
+  static constexpr int LDS_BYTES = D * 4 + D / 2;  // fp32 row, then its codes
+  static_assert(M % 4 == 0 && M <= 32, "m must be a multiple of 4 up to 32");
+  static_assert(TASKS <= kKronBlock, "one phase-2 task per thread");
+};
+
+template <int M, bool CLAMP>
+__global__ __launch_bounds__(kKronBlock) void had_quant_kron(
+    const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
+    float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
+    float* __restrict__ x_rot, float norm) {
+  using C = KronCfg<M>;
+  extern __shared__ float buf[];  // the row in fp32 (phase 1 -> phase 2), then its codes
+  __shared__ float red[kKronBlock / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+
+  // valid elements of this lane's chunk of a group: b = 8 g .. 8 g + cnt - 1
+  const int cnt = min(8, max(0, M - 8 * g));
+  // A operands: H_m rows n (and 16 + n), columns 8 g + j, zero padded
+  const HadMasks& hm = kron_masks<M>();
+  const uint32_t nz_lo = hm.nz[n] >> (8 * g), neg_lo = hm.neg[n] >> (8 * g);
+  const uint32_t nz_hi = hm.nz[n + 16] >> (8 * g), neg_hi = hm.neg[n + 16] >> (8 * g);
+  half8_t h_lo, h_hi;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    h_lo[j] = had_entry(nz_lo, neg_lo, j);
+    h_hi[j] = had_entry(nz_hi, neg_hi, j);
+  }
+  // Element offsets of this lane's phase-1 chunk in group a: lo covers
+  // b = 8 g .. 8 g + 3, hi b = 8 g + 4 .. 8 g + 7.  Lanes past m read an
+  // in-row address (the group start) and discard the value, so every load
+  // is unconditional and in bounds.
+  const int off_lo = cnt > 0 ? 8 * g : 0;
+  const int off_hi = cnt > 4 ? 8 * g + 4 : 0;
+  const uint32_t keep_lo = cnt > 0 ? 0xFFFFFFFFu : 0u;
+  const uint32_t keep_hi = cnt > 4 ? 0xFFFFFFFFu : 0u;
+  // sign masks of this lane's phase-1 elements (the same for every row)
+  uint4 mask[8];
+  if (signs) {
+    uint32_t w[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int a = 128 * wave + 16 * t + n;
+      __builtin_memcpy(&w[t][0], signs + a * M + off_lo, 4);
+      __builtin_memcpy(&w[t][1], signs + a * M + off_hi, 4);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mask[t] = sign_masks8(w[t][0] & keep_lo, w[t][1] & keep_hi);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mask[t] = make_uint4(0, 0, 0, 0);
+  }
+  const float s_q1 = (lane & 1) ? -1.0f : 1.0f;
+  const float s_q2 = (lane & 2) ? -1.0f : 1.0f;
+  const float s_r8 = (lane & 8) ? -1.0f : 1.0f;
+
+  // phase-2 task of this thread
+  const bool task_on = tid < C::TASKS;
+  const int combo = tid & 63, unit = tid >> 6;
+  const int abase = (combo & 1) | ((combo & 2)) | ((combo >> 2) & 1) << 3 | ((combo >> 3) & 7) << 4;
+
+  // loads of one row's phase-1 chunks
+  auto load_row = [&](int64_t row, uint4 (&raw)[8]) {
+    const __half* src = x + row * ld_x;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int a = 128 * wave + 16 * t + n;
+      const uint2 lo = *reinterpret_cast<const uint2*>(src + a * M + off_lo);
+      const uint2 hi = *reinterpret_cast<const uint2*>(src + a * M + off_hi);
+      raw[t] = make_uint4(lo.x & keep_lo, lo.y & keep_lo, hi.x & keep_hi, hi.y & keep_hi);
+    }
+  };
+
+  int64_t row = blockIdx.x;
+  uint4 raw[8];
+  if (row < rows) load_row(row, raw);
+  for (; row < rows; row += gridDim.x) {
+    float v[64];
+    // ---- phase 1: H_m on the matrix cores --------------------------------
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint4 r = raw[t];
+      r.x ^= mask[t].x;
+      r.y ^= mask[t].y;
+      r.z ^= mask[t].z;
+      r.w ^= mask[t].w;
+      const half8_t bop = __builtin_bit_cast(half8_t, r);
+      const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
+      float4_t d1 = zero;
+      if (C::HALVES == 2) d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bop, zero, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[8 * t + q] = d0[q];
+        v[8 * t + 4 + q] = d1[q];
+      }
+    }
+    // prefetch the next row
+    const int64_t nrow = row + gridDim.x;
+    if (nrow < rows) load_row(nrow, raw);
+    // a4-a6: register bits 3-5
+#pragma unroll
+    for (int h = 8; h < 64; h <<= 1)
+#pragma unroll
+      for (int r = 0; r < 64; ++r)
+        if ((r & h) == 0) {
+          const float a = v[r], b = v[r + h];
+          v[r] = a + b;
+          v[r + h] = a - b;
+        }
+    // a0, a1, a3: lane bits 0, 1, 3 through DPP
+#pragma unroll
+    for (int r = 0; r < 64; ++r)
+      if (C::HALVES == 2 || (r & 4) == 0) v[r] = dpp_butterfly<kDppQuadX1>(v[r], s_q1);
+#pragma unroll
+    for (int r = 0; r < 64; ++r)
+      if (C::HALVES == 2 || (r & 4) == 0) v[r] = dpp_butterfly<kDppQuadX2>(v[r], s_q2);
+#pragma unroll
+    for (int r = 0; r < 64; ++r)
+      if (C::HALVES == 2 || (r & 4) == 0) v[r] = dpp_butterfly<kDppRowRor8>(v[r], s_r8);
+    // valid outputs to LDS: b = 16 h + 4 g + (0..3)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int a = 128 * wave + 16 * t + n;
+#pragma unroll
+      for (int h = 0; h < C::HALVES; ++h) {
+        const int b0 = 16 * h + 4 * g;
+        if (b0 < M)
+          *reinterpret_cast<float4*>(buf + a * M + b0) =
+              make_float4(v[8 * t + 4 * h], v[8 * t + 4 * h + 1], v[8 * t + 4 * h + 2],
+                          v[8 * t + 4 * h + 3]);
+      }
+    }
+    __syncthreads();
+    // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
+    float amax = 0.0f;
+    if (task_on) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int a = abase | ((q & 1) << 2) | ((q >> 1) << 7);
+        const float4 f = *reinterpret_cast<const float4*>(buf + a * M + 4 * unit);
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+#pragma unroll
+      for (int h = 4; h < 64; h <<= 1)
+#pragma unroll
+        for (int r = 0; r < 64; ++r)
+          if ((r & h) == 0) {
+            const float a = v[r], b = v[r + h];
+            v[r] = a + b;
+            v[r + h] = a - b;
+          }
+#pragma unroll
+      for (int r = 0; r < 64; ++r) amax = fmaxf(amax, fabsf(v[r]));
+    }
+    amax = wave_max_dpp(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();  // phase-2 reads of buf are done; red is complete
+    amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kKronBlock / 64; ++w) amax = fmaxf(amax, red[w]);
+    const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
+    const float kq = inv_scale(s16) * norm;
+    uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
+    if (task_on) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int a = abase | ((q & 1) << 2) | ((q >> 1) << 7);
+        const float t0 = magic_code<CLAMP>(v[4 * q], kq), t1 = magic_code<CLAMP>(v[4 * q + 1], kq);
+        const float t2 = magic_code<CLAMP>(v[4 * q + 2], kq), t3 = magic_code<CLAMP>(v[4 * q + 3], kq);
+        const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t2),
+                                                  __builtin_bit_cast(uint32_t, t0), 0x0c0c0400u);
+        const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t3),
+                                                  __builtin_bit_cast(uint32_t, t1), 0x0c0c0400u);
+        codes[(a * M + 4 * unit) >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
+        if (x_rot) {
+          float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + a * M + 4 * unit);
+          *dst = make_float4(v[4 * q] * norm, v[4 * q + 1] * norm, v[4 * q + 2] * norm,
+                             v[4 * q + 3] * norm);
+        }
+      }
+    }
+    __syncthreads();
+    // the row's codes: D / 2 bytes, 16-byte stores.  The codes have their
+    // own LDS area, so the next row's phase 1 may start while they leave.
+    uint8_t* qrow = q_out + row * ld_q;
+    constexpr int kChunks = C::D / 32, kIter = (kChunks + kKronBlock - 1) / kKronBlock;
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int c = tid + kKronBlock * i;
+      if (i + 1 < kIter || c < kChunks)
+        *reinterpret_cast<uint4*>(qrow + 16 * c) = reinterpret_cast<const uint4*>(codes)[c];
+    }
+    if (tid == 0) scale_out[row] = s16;
+  }
+}
+
+}  // namespace quarot

@@ -321,3 +321,31 @@ def test_had_quant_no_signs_single_row_and_determinism():
         ref = oracle.had_quant(x16, np.ones(d, np.int8), m)
         check_scales(s1, ref["scales"])
         check_codes(oracle.unpack_int4(q1), ref["codes"], frac=1e-2)
+
+
+@pytest.mark.parametrize("m", [12, 28])
+@pytest.mark.parametrize("clip", [1.0, 0.9])
+def test_had_quant_kron_rows_strided_grid_stride(m, clip):
+    # d = 1024 m takes the Kronecker kernel; 300 rows exceed one block per
+    # compute unit, so blocks walk several rows and prefetch the next one
+    rng = np.random.default_rng(100 + m)
+    d = 1024 * m
+    rows, ld = 300, 1024 * m + 96
+    buf = rng.standard_normal((rows, ld)).astype(np.float32)
+    buf[:, rng.integers(0, d, 3)] *= 60.0
+    buf = buf.astype(np.float16)
+    buf[5] = 0
+    signs = (1 - 2 * rng.integers(0, 2, d)).astype(np.int8)
+    say(f"had_quant kron d={d} rows={rows} ld={ld} clip={clip}")
+    xt = dev(buf)[:, :d]
+    qbuf = torch.full((rows, d // 2 + 48), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float16, device="cuda")
+    xr = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    qr.had_quant(xt, dev(signs), m, clip, q_out=qbuf[:, : d // 2], scale_out=s, x_rot_out=xr)
+    ref = oracle.had_quant(buf[:, :d], signs, m, clip)
+    qh = host(qbuf)
+    assert np.all(qh[:, d // 2:] == 0x5A)
+    check_rot(host(xr), ref["x_rot"])
+    check_scales(host(s), ref["scales"])
+    check_codes(oracle.unpack_int4(qh[:, : d // 2]), ref["codes"])
+    assert np.all(qh[5, : d // 2] == 0)
