@@ -42,6 +42,9 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 CACHE_DEFEAT_BYTES = 1 << 30
 SPIN_CYCLES = 200_000_000  # ~0.1 s of GPU spin before event-timed launches
+CSRC = os.path.join(ROOT, "rotated_w4a4_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COPY_BYTES = 256 << 20
 
 
 def log(msg: str) -> None:
@@ -57,6 +60,11 @@ def parse_args():
     p.add_argument("--kv", action="store_true", help="benchmark the K/V cache write instead")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for 1 GiB)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run a plain 256 MiB device copy (HBM counter calibration)")
+    p.add_argument("--traffic-from", nargs="+", metavar="CSV",
+                   help="write the HBM traffic summary from rocprofv3 --pmc CSVs: CAL_FETCH "
+                        "CAL_WRITE, then WORKLOAD FETCH WRITE triples")
     return p.parse_args()
 
 
@@ -70,6 +78,49 @@ def blas_threads() -> int:
     except Exception:
         pass
     return os.cpu_count() or 1
+
+
+def time_kernel(torch, stream, launch, count: int) -> float:
+    """Average duration (ms) of `count` back-to-back launches on `stream`."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(SPIN_CYCLES)
+    e0.record(stream)
+    for i in range(count):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / count
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources and the public header."""
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(os.listdir(CSRC))
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "quarot.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernels changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(workload, {}).get(kernel)
+    if not k:
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
 
 
 def cpu_baseline_act(cfg, inp) -> dict:
@@ -126,16 +177,10 @@ def bench_act(args, torch, qr) -> dict:
         })
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         s = sets[i % nsets]
-        if ev is not None:
-            ev[0].record(stream)
         qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         qr.w4a4_gemm(s["qx"], s["sx"], s["qw"], s["sw"], d, out=s["y"], stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -148,16 +193,20 @@ def bench_act(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # (2) per-kernel durations from HIP events on the launch stream.  A spin
-    # kernel keeps the GPU busy while the host enqueues every step, so the
-    # events see back-to-back GPU work and no host launch latency.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda._sleep(SPIN_CYCLES)
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    rq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # (2) per-kernel durations from HIP events on the launch stream: K
+    # back-to-back launches of one kernel (cycling over the buffer sets)
+    # between two events, behind a spin kernel so the host has queued them
+    # all before the first starts.
+    def launch_rq(i):
+        s = sets[i % nsets]
+        qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
+
+    def launch_gemm(i):
+        s = sets[i % nsets]
+        qr.w4a4_gemm(s["qx"], s["sx"], s["qw"], s["sw"], d, out=s["y"], stream=stream)
+
+    rq_ms = time_kernel(torch, stream, launch_rq, args.steps)
+    gemm_ms = time_kernel(torch, stream, launch_gemm, args.steps)
     rq_bytes = 2 * T * d + T * d // 2 + 2 * T
     gemm_ops = 2.0 * T * N * d
     rq_gbs = rq_bytes / (rq_ms * 1e-3) / 1e9
@@ -192,7 +241,7 @@ def bench_act(args, torch, qr) -> dict:
             "peak": INT8_PEAK_TOPS,
             "unit": "TFLOP/s",
             "frac": round(tops / INT8_PEAK_TOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, "w4a4_gemm"),
             "note": "integer ops (TOPS) against the dense INT8 MFMA peak; 2*M*N*K per launch",
         },
         "roofline_rotate_quant": {
@@ -202,7 +251,7 @@ def bench_act(args, torch, qr) -> dict:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, "had_quant"),
             "algorithmic_bytes": rq_bytes,
         },
     }
@@ -245,14 +294,7 @@ def bench_kv(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda._sleep(SPIN_CYCLES)
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        step(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms = time_kernel(torch, stream, step, args.steps)
     nbytes = per_set
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"kv {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
@@ -266,12 +308,80 @@ def bench_kv(args, torch, qr) -> dict:
                                f"H_{D} with random signs", "buffer_sets": nsets},
         "roofline": {"kernel": "kv_had_quant", "bound": "hbm", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": nbytes},
+                     "traffic": measured_traffic(cfg.name, "kv_had_quant"),
+                     "algorithmic_bytes": nbytes},
     }
+
+
+def calibrate_copy(torch) -> dict:
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": 5}
+
+
+def counter_means(path: str, counter: str) -> dict:
+    """Median of one counter per kernel name in a rocprofv3 counter CSV (the
+    median drops the one-off launches, e.g. the weight preparation)."""
+    import csv
+
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.median(v)) for k, v in acc.items()}
+
+
+KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant": "kv_had_quant"}
+
+
+def summarize_counters(args) -> dict:
+    """Build the HBM traffic summary from rocprofv3 --pmc runs.
+
+    --traffic-from CAL_FETCH CAL_WRITE then, per workload, NAME FETCH WRITE
+    (CSV paths).  FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by
+    the ratio of known bytes to what the same counter reads for the plain
+    copy kernel of the calibration run."""
+    cal_f = counter_means(args.traffic_from[0], "FETCH_SIZE")
+    cal_w = counter_means(args.traffic_from[1], "WRITE_SIZE")
+    copy_f = max(v for k, v in cal_f.items() if "copy" in k.lower())
+    copy_w = max(v for k, v in cal_w.items() if "copy" in k.lower())
+    kf = COPY_BYTES / (copy_f * 1024.0)
+    kw = COPY_BYTES / (copy_w * 1024.0)
+    out = {"source_sha256": source_digest(),
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
+                                "fetch_scale": kf, "write_scale": kw},
+           "kernels": {}}
+    rest = args.traffic_from[2:]
+    for i in range(0, len(rest), 3):
+        name, fpath, wpath = rest[i:i + 3]
+        f = counter_means(fpath, "FETCH_SIZE")
+        w = counter_means(wpath, "WRITE_SIZE")
+        ent = {}
+        for kname, fv in f.items():
+            key = next((v for k, v in KERNEL_KEYS.items() if k in kname and
+                        not (k == "had_quant" and "kv_had_quant" in kname)), None)
+            if key is None or kname not in w:
+                continue
+            ent[key] = {"kernel": kname.split("(")[0], "fetch_kib": fv, "write_kib": w[kname],
+                        "fetch_bytes": fv * 1024.0 * kf, "write_bytes": w[kname] * 1024.0 * kw}
+        out["kernels"][name] = ent
+    return out
 
 
 def main() -> int:
     args = parse_args()
+    if args.traffic_from:
+        t = summarize_counters(args)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path has no cross-GPU exchange; see the sharding notes)", file=sys.stderr)
@@ -285,7 +395,10 @@ def main() -> int:
 
     qr.lib()
     torch.cuda.set_device(0)
-    out = bench_kv(args, torch, qr) if args.kv else bench_act(args, torch, qr)
+    if args.calibrate_copy:
+        out = calibrate_copy(torch)
+    else:
+        out = bench_kv(args, torch, qr) if args.kv else bench_act(args, torch, qr)
     print(json.dumps(out), flush=True)
     return 0
 
