@@ -36,16 +36,24 @@ __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     float* __restrict__ x_rot) {
   constexpr int NC = D / 32;
   const int lane_q = threadIdx.x & 3;
-  uint32_t mask[NC][4];
+  uint4 mask[NC];
   load_sign_masks<NC>(signs, lane_q, mask);
   const int64_t rows_per_block = kQuadBlock / 4;
-  for (int64_t base = int64_t(blockIdx.x) * rows_per_block; base < rows;
-       base += int64_t(gridDim.x) * rows_per_block) {
-    const int64_t r = base + (threadIdx.x >> 2);
+  const int64_t step = int64_t(gridDim.x) * rows_per_block;
+  int64_t r = int64_t(blockIdx.x) * rows_per_block + (threadIdx.x >> 2);
+  // one row ahead: the next row's loads are in flight while this one computes
+  uint4 raw[NC];
+  quad_load<D>(x + (r < rows ? r : 0) * ld_x, lane_q, raw);
+  for (int64_t base = int64_t(blockIdx.x) * rows_per_block; base < rows; base += step, r += step) {
     const bool active = r < rows;
     const int64_t rr = active ? r : 0;
-    quad_row<D, CLAMP>(x + rr * ld_x, q_out + rr * ld_q, scale_out + rr,
-                x_rot ? x_rot + rr * D : nullptr, mask, lane_q, clip_ratio, active);
+    uint4 cur[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) cur[j] = raw[j];
+    const int64_t nr = r + step;
+    quad_load<D>(x + (nr < rows ? nr : 0) * ld_x, lane_q, raw);
+    quad_row<D, CLAMP>(cur, q_out + rr * ld_q, scale_out + rr, x_rot ? x_rot + rr * D : nullptr,
+                       mask, lane_q, clip_ratio, active);
   }
 }
 

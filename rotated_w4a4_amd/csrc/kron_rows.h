@@ -68,6 +68,44 @@ __device__ __forceinline__ _Float16 had_entry(uint32_t nz, uint32_t neg, int c) 
   return ((neg >> c) & 1u) ? _Float16(-1.0f) : _Float16(1.0f);
 }
 
+// LDS row of group a: a2 is flipped when a4 is set.  Phase 1 writes 16
+// consecutive groups per LDS cycle, phase 2 reads groups that differ in a0,
+// a1, a3, a4; with rows of m floats (m / 4 odd) both hit 16 distinct float4
+// bank slots.
+__device__ __forceinline__ int kron_row(int a) { return a ^ (((a >> 4) & 1) << 2); }
+
+// One butterfly stage over lane bit 0, 1 or 3 (STAGE 0, 1, 2) on the phase-1
+// registers, as v + partner * c in a single v_fmac_f32 with DPP (c = +1 on the
+// low lane, -1 on the high lane, so a high lane ends with b - a).  HALVES == 1
+// skips the registers of the unused upper MFMA half.
+//
+// DPP reads need two wait states after a VALU write of their source.  Stage 0
+// reads registers written by compiler-scheduled code, so each of its blocks
+// opens with s_nop 1; stages 1 and 2 read only what the previous stage's asm
+// blocks wrote, at least 28 instructions earlier.  The last block of stage 2
+// closes with s_nop 1 for whatever follows.
+template <int STAGE, int HALVES>
+__device__ __forceinline__ void dpp_fmac_stage(float (&v)[64], float c) {
+#define QR_FMAC_DPP(LEAD, CTRL, TRAIL)                                                       \
+  asm volatile(LEAD                                                                          \
+               "v_fmac_f32_dpp %0, %0, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %1, %1, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %2, %2, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %3, %3, %4 " CTRL " row_mask:0xf bank_mask:0xf" TRAIL      \
+               : "+v"(v[r]), "+v"(v[r + 1]), "+v"(v[r + 2]), "+v"(v[r + 3])              \
+               : "v"(c))
+  constexpr int kLast = HALVES == 1 ? 56 : 60;
+#pragma unroll
+  for (int r = 0; r < 64; r += 4) {
+    if (HALVES == 1 && (r & 4)) continue;
+    if (STAGE == 0) QR_FMAC_DPP("s_nop 1\n", "quad_perm:[1,0,3,2]", "");
+    else if (STAGE == 1) QR_FMAC_DPP("", "quad_perm:[2,3,0,1]", "");
+    else if (r != kLast) QR_FMAC_DPP("", "row_ror:8", "");
+    else QR_FMAC_DPP("", "row_ror:8", "\ns_nop 1");
+  }
+#undef QR_FMAC_DPP
+}
+
 template <int M>
 struct KronCfg {
   static constexpr int D = 1024 * M;
@@ -85,7 +123,8 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
     float* __restrict__ x_rot, float norm) {
   using C = KronCfg<M>;
-  extern __shared__ float buf[];  // the row in fp32 (phase 1 -> phase 2), then its codes
+  extern __shared__ float4 kron_lds[];  // the row in fp32 (phase 1 -> phase 2), then its codes
+  float* buf = reinterpret_cast<float*>(kron_lds);
   __shared__ float red[kKronBlock / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -134,7 +173,9 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
   // phase-2 task of this thread
   const bool task_on = tid < C::TASKS;
   const int combo = tid & 63, unit = tid >> 6;
-  const int abase = (combo & 1) | ((combo & 2)) | ((combo >> 2) & 1) << 3 | ((combo >> 3) & 7) << 4;
+  const int abase = (combo & 3) + (((combo >> 2) & 1) << 3) + (((combo >> 3) & 7) << 4);
+  // sign left on this task's values by the phase-1 DPP stages
+  const float sigma = (__builtin_popcount(combo & 7) & 1) ? -1.0f : 1.0f;
 
   // loads of one row's phase-1 chunks
   auto load_row = [&](int64_t row, uint4 (&raw)[8]) {
@@ -186,19 +227,15 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
           v[r + h] = a - b;
         }
     // a0, a1, a3: lane bits 0, 1, 3 through DPP
-#pragma unroll
-    for (int r = 0; r < 64; ++r)
-      if (C::HALVES == 2 || (r & 4) == 0) v[r] = dpp_butterfly<kDppQuadX1>(v[r], s_q1);
-#pragma unroll
-    for (int r = 0; r < 64; ++r)
-      if (C::HALVES == 2 || (r & 4) == 0) v[r] = dpp_butterfly<kDppQuadX2>(v[r], s_q2);
-#pragma unroll
-    for (int r = 0; r < 64; ++r)
-      if (C::HALVES == 2 || (r & 4) == 0) v[r] = dpp_butterfly<kDppRowRor8>(v[r], s_r8);
-    // valid outputs to LDS: b = 16 h + 4 g + (0..3)
+    // (one v_fmac_f32_dpp each: a high lane keeps b - a, so after the three
+    // stages lane values carry the sign (-1)^(a0 + a1 + a3), undone in phase 2)
+    dpp_fmac_stage<0, C::HALVES>(v, s_q1);
+    dpp_fmac_stage<1, C::HALVES>(v, s_q2);
+    dpp_fmac_stage<2, C::HALVES>(v, s_r8);
+    // valid outputs to LDS: b = 16 h + 4 g + (0..3), group a at row kron_row(a)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int a = 128 * wave + 16 * t + n;
+      const int a = kron_row(128 * wave + 16 * t + n);
 #pragma unroll
       for (int h = 0; h < C::HALVES; ++h) {
         const int b0 = 16 * h + 4 * g;
@@ -214,7 +251,7 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     if (task_on) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int a = abase | ((q & 1) << 2) | ((q >> 1) << 7);
+        const int a = kron_row(abase + ((q & 1) << 2) + ((q >> 1) << 7));
         const float4 f = *reinterpret_cast<const float4*>(buf + a * M + 4 * unit);
         v[4 * q] = f.x;
         v[4 * q + 1] = f.y;
@@ -240,12 +277,13 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
 #pragma unroll
     for (int w = 1; w < kKronBlock / 64; ++w) amax = fmaxf(amax, red[w]);
     const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
-    const float kq = inv_scale(s16) * norm;
+    const float kq = inv_scale(s16) * norm * sigma;
+    const float xnorm = norm * sigma;
     uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
     if (task_on) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int a = abase | ((q & 1) << 2) | ((q >> 1) << 7);
+        const int a = abase + ((q & 1) << 2) + ((q >> 1) << 7);
         const float t0 = magic_code<CLAMP>(v[4 * q], kq), t1 = magic_code<CLAMP>(v[4 * q + 1], kq);
         const float t2 = magic_code<CLAMP>(v[4 * q + 2], kq), t3 = magic_code<CLAMP>(v[4 * q + 3], kq);
         const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t2),
@@ -255,8 +293,8 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
         codes[(a * M + 4 * unit) >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
         if (x_rot) {
           float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + a * M + 4 * unit);
-          *dst = make_float4(v[4 * q] * norm, v[4 * q + 1] * norm, v[4 * q + 2] * norm,
-                             v[4 * q + 3] * norm);
+          *dst = make_float4(v[4 * q] * xnorm, v[4 * q + 1] * xnorm, v[4 * q + 2] * xnorm,
+                             v[4 * q + 3] * xnorm);
         }
       }
     }

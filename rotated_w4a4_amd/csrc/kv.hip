@@ -17,9 +17,29 @@ namespace {
 
 constexpr int kBlock = 256;  // 64 groups per block iteration
 
+// n / d for 0 <= n < 2^31 by a multiply-high and a shift (round-up method
+// of Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994): with l = ceil(log2 d) and
+// mul = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, mul) + n) >> l.
+struct FastDiv {
+  uint32_t d, mul, shift;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t mul = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  return FastDiv{d, uint32_t(mul), l};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  return uint32_t((uint64_t(__umulhi(n, f.mul)) + n) >> f.shift);
+}
+
 struct KvLaunch {
   KvTensorArgs t[2];
-  int64_t B, H, S;
+  uint32_t groups;
+  FastDiv S, H;
   int64_t stride_b, stride_h, stride_s;
   const int8_t* signs;
   int64_t signs_stride_h;
@@ -27,34 +47,51 @@ struct KvLaunch {
   int64_t S_cache, pos0;
 };
 
+// Group g = (b H + h) S + s: its fp16 source and its cache slot.
+__device__ __forceinline__ void kv_group(const KvLaunch& p, uint32_t g, uint32_t& h,
+                                         int64_t& src_off, int64_t& slot) {
+  const uint32_t bh = fast_div(g, p.S);
+  const uint32_t s = g - bh * p.S.d;
+  const uint32_t b = fast_div(bh, p.H);
+  h = bh - b * p.H.d;
+  src_off = int64_t(b) * p.stride_b + int64_t(h) * p.stride_h + int64_t(s) * p.stride_s;
+  slot = int64_t(bh) * p.S_cache + p.pos0 + s;
+}
+
 template <int D, bool CLAMP>
 __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
   constexpr int NC = D / 32;
   const KvTensorArgs t = blockIdx.y ? p.t[1] : p.t[0];
   const int lane_q = threadIdx.x & 3;
-  const int64_t groups = p.B * p.H * p.S;
-  const int64_t per_block = kBlock / 4;
-  uint32_t mask[NC][4];
+  const uint32_t per_block = kBlock / 4;
+  const uint32_t step = gridDim.x * per_block;
+  uint4 mask[NC];
   int64_t mask_head = -1;
-  for (int64_t base = int64_t(blockIdx.x) * per_block; base < groups;
-       base += int64_t(gridDim.x) * per_block) {
-    const int64_t g = base + (threadIdx.x >> 2);
-    const bool active = g < groups;
-    const int64_t gg = active ? g : 0;
-    const int64_t s = gg % p.S;
-    const int64_t bh = gg / p.S;
-    const int64_t h = bh % p.H;
-    const int64_t b = bh / p.H;
+  uint32_t g = blockIdx.x * per_block + (threadIdx.x >> 2);
+  // one group ahead: the next group's loads are in flight while this one computes
+  uint32_t h;
+  int64_t src_off, slot;
+  kv_group(p, g < p.groups ? g : 0, h, src_off, slot);
+  uint4 raw[NC];
+  quad_load<D>(t.src + src_off, lane_q, raw);
+  for (uint32_t base = blockIdx.x * per_block; base < p.groups; base += step, g += step) {
+    const bool active = g < p.groups;
+    const uint32_t hc = h;
+    const int64_t slot_c = slot;
+    uint4 cur[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) cur[j] = raw[j];
+    const uint32_t ng = g + step;
+    kv_group(p, ng < p.groups ? ng : 0, h, src_off, slot);
+    quad_load<D>(t.src + src_off, lane_q, raw);
     // signs: one vector per head (stride 0: shared by all heads)
-    const int64_t head_key = p.signs_stride_h ? h : 0;
+    const int64_t head_key = p.signs_stride_h ? int64_t(hc) : 0;
     if (head_key != mask_head) {
       load_sign_masks<NC>(p.signs ? p.signs + head_key * p.signs_stride_h : nullptr, lane_q, mask);
       mask_head = head_key;
     }
-    const __half* src = t.src + b * p.stride_b + h * p.stride_h + s * p.stride_s;
-    const int64_t slot = bh * p.S_cache + p.pos0 + s;
-    quad_row<D, CLAMP>(src, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
-                p.clip_ratio, active);
+    quad_row<D, CLAMP>(cur, t.q + slot_c * (D / 2), t.scale + slot_c, nullptr, mask, lane_q,
+                       p.clip_ratio, active);
   }
 }
 
@@ -67,9 +104,9 @@ int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t
                         hipStream_t stream) {
   KvLaunch p{};
   for (int i = 0; i < n_tensors; ++i) p.t[i] = t[i];
-  p.B = B;
-  p.H = H;
-  p.S = S;
+  p.groups = uint32_t(B * H * S);  // < 2^31, checked by the caller
+  p.S = make_fastdiv(uint32_t(S));
+  p.H = make_fastdiv(uint32_t(H));
   p.stride_b = stride_b;
   p.stride_h = stride_h;
   p.stride_s = stride_s;

@@ -39,46 +39,54 @@ __device__ __forceinline__ float quad_max(float v) {
   return fmaxf(v, p);
 }
 
-// Build the XOR masks that flip fp16 sign bits for this lane's elements.
+// XOR masks that flip the fp16 sign bits of this lane's elements (chunk
+// c = q + 4j holds elements 8c .. 8c + 7); all loads issue before any use.
 template <int NC>
-__device__ __forceinline__ void load_sign_masks(const int8_t* sg, int q, uint32_t (&mask)[NC][4]) {
+__device__ __forceinline__ void load_sign_masks(const int8_t* sg, int q, uint4 (&mask)[NC]) {
+  if (!sg) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) mask[j] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  uint32_t w[NC][2];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t mk = 0;
-      if (sg) {
-        const int e = 8 * (q + 4 * j) + 2 * p;
-        mk = (sg[e] < 0 ? 0x8000u : 0u) | (sg[e + 1] < 0 ? 0x80000000u : 0u);
-      }
-      mask[j][p] = mk;
-    }
+    __builtin_memcpy(&w[j][0], sg + 8 * (q + 4 * j), 4);
+    __builtin_memcpy(&w[j][1], sg + 8 * (q + 4 * j) + 4, 4);
   }
+#pragma unroll
+  for (int j = 0; j < NC; ++j) mask[j] = sign_masks8(w[j][0], w[j][1]);
 }
 
-// Process one row held by a quad.  src: fp16 row; qrow: code row (D/2
-// bytes); scale: where the fp16 scale goes; xrot: optional fp32 row.
+// The raw fp16 chunks of one row held by a quad.  The caller passes a valid
+// row address even for an inactive quad (whose values are then unused), so
+// the loads carry no condition.
+template <int D>
+__device__ __forceinline__ void quad_load(const __half* __restrict__ src, int q,
+                                          uint4 (&raw)[D / 32]) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) raw[j] = *reinterpret_cast<const uint4*>(src + 8 * (q + 4 * j));
+}
+
+// Process one row held by a quad, its raw chunks already loaded.  qrow: code
+// row (D/2 bytes); scale: where the fp16 scale goes; xrot: optional fp32 row.
 template <int D, bool CLAMP>
-__device__ __forceinline__ void quad_row(const __half* __restrict__ src, uint8_t* __restrict__ qrow,
+__device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __restrict__ qrow,
                                          __half* __restrict__ scale, float* __restrict__ xrot,
-                                         const uint32_t (&mask)[D / 32][4], int q,
-                                         float clip_ratio, bool active) {
+                                         const uint4 (&mask)[D / 32], int q, float clip_ratio,
+                                         bool active) {
   constexpr int NC = D / 32;  // chunks per lane
   constexpr int E = 8 * NC;   // elements per lane
   float v[E];
-  if (active) {
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * (q + 4 * j));
-      raw.x ^= mask[j][0];
-      raw.y ^= mask[j][1];
-      raw.z ^= mask[j][2];
-      raw.w ^= mask[j][3];
-      unpack_half8(raw, &v[8 * j]);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = 0.0f;
+  for (int j = 0; j < NC; ++j) {
+    uint4 r = raw[j];
+    if (!active) r = make_uint4(0, 0, 0, 0);
+    r.x ^= mask[j].x;
+    r.y ^= mask[j].y;
+    r.z ^= mask[j].z;
+    r.w ^= mask[j].w;
+    unpack_half8(r, &v[8 * j]);
   }
   // register-bit butterflies
 #pragma unroll

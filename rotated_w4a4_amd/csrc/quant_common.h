@@ -90,4 +90,16 @@ __device__ __forceinline__ uint32_t pack8_magic(const float* t) {
   return ((od << 4) | ev) ^ 0x88888888u;
 }
 
+// XOR masks flipping the fp16 sign bits of 8 consecutive elements whose
+// int8 signs (+1 / -1, sign bit = bit 7) are the bytes of w0 (elements 0-3)
+// and w1 (elements 4-7).
+__device__ __forceinline__ uint4 sign_masks8(uint32_t w0, uint32_t w1) {
+  uint4 m;
+  m.x = ((w0 << 8) & 0x8000u) | ((w0 << 16) & 0x80000000u);
+  m.y = ((w0 >> 8) & 0x8000u) | (w0 & 0x80000000u);
+  m.z = ((w1 << 8) & 0x8000u) | ((w1 << 16) & 0x80000000u);
+  m.w = ((w1 >> 8) & 0x8000u) | (w1 & 0x80000000u);
+  return m;
+}
+
 }  // namespace quarot

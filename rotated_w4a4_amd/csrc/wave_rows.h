@@ -55,18 +55,6 @@ __device__ __forceinline__ int x4096_slot(int c) {
               (((c >> 7) & 1) << 3));
 }
 
-// XOR masks flipping the fp16 sign bits of 8 consecutive elements whose
-// int8 signs (+1 / -1, sign bit = bit 7) are the bytes of w0 (elements 0-3)
-// and w1 (elements 4-7).
-__device__ __forceinline__ uint4 sign_masks8(uint32_t w0, uint32_t w1) {
-  uint4 m;
-  m.x = ((w0 << 8) & 0x8000u) | ((w0 << 16) & 0x80000000u);
-  m.y = ((w0 >> 8) & 0x8000u) | (w0 & 0x80000000u);
-  m.z = ((w1 << 8) & 0x8000u) | ((w1 << 16) & 0x80000000u);
-  m.w = ((w1 >> 8) & 0x8000u) | (w1 & 0x80000000u);
-  return m;
-}
-
 constexpr int kWaveRowsBlock = 256;  // 4 waves, one row each per iteration
 
 // d = 4096, one wave per row.
@@ -104,18 +92,18 @@ __global__ __launch_bounds__(kWaveRowsBlock, 2) void had_quant_4096(
       raw[t] = *reinterpret_cast<const uint4*>(x + row * ld_x + 512 * t + 32 * n + 8 * g);
   }
   // sign masks of this lane's phase-1 elements (the same for every row)
+  // (all eight loads are issued before the first use)
   uint4 mask[8];
+  if (signs) {
+    uint2 w[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    if (signs) {
-      const int8_t* sp = signs + 512 * t + 32 * n + 8 * g;
-      uint32_t w0, w1;
-      __builtin_memcpy(&w0, sp, 4);
-      __builtin_memcpy(&w1, sp + 4, 4);
-      mask[t] = sign_masks8(w0, w1);
-    } else {
-      mask[t] = make_uint4(0, 0, 0, 0);
-    }
+    for (int t = 0; t < 8; ++t)
+      w[t] = *reinterpret_cast<const uint2*>(signs + 512 * t + 32 * n + 8 * g);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mask[t] = sign_masks8(w[t].x, w[t].y);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mask[t] = make_uint4(0, 0, 0, 0);
   }
   // A operands: rows n and n + 16 of H_32, columns 8 g + j
   half8_t h_lo, h_hi;
