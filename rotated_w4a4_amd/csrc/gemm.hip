@@ -17,11 +17,12 @@
 // accumulator holds 256 * acc exactly (256 * 64 * K <= 2^30 for K <= 65536)
 // and the epilogue shifts it right by 8.
 //
-// Tiling.  Workgroup tile BM x BN x 128 (K), waves of WM x WN, each wave
-// (WM/32) x (WN/32) blocks of v_mfma_i32_32x32x32_i8.  Packed tiles are
-// staged in LDS (two buffers, 16-byte chunks XOR-swizzled per row); two more
-// tiles are in flight into registers, so global loads are issued two tiles
-// ahead of use and each K step has a single barrier.  Each lane reads 16
+// Tiling.  Workgroup tile BM x BN x 256 (K), waves of WM x WN, each wave
+// (WM/32) x (WN/32) blocks of v_mfma_i32_32x32x32_i8.  Packed tiles go from
+// global memory straight into LDS (three stages, 16-byte chunks
+// XOR-swizzled per row), two tiles ahead of use, with a single barrier per K
+// tile.  The epilogue stages the accumulators through LDS so the fp16
+// output leaves in 16-byte row segments.  Each lane reads 16
 // packed bytes per block and K-pair: the first 8 feed one MFMA, the last 8
 // the next, so lane half h covers K offsets [32h, 32h + 32) of a 64-wide
 // K-pair.  Tiles are assigned XCD-major:
@@ -65,6 +66,30 @@ __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Byte address of a __shared__ object inside the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  typedef __attribute__((address_space(3))) const uint8_t lds_byte;
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_byte*)(p)));
+}
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds + 16 * lane (global_load_lds_dwordx4; the LDS base goes through M0,
+// which needs one wait state before the load).  Completion is counted by
+// vmcnt; the kernel below uses no other vector-memory loads while copies
+// are in flight.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const uint8_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vmcnt_6() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int WAVES_M_, int WAVES_N_, int WM_, int WN_, int BK_>
 struct GemmCfg {
   static constexpr int BK = BK_;                  // int4 elements per K tile
@@ -94,7 +119,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     int64_t ld_acc, int tiles_m, int tiles_n) {
   constexpr int FM = C::FM, FN = C::FN, CH = C::CH, BM = C::BM, BN = C::BN;
   constexpr int BKB = C::BKB, CPR = C::CPR;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3][C::STAGE];
 
   // --- tile assignment: XCD-major, then grouped along M -------------------
   const int total = tiles_m * tiles_n;
@@ -109,24 +134,40 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int wm = (wave / C::WAVES_N) * C::WM;  // wave row offset inside the tile
   const int wn = (wave % C::WAVES_N) * C::WN;  // wave col offset inside the tile
   const int kbytes = K >> 1;
 
-  // Thread tid moves chunk (tid % CPR) of tile rows tid / CPR +
-  // ROWS_PER_PASS * i (A rows first, then B rows); rows past the matrix edge
-  // re-read the last row (their results are never stored).
-  const int lrow = tid / CPR, lchunk = tid % CPR;
+  const int kfull = kbytes / BKB;  // tiles entirely inside K
+  const bool has_tail = (kbytes % BKB) != 0;
+
+  // Global -> LDS copies of the full tiles go straight into LDS
+  // (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
+  // M0 + 16 l).  Wave w's copy i fills tile rows 8 rb .. 8 rb + 7,
+  // rb = 8 i + w (A rows first, then B rows), so lane l owns row
+  // 8 rb + l / 8 and LDS slot l % 8 of it; it fetches the global chunk
+  // that the swizzle puts in that slot.  Rows past the matrix edge re-read
+  // the last row (their results are never stored).
+  static_assert(C::WAVES_M * C::WAVES_N == 8 && CPR == 8 && CH == 6,
+                "copy mapping assumes 8 waves, 128-byte rows, 6 copies per lane");
   const uint8_t* src[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int r = lrow + C::ROWS_PER_PASS * i;
-    src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * lchunk
-                      : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb + 16 * lchunk;
+    const int rb = 8 * i + wave;
+    const int r = 8 * rb + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * c
+                      : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb + 16 * c;
   }
-  const int kfull = kbytes / BKB;  // tiles entirely inside K
-  const bool has_tail = (kbytes % BKB) != 0;
+  const uint32_t lds0 = lds_address(&smem[0][0]);
+  // copy full tile t (clamped to the last full tile) into stage st
+#define QR_COPY(st, t)                                                                     \
+  {                                                                                        \
+    const int64_t kb0_ = int64_t(min((t), kfull - 1)) * BKB;                               \
+    _Pragma("unroll") for (int i = 0; i < CH; ++i)                                         \
+        lds_copy16(src[i] + kb0_, lds0 + uint32_t((st) * C::STAGE + (8 * i + wave) * 1024)); \
+  }
 
   v16i acc[FM][FN];
 #pragma unroll
@@ -136,112 +177,190 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
 
   const int frow = lane & 31;   // row (A) / column (B) of the fragment
   const int fhalf = lane >> 5;  // which 16-byte chunk of a 32-byte K-pair
-  // All fragment reads of a tile are issued before its MFMAs so the LDS
-  // latency overlaps the first MFMAs instead of stalling each K-pair.
   constexpr int KP = BKB / 32;  // 64-wide K-pairs per tile
-  auto compute_tile = [&](int buf) {
-    const uint8_t* sa = smem[buf];
-    const uint8_t* sb = smem[buf] + BM * BKB;
-    uint4 fa[KP][FM], fb[KP][FN];
-#pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[kp][i] = ld16(sa + lds_off<BKB>(wm + i * 32 + frow, 2 * kp + fhalf));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[kp][j] = ld16(sb + lds_off<BKB>(wn + j * 32 + frow, 2 * kp + fhalf));
-    }
-#pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
-      v4i alo[FM], ahi[FM], blo[FN], bhi[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) widen(fa[kp][i], alo[i], ahi[i]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) widen(fb[kp][j], blo[j], bhi[j]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[i], blo[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[i], bhi[j], acc[i][j], 0, 0, 0);
-        }
-    }
-  };
+  static_assert(KP == 4, "the schedule below assumes four K-pairs per tile");
 
-  // Pipeline over the full tiles: tile kt is computed from one LDS buffer,
-  // then tile kt+1 goes from registers into the other buffer while tiles
-  // kt+2 and kt+3 are in flight from memory.  The loop is unrolled by two
-  // so each register set keeps a fixed role, and loads are issued every step
-  // (past the end they re-read the last full tile) so every path through the
-  // loop has the same wait counts.
-  uint4 r0[CH], r1[CH];
-#define QR_LOAD(r, kb0)                                          \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) r[i] = ld16(src[i] + (kb0))
-#define QR_STORE(buf, r)                                                                  \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) *reinterpret_cast<uint4*>(               \
-      smem[buf] + lds_off<BKB>(lrow + C::ROWS_PER_PASS * i, lchunk)) = r[i]
-  if (kfull > 0) {
-    // Step i: compute tile i from buffer i % 2, store tile i+1 (in registers
-    // since step i-2) into the other buffer, issue the loads of tile i+3 into
-    // the registers just freed, one barrier.  sched_barrier keeps that order.
-    QR_LOAD(r0, 0);
-    QR_LOAD(r1, min(1, kfull - 1) * BKB);
-    QR_STORE(0, r0);
-    QR_LOAD(r0, min(2, kfull - 1) * BKB);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 2 <= kfull; kt += 2) {
-      compute_tile(0);  // tile kt
-      __builtin_amdgcn_sched_barrier(0);
-      QR_STORE(1, r1);  // tile kt+1
-      QR_LOAD(r1, min(kt + 3, kfull - 1) * BKB);
-      __syncthreads();
-      compute_tile(1);  // tile kt+1
-      __builtin_amdgcn_sched_barrier(0);
-      QR_STORE(0, r0);  // tile kt+2 (a harmless repeat past the end)
-      QR_LOAD(r0, min(kt + 4, kfull - 1) * BKB);
-      __syncthreads();
-    }
-    if (kt < kfull) compute_tile(0);  // odd count: the last full tile is in buffer 0
+  // Packed fragments of one K-pair (16 bytes per block and lane), their
+  // widened int8 form, and the MFMAs.  Two sets of each: the reads run two
+  // K-pairs ahead of the MFMAs and the widening one K-pair ahead.
+  uint4 ra0[FM], rb0[FN], ra1[FM], rb1[FN];
+  v4i al0[FM], ah0[FM], bl0[FN], bh0[FN], al1[FM], ah1[FM], bl1[FN], bh1[FN];
+#define QR_READ(n, st, kp)                                                                    \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) ra##n[i] =                                  \
+      ld16(smem[st] + lds_off<BKB>(wm + i * 32 + frow, 2 * (kp) + fhalf));                  \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) rb##n[j] =                                  \
+      ld16(smem[st] + BM * BKB + lds_off<BKB>(wn + j * 32 + frow, 2 * (kp) + fhalf))
+#define QR_WIDEN(n)                                                                           \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) widen(ra##n[i], al##n[i], ah##n[i]);        \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) widen(rb##n[j], bl##n[j], bh##n[j])
+// (all low halves first: the two MFMAs into one accumulator are FM * FN
+// instructions apart, not back to back)
+#define QR_MFMA(n)                                                                            \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                              \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                              \
+    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al##n[i], bl##n[j], acc[i][j], 0, 0, 0); \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                              \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                              \
+    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah##n[i], bh##n[j], acc[i][j], 0, 0, 0);
+  // One pipeline step: LDS reads first, then each MFMA followed by a share
+  // of the next K-pair's widening, so the VALU work runs in the MFMAs'
+  // shadow instead of ahead of them.
+#define QR_INTERLEAVE()                                                    \
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FM + FN), 0);          \
+  _Pragma("unroll") for (int q = 0; q < 2 * FM * FN; ++q) {               \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    \
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                    \
   }
+#define QR_STEP(rd, cur, st, kp) \
+  QR_READ(rd, st, kp);           \
+  QR_WIDEN(rd == 0 ? 1 : 0);     \
+  QR_MFMA(cur);                  \
+  QR_INTERLEAVE()
+
+  // Three LDS stages; tile kt lives in stage kt % 3.  Step g (K-pair
+  // g = 4 kt + kp) reads K-pair g + 2 from LDS into register set g % 2,
+  // widens K-pair g + 1 (read one step earlier) into the other widened set,
+  // and runs the MFMAs of K-pair g.  Per tile one barrier, between kp1 and
+  // kp2:
+  //   kp0: copy tile kt+2 into stage (kt+2) % 3 (= the stage of tile kt-1,
+  //        whose reads all finished before the previous barrier); step
+  //   kp1: step (reads tile kt's last K-pair); wait until tile kt+1 has
+  //        landed (its copies were issued one tile earlier; only tile kt+2's
+  //        six may still be in flight); barrier
+  //   kp2, kp3: steps whose reads are tile kt+1's first two K-pairs
+  // Copies past the last full tile repeat it into a stage nobody reads
+  // again, and the reads that run past the end are harmless, so every
+  // iteration has the same counts.
+  if (kfull > 0) {
+    QR_COPY(0, 0);
+    QR_COPY(1, 1);
+    wait_vmcnt_6();  // tile 0 landed
+    __syncthreads();
+    QR_READ(0, 0, 0);
+    QR_READ(1, 0, 1);
+    QR_WIDEN(0);
+    int st = 0;  // stage of tile kt
+    for (int kt = 0; kt < kfull; ++kt) {
+      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+      QR_COPY(st2, kt + 2);
+      // kp0: read kp2 into set 0, widen kp1 (set 1), MFMAs kp0 (set 0)
+      QR_READ(0, st, 2);
+      QR_WIDEN(1);
+      QR_MFMA(0);
+      QR_INTERLEAVE();
+      // kp1: read kp3 into set 1, widen kp2 (set 0), MFMAs kp1 (set 1)
+      QR_READ(1, st, 3);
+      QR_WIDEN(0);
+      QR_MFMA(1);
+      QR_INTERLEAVE();
+      wait_vmcnt_6();  // tile kt+1 landed
+      __syncthreads();
+      // kp2: read tile kt+1 kp0 into set 0, widen kp3 (set 1), MFMAs kp2 (set 0)
+      QR_READ(0, st1, 0);
+      QR_WIDEN(1);
+      QR_MFMA(0);
+      QR_INTERLEAVE();
+      // kp3: read tile kt+1 kp1 into set 1, widen tile kt+1 kp0 (set 0), MFMAs kp3 (set 1)
+      QR_READ(1, st1, 1);
+      QR_WIDEN(0);
+      QR_MFMA(1);
+      QR_INTERLEAVE();
+      st = st1;
+    }
+    wait_vmcnt_0();  // the trailing repeat copies, before any stage is rewritten
+  }
+#undef QR_COPY
   if (has_tail) {  // the partial tile at the end of K: chunks past K read as zero
     __syncthreads();
+    const int lrow = tid / CPR, lchunk = tid % CPR;
     const int kb0 = kfull * BKB;
     const bool ok = kb0 + 16 * lchunk < kbytes;
-    QR_LOAD(r0, ok ? kb0 : 0);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) r0[i] = ok ? r0[i] : make_uint4(0, 0, 0, 0);
-    QR_STORE(1, r0);
+    for (int i = 0; i < CH; ++i) {
+      const int r = lrow + C::ROWS_PER_PASS * i;
+      const uint8_t* p = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda
+                                  : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb;
+      const uint4 v = ok ? ld16(p + kb0 + 16 * lchunk) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(smem[0] + lds_off<BKB>(r, lchunk)) = v;
+    }
     __syncthreads();
-    compute_tile(1);
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
+      QR_READ(0, 0, kp);
+      QR_WIDEN(0);
+      QR_MFMA(0);
+    }
   }
-#undef QR_LOAD
-#undef QR_STORE
+#undef QR_READ
+#undef QR_WIDEN
+#undef QR_MFMA
+#undef QR_INTERLEAVE
+#undef QR_STEP
 
   // --- epilogue: acc / 256 -> fp32 * scale_x * scale_w -> fp16 -----------
-  // 32x32 block layout: lane holds column (lane & 31); register r holds row
-  // 8 * (r / 4) + 4 * (lane / 32) + (r % 4).
-  float sx[FM][16];
+  // The accumulators go through LDS so that each lane ends up with 8
+  // consecutive columns of one row: 16-byte output stores instead of 2-byte
+  // ones.  32x32 block layout: lane holds column (lane & 31); register r
+  // holds row 8 * (r / 4) + 4 * (lane / 32) + (r % 4).  Each wave owns a
+  // [WM][WN + 8] int32 staging tile (the 8-word pad puts the rows r and r + 4
+  // written by one instruction on opposite bank halves).
+  constexpr int WM = C::WM, WN = C::WN, LDS_ROW = WN + 8;
+  static_assert(C::WAVES_M * C::WAVES_N * WM * LDS_ROW * 4 <= 3 * C::STAGE,
+                "staging tiles must fit in the pipeline's LDS");
+  __syncthreads();  // every wave is done reading the last K tile
+  int32_t* stg = reinterpret_cast<int32_t*>(&smem[0][0]) + wave * (WM * LDS_ROW);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      sx[i][r] = __half2float(a_scale[min(row, M - 1)]);
-    }
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = n0 + wn + j * 32 + (lane & 31);
-    const bool col_ok = col < N;
-    const float sw = __half2float(b_scale[min(col, N - 1)]);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (!col_ok || row >= M) continue;
-        const int32_t v = acc[i][j][r] >> 8;
-        c[int64_t(row) * ldc + col] = __float2half_rn((float(v) * sx[i][r]) * sw);
-        if (acc_out) acc_out[int64_t(row) * ld_acc + col] = v;
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        stg[row * LDS_ROW + j * 32 + (lane & 31)] = acc[i][j][r] >> 8;
+      }
+  __syncthreads();
+  // lane -> columns 8 cg .. 8 cg + 7 of the wave tile, rows lane / 8 + 8 s
+  constexpr int CG = WN / 8, RSTEP = 64 / CG;
+  const int cg = lane % CG, r0 = lane / CG;
+  const int col0 = n0 + wn + 8 * cg;
+  float sw[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sw[k] = __half2float(b_scale[min(col0 + k, N - 1)]);
+  const bool full_cols = col0 + 8 <= N;
+  const bool vec_c = full_cols && (ldc % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0;
+  const bool vec_acc = full_cols && acc_out && (ld_acc % 4) == 0 &&
+                       (reinterpret_cast<uintptr_t>(acc_out) % 16) == 0;
+#pragma unroll
+  for (int sidx = 0; sidx < WM / RSTEP; ++sidx) {
+    const int lrow_ = r0 + RSTEP * sidx;
+    const int row = m0 + wm + lrow_;
+    if (row >= M) continue;
+    const float sx = __half2float(a_scale[row]);
+    const int4 v0 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg);
+    const int4 v1 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg + 4);
+    const int v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    __half h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = __float2half_rn((float(v[k]) * sx) * sw[k]);
+    __half* crow = c + int64_t(row) * ldc + col0;
+    if (vec_c) {
+      uint4 pk;
+      __builtin_memcpy(&pk, h, 16);
+      *reinterpret_cast<uint4*>(crow) = pk;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (col0 + k < N) crow[k] = h[k];
+    }
+    if (acc_out) {
+      int32_t* arow = acc_out + int64_t(row) * ld_acc + col0;
+      if (vec_acc) {
+        *reinterpret_cast<int4*>(arow) = v0;
+        *reinterpret_cast<int4*>(arow + 4) = v1;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (col0 + k < N) arow[k] = v[k];
       }
     }
   }
