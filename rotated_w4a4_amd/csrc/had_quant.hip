@@ -11,8 +11,8 @@
 //
 // Kernels:
 //   * had_quant_quad<D>   d = 32..256: a quad of lanes per row (quad_rows.h).
-//   * had_quant_4096      d = 4096: a wave per row, one LDS exchange
-//                         (wave_rows.h).
+//   * had_quant_4096_split  d = 4096: four waves per row, one LDS exchange
+//                         (split_rows.h).
 //   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
 //                         on the matrix cores, one LDS exchange (kron_rows.h).
 //   * had_quant_lds<M>    any supported d (<= 32768): one workgroup per row,
@@ -22,6 +22,7 @@
 #include "quad_rows.h"
 #include "wave_rows.h"
 #include "kron_rows.h"
+#include "split_rows.h"
 
 namespace quarot {
 
@@ -225,18 +226,16 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
     return check_launch("had_quant_quad");
   }
   if (m == 1 && d == 4096) {
-    const int64_t rpb = kWaveRowsBlock / 64;
-    int64_t blocks = (rows + rpb - 1) / rpb;
-    const int64_t cap = int64_t(cus) * 2;  // 64 KiB LDS per block: two blocks per CU
-    if (blocks > cap) blocks = cap;
-    const dim3 grid{unsigned(blocks)}, block{unsigned(kWaveRowsBlock)};
+    const int64_t cap = int64_t(cus) * 8;  // 16 KiB LDS, two waves per block
+    const int64_t blocks = rows < cap ? rows : cap;
+    const dim3 grid{unsigned(blocks)}, block{unsigned(kSplitBlock)};
     if (clip_ratio == 1.0f)
-      hipLaunchKernelGGL(had_quant_4096<false>, grid, block, 0, stream, x, rows, ld_x, signs,
+      hipLaunchKernelGGL(had_quant_4096_split<false>, grid, block, 0, stream, x, rows, ld_x, signs,
                          clip_ratio, q_out, ld_q, scale_out, x_rot_out);
     else
-      hipLaunchKernelGGL(had_quant_4096<true>, grid, block, 0, stream, x, rows, ld_x, signs,
+      hipLaunchKernelGGL(had_quant_4096_split<true>, grid, block, 0, stream, x, rows, ld_x, signs,
                          clip_ratio, q_out, ld_q, scale_out, x_rot_out);
-    return check_launch("had_quant_4096");
+    return check_launch("had_quant_4096_split");
   }
   if ((m == 12 || m == 28) && d == 1024 * m) {
     static const bool kron_attr_ok = [] {
