@@ -80,14 +80,21 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
-def time_kernel(torch, stream, launch, count: int) -> float:
-    """Average duration (ms) of `count` back-to-back launches on `stream`."""
+def time_kernel(torch, stream, launch, count: int, lead: int = 10) -> float:
+    """Average duration (ms) of `count` back-to-back launches on `stream`.
+
+    A spin kernel holds the stream while the host enqueues everything, so no
+    host launch latency lands between the events; `lead` untimed launches run
+    right before the first event so the clocks have left the spin's idle
+    state."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(SPIN_CYCLES)
+    for i in range(lead):
+        launch(i)
     e0.record(stream)
     for i in range(count):
-        launch(i)
+        launch(lead + i)
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / count

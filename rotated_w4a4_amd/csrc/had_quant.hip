@@ -41,19 +41,14 @@ __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
   load_sign_masks<NC>(signs, lane_q, mask);
   const int64_t rows_per_block = kQuadBlock / 4;
   const int64_t step = int64_t(gridDim.x) * rows_per_block;
-  int64_t r = int64_t(blockIdx.x) * rows_per_block + (threadIdx.x >> 2);
-  // one row ahead: the next row's loads are in flight while this one computes
-  uint4 raw[NC];
-  quad_load<D>(x + (r < rows ? r : 0) * ld_x, lane_q, raw);
-  for (int64_t base = int64_t(blockIdx.x) * rows_per_block; base < rows; base += step, r += step) {
+  // the grid normally covers every row once; the loop serves capped grids
+  for (int64_t base = int64_t(blockIdx.x) * rows_per_block; base < rows; base += step) {
+    const int64_t r = base + (threadIdx.x >> 2);
     const bool active = r < rows;
     const int64_t rr = active ? r : 0;
-    uint4 cur[NC];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) cur[j] = raw[j];
-    const int64_t nr = r + step;
-    quad_load<D>(x + (nr < rows ? nr : 0) * ld_x, lane_q, raw);
-    quad_row<D, CLAMP>(cur, q_out + rr * ld_q, scale_out + rr, x_rot ? x_rot + rr * D : nullptr,
+    uint4 raw[NC];
+    quad_load<D>(x + rr * ld_x, lane_q, raw);
+    quad_row<D, CLAMP>(raw, q_out + rr * ld_q, scale_out + rr, x_rot ? x_rot + rr * D : nullptr,
                        mask, lane_q, clip_ratio, active);
   }
 }
@@ -209,7 +204,7 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
   if (m == 1 && d <= 256) {
     const int64_t rpb = kQuadBlock / 4;
     int64_t blocks = (rows + rpb - 1) / rpb;
-    const int64_t cap = int64_t(cus) * 8;
+    const int64_t cap = int64_t(1) << 24;  // grid limit; beyond it blocks loop
     if (blocks > cap) blocks = cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kQuadBlock)};
 #define QR_QUAD(DD, CL)                                                                 \

@@ -68,29 +68,23 @@ __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
   uint4 mask[NC];
   int64_t mask_head = -1;
   uint32_t g = blockIdx.x * per_block + (threadIdx.x >> 2);
-  // one group ahead: the next group's loads are in flight while this one computes
-  uint32_t h;
-  int64_t src_off, slot;
-  kv_group(p, g < p.groups ? g : 0, h, src_off, slot);
-  uint4 raw[NC];
-  quad_load<D>(t.src + src_off, lane_q, raw);
+  // The grid normally covers every group once (a streaming kernel wants
+  // all loads in flight at once rather than a prefetch chain), the loop only
+  // serves grids capped below that.
   for (uint32_t base = blockIdx.x * per_block; base < p.groups; base += step, g += step) {
     const bool active = g < p.groups;
-    const uint32_t hc = h;
-    const int64_t slot_c = slot;
-    uint4 cur[NC];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) cur[j] = raw[j];
-    const uint32_t ng = g + step;
-    kv_group(p, ng < p.groups ? ng : 0, h, src_off, slot);
+    uint32_t h;
+    int64_t src_off, slot;
+    kv_group(p, active ? g : 0, h, src_off, slot);
+    uint4 raw[NC];
     quad_load<D>(t.src + src_off, lane_q, raw);
     // signs: one vector per head (stride 0: shared by all heads)
-    const int64_t head_key = p.signs_stride_h ? int64_t(hc) : 0;
+    const int64_t head_key = p.signs_stride_h ? int64_t(h) : 0;
     if (head_key != mask_head) {
       load_sign_masks<NC>(p.signs ? p.signs + head_key * p.signs_stride_h : nullptr, lane_q, mask);
       mask_head = head_key;
     }
-    quad_row<D, CLAMP>(cur, t.q + slot_c * (D / 2), t.scale + slot_c, nullptr, mask, lane_q,
+    quad_row<D, CLAMP>(raw, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
                        p.clip_ratio, active);
   }
 }
@@ -115,13 +109,10 @@ int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t
   p.clip_ratio = clip_ratio;
   p.S_cache = S_cache;
   p.pos0 = pos0;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t groups = B * H * S;
   const int64_t per_block = kBlock / 4;
   int64_t blocks = (groups + per_block - 1) / per_block;
-  const int64_t cap = int64_t(cus > 0 ? cus : 256) * 8 / n_tensors;
+  const int64_t cap = int64_t(1) << 24;  // grid limit; beyond it blocks loop
   if (blocks > cap) blocks = cap;
   const dim3 grid{unsigned(blocks), unsigned(n_tensors)}, block{unsigned(kBlock)};
 #define QR_KV(DD, CL) hipLaunchKernelGGL((kv_had_quant_kernel<DD, CL>), grid, block, 0, stream, p)
