@@ -10,8 +10,9 @@
 * KV cache (same page, Stage 1d "online head-wise rotation after RoPE" and
   Stage 2c; "QuaRot Guide", step 4 of "Deep Dive"): each (batch, head,
   position) vector of head_dim values is rotated by the head-wise Hadamard and
-  quantised as one group.  This module implements the symmetric per-group
-  variant (fp16 scale, no zero point).
+  quantised as one group: symmetric (fp16 scale, int4 codes; the configured
+  KV workload) or asymmetric (fp16 scale, fp16 integer zero point, uint4
+  codes; Stage 2c's own quantiser, clip 0.95).
 """
 
 from __future__ import annotations
@@ -19,10 +20,10 @@ from __future__ import annotations
 import numpy as np
 
 from .gemm import w4a4_reference
-from .quant import pack_int4, quantize_rows
+from .quant import pack_int4, pack_uint4, quantize_rows, quantize_rows_asym
 from .rotate import rotate_rows
 
-__all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant"]
+__all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant", "kv_had_quant_asym"]
 
 
 def had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0):
@@ -63,4 +64,23 @@ def kv_had_quant(t: np.ndarray, signs: np.ndarray, clip_ratio: float = 1.0):
         "codes": r["codes"].reshape(b, h, s, d),
         "packed": r["packed"].reshape(b, h, s, d // 2),
         "scales": r["scales"].reshape(b, h, s),
+    }
+
+
+def kv_had_quant_asym(t: np.ndarray, signs: np.ndarray, clip_ratio: float = 0.95):
+    """Asymmetric per-(b, h, s) group quantisation of a [B, H, S, D] tensor.
+
+    Returns dict(x_rot float64, codes uint8 [B,H,S,D], packed uint8
+    [B,H,S,D/2], scales fp16 [B,H,S], zeros int32 [B,H,S]).
+    """
+    t = np.asarray(t)
+    b, h, s, d = t.shape
+    x_rot = rotate_rows(t.reshape(-1, d), signs, 1)
+    codes, scales, zeros = quantize_rows_asym(x_rot, clip_ratio)
+    return {
+        "x_rot": x_rot.reshape(b, h, s, d),
+        "codes": codes.reshape(b, h, s, d),
+        "packed": pack_uint4(codes).reshape(b, h, s, d // 2),
+        "scales": scales.reshape(b, h, s),
+        "zeros": zeros.reshape(b, h, s),
     }

@@ -34,6 +34,12 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "ZMAX",
+    "asym_params",
+    "asym_codes",
+    "quantize_rows_asym",
+    "pack_uint4",
+    "unpack_uint4",
     "QMIN",
     "QMAX",
     "ABSMAX_FLOOR",
@@ -92,4 +98,77 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int8)
     out[..., 0::2] = lo
     out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Asymmetric per-group INT4 (the KV cache's own quantiser)
+#
+# "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
+# summary), section 3.4 Stage 2c: per-group asymmetric quantisation with a
+# scale and a zero point, s = (alpha_max - alpha_min) / (2^b - 1), the range
+# taken with a clipping ratio of 0.95, group = the 128 values of one head.
+# The page's zero-point formula mixes units (it subtracts round(alpha_min /
+# s) from a value in real units); the reading used here is the textbook
+# uint4 form that the rest of the passage describes:
+#   alpha_min = clip * min(x),  alpha_max = clip * max(x)
+#   S = fp16(max(alpha_max - alpha_min, 1e-5) / 15)
+#   z = clamp(rint(-alpha_min / S), -ZMAX, ZMAX)          (integer zero point)
+#   q = clamp(rint(x / S) + z, 0, 15)                     (uint4 code)
+#   x_hat = S * (q - z)
+# with the same precision conventions as the symmetric quantiser: S is the
+# stored fp16 scale; alpha and the zero-point division are taken in fp32
+# (the fp32 value of x~), x / S in fp32 with ties to even; z is kept within
+# +-ZMAX so it is exactly representable in the fp16 it is stored in.
+# ---------------------------------------------------------------------------
+
+ZMAX = 1024
+UQMAX = 15
+
+
+def asym_params(x_rot: np.ndarray, clip_ratio: float = 0.95):
+    """Per-row (scale fp16, zero point int32) of the asymmetric quantiser."""
+    if not (0.0 < clip_ratio <= 1.0):
+        raise ValueError("clip_ratio must be in (0, 1]")
+    x32 = np.asarray(x_rot).astype(np.float32)
+    c = np.float32(clip_ratio)
+    amin = c * x32.min(axis=1)
+    amax = c * x32.max(axis=1)
+    rng = np.maximum(amax - amin, np.float32(ABSMAX_FLOOR))
+    s16 = (rng / np.float32(UQMAX)).astype(np.float16)
+    z = np.rint(-amin / s16.astype(np.float32))
+    z = np.clip(z, -ZMAX, ZMAX).astype(np.int32)
+    return s16, z
+
+
+def asym_codes(x_rot: np.ndarray, scales16: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """q = clamp(rint(fp32(x) / fp32(S)) + z, 0, 15), one (S, z) per row (uint8)."""
+    x32 = np.asarray(x_rot).astype(np.float32)
+    s32 = np.asarray(scales16, dtype=np.float16).astype(np.float32)[:, None]
+    r = np.rint(x32 / s32) + np.asarray(zeros, dtype=np.float32)[:, None]
+    return np.clip(r, 0, UQMAX).astype(np.uint8)
+
+
+def quantize_rows_asym(x_rot: np.ndarray, clip_ratio: float = 0.95):
+    """Per-row asymmetric uint4: returns (codes uint8, scales fp16, zeros int32)."""
+    s, z = asym_params(x_rot, clip_ratio)
+    return asym_codes(x_rot, s, z), s, z
+
+
+def pack_uint4(codes: np.ndarray) -> np.ndarray:
+    """Two uint4 codes per byte: byte k = q[2k] | (q[2k+1] << 4)."""
+    q = np.asarray(codes, dtype=np.int64)
+    if q.shape[-1] % 2:
+        raise ValueError("need an even number of codes per row")
+    if q.min(initial=0) < 0 or q.max(initial=0) > UQMAX:
+        raise ValueError("uint4 codes must be in [0, 15]")
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_uint4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_uint4 (uint8 codes in [0, 15])."""
+    b = np.asarray(packed, dtype=np.int64)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = (b >> 4) & 0xF
     return out

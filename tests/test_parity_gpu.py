@@ -145,7 +145,8 @@ def test_gemm_fed_oracle_codes(name, mr, nr):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 65, 96), (129, 257, 160), (256, 512, 384),
-                                   (300, 700, 1056)])
+                                   (300, 700, 1056), (130, 260, 256), (64, 256, 512),
+                                   (200, 300, 832), (128, 256, 1280), (257, 513, 1792)])
 def test_gemm_ragged_shapes(M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
@@ -349,3 +350,26 @@ def test_had_quant_kron_rows_strided_grid_stride(m, clip):
     check_scales(host(s), ref["scales"])
     check_codes(oracle.unpack_int4(qh[:, : d // 2]), ref["codes"])
     assert np.all(qh[5, : d // 2] == 0)
+
+
+def test_gemm_strided_outputs():
+    # output rows with ld % 8 != 0 and an accumulator row stride % 4 != 0 take
+    # the element-wise epilogue stores; a guard band past each row must stay
+    # untouched
+    rng = np.random.default_rng(31)
+    M, N, K = 150, 264, 768
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, M).astype(np.float16)
+    sb = rng.uniform(0.001, 0.1, N).astype(np.float16)
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    say(f"gemm strided outputs M={M} N={N} K={K}")
+    ybuf = torch.full((M, N + 3), 7.0, dtype=torch.float16, device="cuda")
+    abuf = torch.full((M, N + 5), -123, dtype=torch.int32, device="cuda")
+    qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(sa), dev(oracle.pack_int4(qb)), dev(sb), K,
+                 out=ybuf[:, :N], acc_out=abuf[:, :N])
+    yh, ah = host(ybuf), host(abuf)
+    np.testing.assert_array_equal(ah[:, :N], acc_ref)
+    assert np.all(ah[:, N:] == -123)
+    assert np.all(yh[:, N:] == np.float16(7.0))
+    check_y_elementwise(yh[:, :N], y_ref)
