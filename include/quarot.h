@@ -126,11 +126,22 @@ int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
  *
  * For every (b, h, s) with 0 <= s < S, the D values
  * t[b][h][s][:] (element (b,h,s,i) at t + b*stride_b + h*stride_h +
- * s*stride_s + i) are rotated by diag(signs_h) then the Sylvester H_D / sqrt(D),
- * and quantised as one group exactly like quarot_had_quant (mode 0), with
- * the code row written to cache position p = pos0 + s:
+ * s*stride_s + i) are rotated by diag(signs_h) then the Sylvester H_D / sqrt(D)
+ * and quantised as one group, with the code row written to cache position
+ * p = pos0 + s:
  *   t_q    [B x H x S_cache x D/2] uint8, contiguous, row (b,h,p)
- *   t_scale[B x H x S_cache]       fp16, contiguous.
+ *   t_scale[B x H x S_cache]       fp16, contiguous
+ *   t_zero [B x H x S_cache]       fp16, contiguous (mode 1 only).
+ * mode 0 (symmetric, the configured cache workload): exactly like
+ *   quarot_had_quant: S = fp16(clip * max(max|x~|, 1e-5) / 7),
+ *   q = clamp(rint(x~ / S), -8, 7) as two's complement nibbles.
+ * mode 1 (asymmetric, [S] Stage 2c's own KV quantiser; the pages use
+ *   clip 0.95): alpha_min = clip * min x~, alpha_max = clip * max x~,
+ *   S = fp16(max(alpha_max - alpha_min, 1e-5) / 15),
+ *   z = clamp(rint(-alpha_min / S), -1024, 1024) stored as fp16 (exact),
+ *   q = clamp(rint(x~ / S) + z, 0, 15) as unsigned nibbles; x^ = S (q - z).
+ * In both modes element 2k goes to the low nibble of byte k; the decisions
+ * are taken in fp32 from the stored fp16 scale.
  *
  * Arguments:
  *   k, v         fp16 inputs; either may be NULL (that tensor is skipped),
@@ -139,13 +150,15 @@ int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
  *   D            head dimension: 32, 64, 128 or 256.
  *   signs        int8 +1/-1; head h uses signs + h*signs_stride_h (stride 0:
  *                one vector shared by all heads).  NULL = all +1.
- *   mode         0 = symmetric (scale only).  1 = asymmetric with zero point
- *                (reserved; returns QUAROT_ERR_UNSUPPORTED).
+ *   mode         0 = symmetric, 1 = asymmetric with a zero point.
  *   clip_ratio   in (0, 1].
  *   k_q/v_q      16-byte aligned cache code buffers; k_scale/v_scale fp16.
- *   k_zero/v_zero  reserved for mode 1; ignored in mode 0.
+ *   k_zero/v_zero  fp16, 2-byte aligned; required in mode 1 for every tensor
+ *                given, ignored in mode 0.
  *   S_cache, pos0  cache length and first position written;
  *                0 <= pos0 and pos0 + S <= S_cache.
+ * Errors: INVALID for bad sizes, mode, clip or missing buffers;
+ * UNSUPPORTED for other D or B*H*S >= 2^31; MISALIGNED as stated.
  */
 int quarot_kv_had_quant(const void* k, const void* v,
                         int64_t B, int64_t H, int64_t S, int64_t D,

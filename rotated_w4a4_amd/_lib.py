@@ -163,8 +163,13 @@ def w4a4_gemm(a_q, a_scale, b_q, b_scale, k: int, out=None, acc_out=None, stream
 
 
 def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0: int = 0,
-                 signs_stride_h: int = 0, clip_ratio: float = 1.0, mode: int = 0, stream=None):
-    """Quantise K (and V) [B, H, S, D] into caches [B, H, S_cache, D/2] at pos0."""
+                 signs_stride_h: int = 0, clip_ratio: float = 1.0, mode: int = 0,
+                 k_zero=None, v_zero=None, stream=None):
+    """Quantise K (and V) [B, H, S, D] into caches [B, H, S_cache, D/2] at pos0.
+
+    mode 0: symmetric int4 codes + fp16 scales.  mode 1: asymmetric uint4
+    codes + fp16 scales + fp16 zero points (k_zero / v_zero, shaped like the
+    scales); the pages use clip_ratio 0.95 for it."""
     torch = _torch()
     ref = k if k is not None else v
     _need(ref, torch.float16, "k/v", 4)
@@ -177,11 +182,15 @@ def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0
             raise ValueError(f"{name} must be [B, H, S, D] with contiguous D")
         if t.stride() != ref.stride():
             raise ValueError("k and v must share strides")
-    caches = [(k, k_cache, k_scale, "k"), (v, v_cache, v_scale, "v")]
+    caches = [(k, k_cache, k_scale, k_zero, "k"), (v, v_cache, v_scale, v_zero, "v")]
     S_cache = None
-    for t, cq, cs, name in caches:
+    for t, cq, cs, cz, name in caches:
         if t is None:
             continue
+        if mode == 1:
+            _need(cz, torch.float16, f"{name}_zero", 3)
+            if not cz.is_contiguous() or tuple(cz.shape) != tuple(cs.shape):
+                raise ValueError(f"{name}_zero must be contiguous and shaped like {name}_scale")
         _need(cq, torch.uint8, f"{name}_cache", 4)
         _need(cs, torch.float16, f"{name}_scale", 3)
         if not cq.is_contiguous() or not cs.is_contiguous():
@@ -200,9 +209,13 @@ def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0
     st = lib().quarot_kv_had_quant(_ptr(k), _ptr(v), B, H, S, D, sb, sh, ss, _ptr(signs),
                                    int(signs_stride_h), int(mode), float(clip_ratio),
                                    _ptr(k_cache) if k is not None else None,
-                                   _ptr(k_scale) if k is not None else None, None,
+                                   _ptr(k_scale) if k is not None else None,
+                                   _ptr(k_zero) if (k is not None and mode == 1) else None,
                                    _ptr(v_cache) if v is not None else None,
-                                   _ptr(v_scale) if v is not None else None, None,
+                                   _ptr(v_scale) if v is not None else None,
+                                   _ptr(v_zero) if (v is not None and mode == 1) else None,
                                    S_cache, int(pos0), _stream(stream))
     _check("quarot_kv_had_quant", st)
+    if mode == 1:
+        return k_cache, k_scale, k_zero, v_cache, v_scale, v_zero
     return k_cache, k_scale, v_cache, v_scale

@@ -146,13 +146,10 @@ int quarot_kv_had_quant(const void* k, const void* v,
                         uint8_t* v_q, void* v_scale, void* v_zero,
                         int64_t S_cache, int64_t pos0, void* stream) {
   clear_error();
-  (void)k_zero;
-  (void)v_zero;
   QR_CHECK_ARG(B >= 0 && H >= 0 && S >= 0, QUAROT_ERR_INVALID, "B, H, S must be >= 0");
   QR_CHECK_ARG(D == 32 || D == 64 || D == 128 || D == 256, QUAROT_ERR_UNSUPPORTED,
                "D = %lld: supported head dims are 32, 64, 128, 256", (long long)D);
   QR_CHECK_ARG(mode == 0 || mode == 1, QUAROT_ERR_INVALID, "mode must be 0 or 1");
-  QR_CHECK_ARG(mode == 0, QUAROT_ERR_UNSUPPORTED, "mode 1 (asymmetric) is not implemented");
   QR_CHECK_ARG(clip_ok(clip_ratio), QUAROT_ERR_INVALID, "clip_ratio must be in (0, 1]");
   QR_CHECK_ARG(stride_b >= 0 && stride_h >= 0 && stride_s >= 0 && signs_stride_h >= 0,
                QUAROT_ERR_INVALID, "strides must be >= 0");
@@ -167,18 +164,23 @@ int quarot_kv_had_quant(const void* k, const void* v,
   const void* srcs[2] = {k, v};
   uint8_t* qs[2] = {k_q, v_q};
   void* ss[2] = {k_scale, v_scale};
+  void* zs[2] = {k_zero, v_zero};
   for (int i = 0; i < 2; ++i) {
     if (!srcs[i]) continue;
     QR_CHECK_ARG(qs[i] && ss[i], QUAROT_ERR_INVALID, "%s_q and %s_scale are required",
                  i ? "v" : "k", i ? "v" : "k");
-    QR_CHECK_ARG(aligned(srcs[i], 16) && aligned(qs[i], 16) && aligned(ss[i], 2),
+    QR_CHECK_ARG(mode == 0 || zs[i], QUAROT_ERR_INVALID, "mode 1 needs %s_zero",
+                 i ? "v" : "k");
+    QR_CHECK_ARG(aligned(srcs[i], 16) && aligned(qs[i], 16) && aligned(ss[i], 2) &&
+                     (mode == 0 || aligned(zs[i], 2)),
                  QUAROT_ERR_MISALIGNED, "inputs and code buffers must be 16-byte aligned");
     t[nt++] = KvTensorArgs{static_cast<const __half*>(srcs[i]), qs[i],
-                           static_cast<__half*>(ss[i])};
+                           static_cast<__half*>(ss[i]),
+                           mode == 1 ? static_cast<__half*>(zs[i]) : nullptr};
   }
   QR_CHECK_ARG(B * H * S < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED, "too many groups");
   return launch_kv_had_quant(t, nt, B, H, S, int(D), stride_b, stride_h, stride_s, signs,
-                             signs_stride_h, clip_ratio, S_cache, pos0,
+                             signs_stride_h, int(mode), clip_ratio, S_cache, pos0,
                              static_cast<hipStream_t>(stream));
 }
 

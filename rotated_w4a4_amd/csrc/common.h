@@ -169,12 +169,13 @@ struct KvTensorArgs {
   const __half* src;
   uint8_t* q;
   __half* scale;
+  __half* zero;  // asymmetric mode only
 };
 
 int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t H,
                         int64_t S, int D, int64_t stride_b, int64_t stride_h,
                         int64_t stride_s, const int8_t* signs, int64_t signs_stride_h,
-                        float clip_ratio, int64_t S_cache, int64_t pos0,
+                        int mode, float clip_ratio, int64_t S_cache, int64_t pos0,
                         hipStream_t stream);
 
 }  // namespace quarot

@@ -87,8 +87,14 @@ __device__ __forceinline__ void lds_copy16(const uint8_t* g, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ void wait_vmcnt_6() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
 
 template <int WAVES_M_, int WAVES_N_, int WM_, int WN_, int BK_>
 struct GemmCfg {
@@ -149,12 +155,13 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   // 8 rb + l / 8 and LDS slot l % 8 of it; it fetches the global chunk
   // that the swizzle puts in that slot.  Rows past the matrix edge re-read
   // the last row (their results are never stored).
-  static_assert(C::WAVES_M * C::WAVES_N == 8 && CPR == 8 && CH == 6,
-                "copy mapping assumes 8 waves, 128-byte rows, 6 copies per lane");
+  constexpr int NW = C::WAVES_M * C::WAVES_N;
+  static_assert(CPR == 8 && C::ROWS % (8 * NW) == 0 && CH == C::ROWS / (8 * NW),
+                "copy mapping assumes 128-byte rows and whole 8-row blocks per wave");
   const uint8_t* src[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int rb = 8 * i + wave;
+    const int rb = NW * i + wave;
     const int r = 8 * rb + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * c
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   {                                                                                        \
     const int64_t kb0_ = int64_t(min((t), kfull - 1)) * BKB;                               \
     _Pragma("unroll") for (int i = 0; i < CH; ++i)                                         \
-        lds_copy16(src[i] + kb0_, lds0 + uint32_t((st) * C::STAGE + (8 * i + wave) * 1024)); \
+        lds_copy16(src[i] + kb0_, lds0 + uint32_t((st) * C::STAGE + (NW * i + wave) * 1024)); \
   }
 
   v16i acc[FM][FN];
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   //        whose reads all finished before the previous barrier); step
   //   kp1: step (reads tile kt's last K-pair); wait until tile kt+1 has
   //        landed (its copies were issued one tile earlier; only tile kt+2's
-  //        six may still be in flight); barrier
+  //        CH may still be in flight); barrier
   //   kp2, kp3: steps whose reads are tile kt+1's first two K-pairs
   // Copies past the last full tile repeat it into a stage nobody reads
   // again, and the reads that run past the end are harmless, so every
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   if (kfull > 0) {
     QR_COPY(0, 0);
     QR_COPY(1, 1);
-    wait_vmcnt_6();  // tile 0 landed
+    wait_vmcnt<CH>();  // tile 0 landed
     __syncthreads();
     QR_READ(0, 0, 0);
     QR_READ(1, 0, 1);
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
       QR_WIDEN(0);
       QR_MFMA(1);
       QR_INTERLEAVE();
-      wait_vmcnt_6();  // tile kt+1 landed
+      wait_vmcnt<CH>();  // tile kt+1 landed
       __syncthreads();
       // kp2: read tile kt+1 kp0 into set 0, widen kp3 (set 1), MFMAs kp2 (set 0)
       QR_READ(0, st1, 0);
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
       QR_INTERLEAVE();
       st = st1;
     }
-    wait_vmcnt_0();  // the trailing repeat copies, before any stage is rewritten
+    wait_vmcnt<0>();  // the trailing repeat copies, before any stage is rewritten
   }
 #undef QR_COPY
   if (has_tail) {  // the partial tile at the end of K: chunks past K read as zero

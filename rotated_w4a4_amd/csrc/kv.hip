@@ -58,7 +58,9 @@ __device__ __forceinline__ void kv_group(const KvLaunch& p, uint32_t g, uint32_t
   slot = int64_t(bh) * p.S_cache + p.pos0 + s;
 }
 
-template <int D, bool CLAMP>
+// MODE 0: symmetric (CLAMP when clip < 1); MODE 1: asymmetric with a zero
+// point (clipping is part of its range).
+template <int D, bool CLAMP, int MODE>
 __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
   constexpr int NC = D / 32;
   const KvTensorArgs t = blockIdx.y ? p.t[1] : p.t[0];
@@ -84,7 +86,11 @@ __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
       load_sign_masks<NC>(p.signs ? p.signs + head_key * p.signs_stride_h : nullptr, lane_q, mask);
       mask_head = head_key;
     }
-    quad_row<D, CLAMP>(raw, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
+    if (MODE == 0)
+      quad_row<D, CLAMP>(raw, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
+                         p.clip_ratio, active);
+    else
+      quad_row_asym<D>(raw, t.q + slot * (D / 2), t.scale + slot, t.zero + slot, mask, lane_q,
                        p.clip_ratio, active);
   }
 }
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
 int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t H,
                         int64_t S, int D, int64_t stride_b, int64_t stride_h,
                         int64_t stride_s, const int8_t* signs, int64_t signs_stride_h,
-                        float clip_ratio, int64_t S_cache, int64_t pos0,
+                        int mode, float clip_ratio, int64_t S_cache, int64_t pos0,
                         hipStream_t stream) {
   KvLaunch p{};
   for (int i = 0; i < n_tensors; ++i) p.t[i] = t[i];
@@ -115,14 +121,20 @@ int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t
   const int64_t cap = int64_t(1) << 24;  // grid limit; beyond it blocks loop
   if (blocks > cap) blocks = cap;
   const dim3 grid{unsigned(blocks), unsigned(n_tensors)}, block{unsigned(kBlock)};
-#define QR_KV(DD, CL) hipLaunchKernelGGL((kv_had_quant_kernel<DD, CL>), grid, block, 0, stream, p)
+#define QR_KV(DD, CL, MD) \
+  hipLaunchKernelGGL((kv_had_quant_kernel<DD, CL, MD>), grid, block, 0, stream, p)
+#define QR_KV_D(DD)                          \
+  if (mode == 1) QR_KV(DD, false, 1);        \
+  else if (clamp) QR_KV(DD, true, 0);        \
+  else QR_KV(DD, false, 0)
   const bool clamp = clip_ratio != 1.0f;
   switch (D) {
-    case 32: if (clamp) QR_KV(32, true); else QR_KV(32, false); break;
-    case 64: if (clamp) QR_KV(64, true); else QR_KV(64, false); break;
-    case 128: if (clamp) QR_KV(128, true); else QR_KV(128, false); break;
-    default: if (clamp) QR_KV(256, true); else QR_KV(256, false); break;
+    case 32: QR_KV_D(32); break;
+    case 64: QR_KV_D(64); break;
+    case 128: QR_KV_D(128); break;
+    default: QR_KV_D(256); break;
   }
+#undef QR_KV_D
 #undef QR_KV
   return check_launch("kv_had_quant");
 }

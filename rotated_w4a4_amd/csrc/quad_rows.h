@@ -68,16 +68,24 @@ __device__ __forceinline__ void quad_load(const __half* __restrict__ src, int q,
   for (int j = 0; j < D / 32; ++j) raw[j] = *reinterpret_cast<const uint4*>(src + 8 * (q + 4 * j));
 }
 
-// Process one row held by a quad, its raw chunks already loaded.  qrow: code
-// row (D/2 bytes); scale: where the fp16 scale goes; xrot: optional fp32 row.
-template <int D, bool CLAMP>
-__device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __restrict__ qrow,
-                                         __half* __restrict__ scale, float* __restrict__ xrot,
-                                         const uint4 (&mask)[D / 32], int q, float clip_ratio,
-                                         bool active) {
+// 1 / sqrt(D) for the supported head dimensions.
+template <int D>
+__device__ __forceinline__ constexpr float quad_norm() {
+  return 1.0f / (D == 32 ? 5.656854249492380f
+                 : D == 64 ? 8.0f
+                 : D == 128 ? 11.313708498984761f
+                            : 16.0f);
+}
+
+// The unnormalised transform of one row held by a quad: sign flip, then the
+// Sylvester butterflies (register bits, then the two lane bits by DPP).
+// x~ = v / sqrt(D).  An inactive quad transforms zeros.
+template <int D>
+__device__ __forceinline__ void quad_transform(const uint4 (&raw)[D / 32],
+                                               const uint4 (&mask)[D / 32], int q, bool active,
+                                               float (&v)[D / 4]) {
   constexpr int NC = D / 32;  // chunks per lane
   constexpr int E = 8 * NC;   // elements per lane
-  float v[E];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     uint4 r = raw[j];
@@ -108,11 +116,21 @@ __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __
   for (int r = 0; r < E; ++r) v[r] = quad_butterfly<0>(v[r], s0);
 #pragma unroll
   for (int r = 0; r < E; ++r) v[r] = quad_butterfly<1>(v[r], s1);
+}
 
-  constexpr float kNorm = 1.0f / (D == 32 ? 5.656854249492380f
-                                  : D == 64 ? 8.0f
-                                  : D == 128 ? 11.313708498984761f
-                                             : 16.0f);
+// Rotate+quant (symmetric) of one row held by a quad, its raw chunks already
+// loaded.  qrow: code row (D/2 bytes); scale: where the fp16 scale goes;
+// xrot: optional fp32 row.
+template <int D, bool CLAMP>
+__device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __restrict__ qrow,
+                                         __half* __restrict__ scale, float* __restrict__ xrot,
+                                         const uint4 (&mask)[D / 32], int q, float clip_ratio,
+                                         bool active) {
+  constexpr int NC = D / 32;
+  constexpr int E = 8 * NC;
+  constexpr float kNorm = quad_norm<D>();
+  float v[E];
+  quad_transform<D>(raw, mask, q, active, v);
   // the transform is unnormalised: max|x~| = max|v| / sqrt(D)
   float amax = 0.0f;
 #pragma unroll
@@ -144,6 +162,70 @@ __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __
       dst[1] = make_float4(v[8 * j + 4] * kNorm, v[8 * j + 5] * kNorm, v[8 * j + 6] * kNorm,
                            v[8 * j + 7] * kNorm);
     }
+  }
+}
+
+template <int LB>
+__device__ __forceinline__ float quad_min(float v) {
+  constexpr int ctrl = (LB == 0) ? 0xB1 : 0x4E;
+  const float p = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+  return fminf(v, p);
+}
+
+// Rotate+quant (asymmetric, one zero point per group) of one row held by a
+// quad.  "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs"
+// (paper-graph-ui summary), section 3.4 Stage 2c: the range is the clipped
+// min and max of the group, S = fp16(max(range, 1e-5) / 15), the zero point
+// z = rint(-alpha_min / S) kept within +-1024 (stored as fp16, exact), and
+// the uint4 code q = clamp(rint(x / S) + z, 0, 15); element 2k in the low
+// nibble of byte k.
+template <int D>
+__device__ __forceinline__ void quad_row_asym(const uint4 (&raw)[D / 32],
+                                              uint8_t* __restrict__ qrow,
+                                              __half* __restrict__ scale,
+                                              __half* __restrict__ zero,
+                                              const uint4 (&mask)[D / 32], int q,
+                                              float clip_ratio, bool active) {
+  constexpr int NC = D / 32;
+  constexpr int E = 8 * NC;
+  constexpr float kNorm = quad_norm<D>();
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: integers in the low mantissa bits
+  float v[E];
+  quad_transform<D>(raw, mask, q, active, v);
+  float vmin = v[0], vmax = v[0];
+#pragma unroll
+  for (int r = 1; r < E; ++r) {
+    vmin = fminf(vmin, v[r]);
+    vmax = fmaxf(vmax, v[r]);
+  }
+  vmin = quad_min<1>(quad_min<0>(vmin));
+  vmax = quad_max<1>(quad_max<0>(vmax));
+  // x~ = v / sqrt(D); scaling by a positive constant keeps the extremes
+  const float amin = clip_ratio * (vmin * kNorm);
+  const float amax = clip_ratio * (vmax * kNorm);
+  const float range = fmaxf(amax - amin, 1e-5f);
+  const __half s16 = __float2half_rn(range / 15.0f);
+  const float sf = __half2float(s16);
+  const float z = fminf(fmaxf(__builtin_rintf(-amin / sf), -1024.0f), 1024.0f);
+  if (!active) return;
+  const float kq = (1.0f / sf) * kNorm;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // rint(x / S) + M, then + z (both integers, exact), clamped to [M, M + 15]
+      const float t = fmaf(v[8 * j + i], kq, kMagic) + z;
+      t8[i] = fminf(fmaxf(t, kMagic), kMagic + 15.0f);
+    }
+    const uint32_t ev = gather_byte0(t8[0], t8[2], t8[4], t8[6]);
+    const uint32_t od = gather_byte0(t8[1], t8[3], t8[5], t8[7]);
+    *reinterpret_cast<uint32_t*>(qrow + 4 * (q + 4 * j)) = (od << 4) | ev;
+  }
+  if (q == 0) {
+    *scale = s16;
+    *zero = __float2half_rn(z);
   }
 }
 

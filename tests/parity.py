@@ -79,3 +79,39 @@ def check_y_frobenius(gpu16: np.ndarray, ref16: np.ndarray, tol: float = Y_REL) 
     e = np.linalg.norm(g - r) / np.linalg.norm(r)
     assert e <= tol, f"end-to-end Frobenius relative error {e:.3e} > {tol:.0e}"
     return float(e)
+
+
+def check_asym(codes_gpu: np.ndarray, scales_gpu16: np.ndarray, zeros_gpu16: np.ndarray,
+               x_rot: np.ndarray, ref: dict, clip_ratio: float,
+               group_frac: float = 1e-3, code_frac: float = CODE_FRAC) -> tuple:
+    """Asymmetric group quantiser: (scale, zero) pairs and uint4 codes.
+
+    Scales within 1 fp16 ulp of the oracle's and zero points within 1 of it,
+    with at most `group_frac` of the groups differing at all (fp32 rounding
+    of x~ near a decision boundary); the codes are then checked against the
+    oracle's decision taken with the kernel's own (scale, zero), the same
+    +-1 on at most `code_frac` rule as the symmetric codes.
+    """
+    import oracle  # test infrastructure
+
+    s_g = np.asarray(scales_gpu16, dtype=np.float16).reshape(-1)
+    z_g = np.asarray(zeros_gpu16, dtype=np.float16).reshape(-1).astype(np.float64)
+    assert np.all(z_g == np.rint(z_g)), "zero points must be integers"
+    z_g = z_g.astype(np.int64)
+    s_r = np.asarray(ref["scales"], dtype=np.float16).reshape(-1)
+    z_r = np.asarray(ref["zeros"]).reshape(-1).astype(np.int64)
+    du = np.abs(s_g.view(np.uint16).astype(np.int64) - s_r.view(np.uint16).astype(np.int64))
+    dz = np.abs(z_g - z_r)
+    assert du.max() <= 1, f"scales differ by {du.max()} fp16 ulps"
+    assert dz.max() <= 1, f"zero points differ by {dz.max()}"
+    differ = float(((du > 0) | (dz > 0)).mean())
+    assert differ <= group_frac, f"{differ:.2e} of the groups have other (scale, zero)"
+    d = x_rot.shape[-1]
+    want = oracle.asym_codes(np.asarray(x_rot).reshape(-1, d), s_g, z_g)
+    got = np.asarray(codes_gpu).reshape(-1, d).astype(np.int64)
+    assert got.min() >= 0 and got.max() <= 15
+    diff = np.abs(got - want.astype(np.int64))
+    assert diff.max() <= 1, f"codes differ by up to {diff.max()}"
+    f = float((diff > 0).mean())
+    assert f <= code_frac, f"{f:.2e} of the codes differ (> {code_frac:.0e})"
+    return differ, f

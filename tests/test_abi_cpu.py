@@ -130,12 +130,13 @@ def test_gemm_empty_is_noop(lib):
 
 def _kv(lib, **kw):
     a = dict(k=FAKE, v=FAKE, B=2, H=2, S=4, D=128, sb=1024, sh=512, ss=128, signs=None,
-             ssh=0, mode=0, clip=1.0, kq=FAKE, ks=FAKE, vq=FAKE, vs=FAKE, S_cache=8, pos0=0)
+             ssh=0, mode=0, clip=1.0, kq=FAKE, ks=FAKE, kz=None, vq=FAKE, vs=FAKE, vz=None,
+             S_cache=8, pos0=0)
     a.update(kw)
     return lib.quarot_kv_had_quant(a["k"], a["v"], a["B"], a["H"], a["S"], a["D"], a["sb"],
                                    a["sh"], a["ss"], a["signs"], a["ssh"], a["mode"], a["clip"],
-                                   a["kq"], a["ks"], None, a["vq"], a["vs"], None, a["S_cache"],
-                                   a["pos0"], None)
+                                   a["kq"], a["ks"], a["kz"], a["vq"], a["vs"], a["vz"],
+                                   a["S_cache"], a["pos0"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -143,7 +144,9 @@ def _kv(lib, **kw):
     (dict(D=96), UNSUPPORTED),
     (dict(D=512), UNSUPPORTED),
     (dict(mode=2), INVALID),
-    (dict(mode=1), UNSUPPORTED),
+    (dict(mode=1), INVALID),  # mode 1 needs the zero-point buffers
+    (dict(mode=1, kz=FAKE), INVALID),
+    (dict(mode=1, kz=FAKE, vz=FAKE + 1), MISALIGNED),
     (dict(clip=0.0), INVALID),
     (dict(pos0=5), INVALID),
     (dict(pos0=-1), INVALID),

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import (check_codes, check_rot, check_scales, check_y_elementwise,
+from parity import (check_asym, check_codes, check_rot, check_scales, check_y_elementwise,
                     check_y_frobenius)
 
 torch = pytest.importorskip("torch")
@@ -373,3 +373,76 @@ def test_gemm_strided_outputs():
     assert np.all(ah[:, N:] == -123)
     assert np.all(yh[:, N:] == np.float16(7.0))
     check_y_elementwise(yh[:, :N], y_ref)
+
+
+# ---------------------------------------------------------------------------
+# Asymmetric KV mode (zero point, uint4 codes)
+# ---------------------------------------------------------------------------
+def gpu_kv_asym(k16, v16, signs, clip, S_cache=None, pos0=0, signs_stride_h=0, k_t=None, v_t=None):
+    B, H, S, D = k16.shape if k16 is not None else v16.shape
+    S_cache = S if S_cache is None else S_cache
+    out = {}
+    bufs = []
+    for nm in ("k", "v"):
+        q = torch.full((B, H, S_cache, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+        sc = torch.full((B, H, S_cache), -3.0, dtype=torch.float16, device="cuda")
+        z = torch.full((B, H, S_cache), -5.0, dtype=torch.float16, device="cuda")
+        bufs.append((q, sc, z))
+    kt = k_t if k_t is not None else (dev(k16) if k16 is not None else None)
+    vt = v_t if v_t is not None else (dev(v16) if v16 is not None else None)
+    qr.kv_had_quant(kt, vt, dev(signs), bufs[0][0], bufs[0][1], bufs[1][0], bufs[1][1],
+                    pos0=pos0, signs_stride_h=signs_stride_h, clip_ratio=clip, mode=1,
+                    k_zero=bufs[0][2], v_zero=bufs[1][2])
+    for nm, (q, sc, z) in zip(("k", "v"), bufs):
+        out[nm] = (host(q), host(sc), host(z))
+    return out
+
+
+def test_kv_asym_workload():
+    cfg = workloads.KV_CONFIG
+    inp = workloads.make_kv_inputs(cfg, batch=2)
+    k16, v16, signs = inp["k"], inp["v"], inp["signs"]
+    B, H, S, D = k16.shape
+    say(f"kv asym {cfg.name}: K/V {k16.shape} clip 0.95")
+    out = gpu_kv_asym(k16, v16, signs, 0.95)
+    for t16, nm in ((k16, "k"), (v16, "v")):
+        q_h, s_h, z_h = out[nm]
+        ref = oracle.kv_had_quant_asym(t16, signs, 0.95)
+        g, f = check_asym(oracle.unpack_uint4(q_h.reshape(-1, D // 2)), s_h, z_h,
+                          ref["x_rot"], ref, 0.95)
+        say(f"  {nm}: {B * H * S} groups, (scale, zero) differ on {g:.2e}, codes {f:.2e}")
+
+
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+@pytest.mark.parametrize("clip", [1.0, 0.95])
+def test_kv_asym_positions_heads_and_degenerate_groups(D, clip):
+    rng = np.random.default_rng(40 + D)
+    B, H, S, S_cache, pos0 = 2, 3, 21, 40, 11
+    k_bshd = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    k_bshd[:, :, 1, :] += 4.0                       # a head with a large offset
+    k_bshd = k_bshd.astype(np.float16)
+    k_bshd[0, 2, 0, :] = 0                          # an all-zero group
+    k_bshd[1, 3, 2, :] = np.float16(1.5)            # a constant group
+    v_bshd = (np.abs(rng.standard_normal((B, S, H, D))) + 0.25).astype(np.float16)
+    signs = (1 - 2 * rng.integers(0, 2, (H, D))).astype(np.int8)
+    say(f"kv asym D={D} clip={clip} pos0={pos0}")
+    k_t = dev(k_bshd).permute(0, 2, 1, 3)
+    v_t = dev(v_bshd).permute(0, 2, 1, 3)
+    out = gpu_kv_asym(k_bshd.transpose(0, 2, 1, 3), v_bshd.transpose(0, 2, 1, 3), signs, clip,
+                      S_cache=S_cache, pos0=pos0, signs_stride_h=D, k_t=k_t, v_t=v_t)
+    for src, nm in ((k_bshd, "k"), (v_bshd, "v")):
+        q_h, s_h, z_h = out[nm]
+        for h in range(H):
+            rows = src[:, :, h, :].reshape(-1, D)
+            x_rot = oracle.rotate_rows(rows, signs[h], 1)
+            codes, sc, zz = oracle.quantize_rows_asym(x_rot, clip)
+            ref = {"scales": sc, "zeros": zz}
+            check_asym(oracle.unpack_uint4(q_h[:, h, pos0:pos0 + S].reshape(-1, D // 2)),
+                       s_h[:, h, pos0:pos0 + S], z_h[:, h, pos0:pos0 + S], x_rot, ref, clip,
+                       group_frac=0.05, code_frac=1e-2)
+        assert np.all(q_h[:, :, :pos0] == 0x5A) and np.all(q_h[:, :, pos0 + S:] == 0x5A)
+        assert np.all(s_h[:, :, :pos0] == -3.0) and np.all(z_h[:, :, pos0 + S:] == -5.0)
+    # the zero and constant groups: scale from the 1e-5 floor, codes = the zero point
+    q_h, s_h, z_h = out["k"]
+    zg = oracle.unpack_uint4(q_h[0, 0, pos0 + 2])
+    assert np.all(zg == int(z_h[0, 0, pos0 + 2])) and float(z_h[0, 0, pos0 + 2]) == 0.0
