@@ -58,6 +58,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama7b_proj", choices=sorted(workloads.ACT_CONFIGS))
     p.add_argument("--kv", action="store_true", help="benchmark the K/V cache write instead")
+    p.add_argument("--kv-asym", action="store_true",
+                   help="with --kv: the asymmetric mode (zero point, clip 0.95)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for 1 GiB)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -276,7 +278,8 @@ def bench_kv(args, torch, qr) -> dict:
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     signs = dev(inp["signs"])
     k0, v0 = dev(inp["k"]), dev(inp["v"])
-    per_set = 2 * (B * H * S * D * 2 + B * H * S * D // 2 + B * H * S * 2)
+    asym = args.kv_asym
+    per_set = 2 * (B * H * S * D * 2 + B * H * S * D // 2 + B * H * S * 2 * (2 if asym else 1))
     nsets = args.sets or max(2, -(-CACHE_DEFEAT_BYTES // per_set))
     sets = []
     for i in range(nsets):
@@ -286,12 +289,19 @@ def bench_kv(args, torch, qr) -> dict:
             "vq": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda"),
             "ks": torch.empty((B, H, S), dtype=torch.float16, device="cuda"),
             "vs": torch.empty((B, H, S), dtype=torch.float16, device="cuda"),
+            "kz": torch.empty((B, H, S), dtype=torch.float16, device="cuda") if asym else None,
+            "vz": torch.empty((B, H, S), dtype=torch.float16, device="cuda") if asym else None,
         })
     stream = torch.cuda.current_stream()
 
     def step(i):
         s = sets[i % nsets]
-        qr.kv_had_quant(s["k"], s["v"], signs, s["kq"], s["ks"], s["vq"], s["vs"], stream=stream)
+        if asym:
+            qr.kv_had_quant(s["k"], s["v"], signs, s["kq"], s["ks"], s["vq"], s["vs"],
+                            clip_ratio=0.95, mode=1, k_zero=s["kz"], v_zero=s["vz"], stream=stream)
+        else:
+            qr.kv_had_quant(s["k"], s["v"], signs, s["kq"], s["ks"], s["vq"], s["vs"],
+                            stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -306,16 +316,21 @@ def bench_kv(args, torch, qr) -> dict:
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"kv {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
     return {
-        "metric": "KV rotate+quant GB/s (% HBM peak)", "value": round(gbs, 2), "unit": "GB/s",
+        "metric": "KV rotate+quant GB/s (% HBM peak)" + (" [asymmetric, zero point]" if asym else ""),
+        "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp32 rotate / int4 codes",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: K and V fp16 [{B} x {H} x {S} x {D}], "
-                               f"H_{D} with random signs", "buffer_sets": nsets},
+                               f"H_{D} with random signs"
+                               + (", asymmetric uint4 + fp16 scale and zero point, clip 0.95"
+                                  if asym else ", symmetric int4 + fp16 scale"),
+                   "buffer_sets": nsets},
         "roofline": {"kernel": "kv_had_quant", "bound": "hbm", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name, "kv_had_quant"),
+                     "traffic": measured_traffic(cfg.name + ("_asym" if asym else ""),
+                                                 "kv_had_quant"),
                      "algorithmic_bytes": nbytes},
     }
 

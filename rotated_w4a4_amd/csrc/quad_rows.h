@@ -21,14 +21,36 @@
 
 namespace quarot {
 
-// One DPP butterfly across lanes: the partner is lane ^ (1 << LB) inside the
-// quad.  The low lane keeps a + b, the high lane keeps a - b.
-template <int LB>
-__device__ __forceinline__ float quad_butterfly(float v, float sgn) {
-  constexpr int ctrl = (LB == 0) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  const float p = __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
-  return fmaf(v, sgn, p);
+// The two quad butterfly stages (partner lane ^ 1, then ^ 2) on E registers,
+// each as v + partner * c in one v_fmac_f32 with DPP, c = +1 on the low lane
+// and -1 on the high lane.  A high lane ends with b - a instead of a - b, so
+// afterwards every value of lane q carries the sign (-1)^(q0 + q1), which the
+// quantisers fold into their scale.  DPP needs two wait states after a VALU
+// write of its source: stage 1 reads only what stage 0's blocks
+// wrote at least E - 4 instructions earlier, and the last block closes with
+// s_nop 1.  (Every stage-0 block opens with s_nop 1: the compiler may
+// schedule the producer of any register right before it.)
+template <int E>
+__device__ __forceinline__ void quad_butterflies(float (&v)[E], float c0, float c1) {
+  static_assert(E % 4 == 0 && E >= 8, "blocks of four registers");
+#define QR_QUAD_DPP(LEAD, CTRL, C, TRAIL)                                                    \
+  asm volatile(LEAD                                                                          \
+               "v_fmac_f32_dpp %0, %0, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %1, %1, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %2, %2, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %3, %3, %4 " CTRL " row_mask:0xf bank_mask:0xf" TRAIL      \
+               : "+v"(v[r]), "+v"(v[r + 1]), "+v"(v[r + 2]), "+v"(v[r + 3])              \
+               : "v"(C))
+#pragma unroll
+  for (int r = 0; r < E; r += 4) {
+    QR_QUAD_DPP("s_nop 1\n", "quad_perm:[1,0,3,2]", c0, "");
+  }
+#pragma unroll
+  for (int r = 0; r < E; r += 4) {
+    if (r + 4 < E) QR_QUAD_DPP("", "quad_perm:[2,3,0,1]", c1, "");
+    else QR_QUAD_DPP("", "quad_perm:[2,3,0,1]", c1, "\ns_nop 1");
+  }
+#undef QR_QUAD_DPP
 }
 
 template <int LB>
@@ -79,7 +101,7 @@ __device__ __forceinline__ constexpr float quad_norm() {
 
 // The unnormalised transform of one row held by a quad: sign flip, then the
 // Sylvester butterflies (register bits, then the two lane bits by DPP).
-// x~ = v / sqrt(D).  An inactive quad transforms zeros.
+// x~ = quad_sigma(q) * v / sqrt(D).  An inactive quad transforms zeros.
 template <int D>
 __device__ __forceinline__ void quad_transform(const uint4 (&raw)[D / 32],
                                                const uint4 (&mask)[D / 32], int q, bool active,
@@ -110,12 +132,12 @@ __device__ __forceinline__ void quad_transform(const uint4 (&raw)[D / 32],
   }
   // lane-bit butterflies (element bits 3 and 4); every lane of the wave takes
   // part so the DPP sources are always defined
-  const float s0 = (q & 1) ? -1.0f : 1.0f;
-  const float s1 = (q & 2) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int r = 0; r < E; ++r) v[r] = quad_butterfly<0>(v[r], s0);
-#pragma unroll
-  for (int r = 0; r < E; ++r) v[r] = quad_butterfly<1>(v[r], s1);
+  quad_butterflies<E>(v, (q & 1) ? -1.0f : 1.0f, (q & 2) ? -1.0f : 1.0f);
+}
+
+// Sign that quad_transform leaves on lane q's values.
+__device__ __forceinline__ float quad_sigma(int q) {
+  return (((q ^ (q >> 1)) & 1) != 0) ? -1.0f : 1.0f;
 }
 
 // Rotate+quant (symmetric) of one row held by a quad, its raw chunks already
@@ -139,7 +161,8 @@ __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __
   amax = quad_max<1>(amax);
   const __half s16 = row_scale_fp16(amax * kNorm, clip_ratio);
   if (!active) return;
-  const float kq = inv_scale(s16) * kNorm;
+  const float sigma = quad_sigma(q);
+  const float kq = inv_scale(s16) * kNorm * sigma;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     float t8[8];
@@ -154,13 +177,14 @@ __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __
   }
   if (q == 0) *scale = s16;
   if (xrot) {
+    const float xn = kNorm * sigma;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       float4* dst = reinterpret_cast<float4*>(xrot + 8 * (q + 4 * j));
-      dst[0] = make_float4(v[8 * j + 0] * kNorm, v[8 * j + 1] * kNorm, v[8 * j + 2] * kNorm,
-                           v[8 * j + 3] * kNorm);
-      dst[1] = make_float4(v[8 * j + 4] * kNorm, v[8 * j + 5] * kNorm, v[8 * j + 6] * kNorm,
-                           v[8 * j + 7] * kNorm);
+      dst[0] = make_float4(v[8 * j + 0] * xn, v[8 * j + 1] * xn, v[8 * j + 2] * xn,
+                           v[8 * j + 3] * xn);
+      dst[1] = make_float4(v[8 * j + 4] * xn, v[8 * j + 5] * xn, v[8 * j + 6] * xn,
+                           v[8 * j + 7] * xn);
     }
   }
 }
@@ -199,9 +223,17 @@ __device__ __forceinline__ void quad_row_asym(const uint4 (&raw)[D / 32],
     vmin = fminf(vmin, v[r]);
     vmax = fmaxf(vmax, v[r]);
   }
+  // the lane's values are sigma * x~ * sqrt(D): a negative sigma swaps and
+  // negates the extremes
+  const float sigma = quad_sigma(q);
+  if (sigma < 0.0f) {
+    const float t = vmin;
+    vmin = -vmax;
+    vmax = -t;
+  }
   vmin = quad_min<1>(quad_min<0>(vmin));
   vmax = quad_max<1>(quad_max<0>(vmax));
-  // x~ = v / sqrt(D); scaling by a positive constant keeps the extremes
+  // scaling by the positive 1 / sqrt(D) keeps the extremes
   const float amin = clip_ratio * (vmin * kNorm);
   const float amax = clip_ratio * (vmax * kNorm);
   const float range = fmaxf(amax - amin, 1e-5f);
@@ -209,7 +241,7 @@ __device__ __forceinline__ void quad_row_asym(const uint4 (&raw)[D / 32],
   const float sf = __half2float(s16);
   const float z = fminf(fmaxf(__builtin_rintf(-amin / sf), -1024.0f), 1024.0f);
   if (!active) return;
-  const float kq = (1.0f / sf) * kNorm;
+  const float kq = (1.0f / sf) * kNorm * sigma;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     float t8[8];
