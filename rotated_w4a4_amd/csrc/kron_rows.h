@@ -183,9 +183,11 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int a = 128 * wave + 16 * t + n;
+      // (the lanes past m are masked at use: masking here would make the
+      // prefetch wait for its own data)
       const uint2 lo = *reinterpret_cast<const uint2*>(src + a * M + off_lo);
       const uint2 hi = *reinterpret_cast<const uint2*>(src + a * M + off_hi);
-      raw[t] = make_uint4(lo.x & keep_lo, lo.y & keep_lo, hi.x & keep_hi, hi.y & keep_hi);
+      raw[t] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
 
@@ -198,10 +200,10 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint4 r = raw[t];
-      r.x ^= mask[t].x;
-      r.y ^= mask[t].y;
-      r.z ^= mask[t].z;
-      r.w ^= mask[t].w;
+      r.x = (r.x & keep_lo) ^ mask[t].x;
+      r.y = (r.y & keep_lo) ^ mask[t].y;
+      r.z = (r.z & keep_hi) ^ mask[t].z;
+      r.w = (r.w & keep_hi) ^ mask[t].w;
       const half8_t bop = __builtin_bit_cast(half8_t, r);
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       const float4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
