@@ -102,32 +102,43 @@ def time_kernel(torch, stream, launch, count: int, lead: int = 10) -> float:
     return e0.elapsed_time(e1) / count
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources and the public header."""
-    import hashlib
+# The source file each timed kernel is compiled from.
+KERNEL_FILES = {"had_quant": "had_quant.hip", "w4a4_gemm": "gemm.hip",
+                "kv_had_quant": "kv.hip", "kv_decode": "decode.hip"}
 
+
+def source_digest(kernel: str) -> str:
+    """sha256 over a kernel's source file and the local headers it includes,
+    transitively (the public header holds declarations only)."""
+    import hashlib
+    import re
+
+    seen, todo = [], [KERNEL_FILES[kernel]]
+    while todo:
+        name = todo.pop()
+        path = os.path.join(CSRC, name)
+        if name in seen or not os.path.exists(path):
+            continue
+        seen.append(name)
+        with open(path) as f:
+            todo += re.findall(r'#include "([^"]+)"', f.read())
     h = hashlib.sha256()
-    files = sorted(os.listdir(CSRC))
-    for name in files:
+    for name in sorted(seen):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "quarot.h"), "rb") as f:
-        h.update(f.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed counter summary, or None when
-    the kernels changed since the counters were taken."""
+    the kernel's sources changed since its counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_digest():
-        return None
     k = t.get("kernels", {}).get(workload, {}).get(kernel)
-    if not k:
+    if not k or k.get("source_sha256") != source_digest(kernel):
         return None
     return int(k["fetch_bytes"] + k["write_bytes"])
 
@@ -359,7 +370,8 @@ def counter_means(path: str, counter: str) -> dict:
     return {k: float(np.median(v)) for k, v in acc.items()}
 
 
-KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant": "kv_had_quant"}
+KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant": "kv_had_quant",
+               "decode_split": "kv_decode"}
 
 
 def summarize_counters(args) -> dict:
@@ -375,8 +387,7 @@ def summarize_counters(args) -> dict:
     copy_w = max(v for k, v in cal_w.items() if "copy" in k.lower())
     kf = COPY_BYTES / (copy_f * 1024.0)
     kw = COPY_BYTES / (copy_w * 1024.0)
-    out = {"source_sha256": source_digest(),
-           "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
+    out = {"copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": copy_f, "write_kib": copy_w,
                                 "fetch_scale": kf, "write_scale": kw},
            "kernels": {}}
     rest = args.traffic_from[2:]
@@ -390,7 +401,8 @@ def summarize_counters(args) -> dict:
                         not (k == "had_quant" and "kv_had_quant" in kname)), None)
             if key is None or kname not in w:
                 continue
-            ent[key] = {"kernel": kname.split("(")[0], "fetch_kib": fv, "write_kib": w[kname],
+            ent[key] = {"kernel": kname.split("(")[0], "source_sha256": source_digest(key),
+                        "fetch_kib": fv, "write_kib": w[kname],
                         "fetch_bytes": fv * 1024.0 * kf, "write_bytes": w[kname] * 1024.0 * kw}
         out["kernels"][name] = ent
     return out
