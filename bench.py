@@ -19,7 +19,10 @@ Prints ONE JSON line:
   roofline         the dominant kernel (the GEMM) against INT8 MFMA peak
   roofline_rotate_quant  rotate+quant against HBM peak
   cpu_baseline     the CPU oracle timed on this host on the same workload
-Extra workloads for profiling: --workload NAME, --kv (the K/V cache write).
+Extra workloads for profiling: --workload NAME, --kv (the K/V cache write),
+--decode (one decode step: append the new token's K/V, then attention of every
+query head over the int4 cache, with the head-wise query rotation and the
+cross-head transform).
 """
 
 from __future__ import annotations
@@ -59,7 +62,13 @@ def parse_args():
     p.add_argument("--workload", default="llama7b_proj", choices=sorted(workloads.ACT_CONFIGS))
     p.add_argument("--kv", action="store_true", help="benchmark the K/V cache write instead")
     p.add_argument("--kv-asym", action="store_true",
-                   help="with --kv: the asymmetric mode (zero point, clip 0.95)")
+                   help="with --kv or --decode: the asymmetric cache (zero point, clip 0.95)")
+    p.add_argument("--decode", action="store_true",
+                   help="benchmark one decode step (append + attention over the int4 cache)")
+    p.add_argument("--decode-workload", default="decode_70b_gqa",
+                   choices=sorted(workloads.DECODE_CONFIGS))
+    p.add_argument("--no-cross-head", action="store_true",
+                   help="with --decode: leave out the cross-head transform")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for 1 GiB)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -346,6 +355,145 @@ def bench_kv(args, torch, qr) -> dict:
     }
 
 
+def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows: int = 2) -> dict:
+    """The oracle, as it stands, on `rows` batch rows of the decode step (its
+    cache built by the oracle's KV quantiser, untimed)."""
+    import oracle
+    from oracle.attention import decode_attention
+
+    cfg = dcfg.kv
+    S = cfg.positions
+    quant = oracle.kv_had_quant if mode == 0 else (
+        lambda t, s: oracle.kv_had_quant_asym(t, s, 0.95))
+    kc, vc = quant(inp["k"][:rows], inp["signs"]), quant(inp["v"][:rows], inp["signs"])
+    cache = {"k_q": kc["packed"], "k_scale": kc["scales"], "v_q": vc["packed"],
+             "v_scale": vc["scales"]}
+    if mode == 1:
+        cache["k_zero"] = kc["zeros"].astype(np.float16)
+        cache["v_zero"] = vc["zeros"].astype(np.float16)
+    t0 = time.perf_counter()
+    decode_attention(q16[:rows], inp["signs"], cache, [S] * rows, mode=mode, cross=cross)
+    sec = time.perf_counter() - t0
+    nbytes = decode_call_bytes(rows, cfg.heads, dcfg.q_heads, S, cfg.head_dim, mode)
+    return {"value": nbytes / sec / 1e9, "unit": "GB/s", "seconds": sec, "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of {cfg.batch} batch rows of the decode attention (query rotation, "
+                      f"dequantisation, float64 softmax attention{', cross-head' if cross else ''}) "
+                      f"over {S} cached positions; the oracle's cache build is not timed"}
+
+
+def decode_call_bytes(B, H, Hq, S, D, mode) -> int:
+    """Algorithmic bytes of one decode attention call: every cached code, scale
+    (and zero point) of K and V once, the queries read and the output written."""
+    per_pos = D // 2 + 2 + (2 if mode == 1 else 0)
+    return 2 * B * H * S * per_pos + 2 * B * Hq * D * 2
+
+
+def bench_decode(args, torch, qr) -> dict:
+    dcfg = workloads.DECODE_CONFIGS[args.decode_workload]
+    cfg = dcfg.kv
+    B, H, S, D, Hq = cfg.batch, cfg.heads, cfg.positions, cfg.head_dim, dcfg.q_heads
+    mode = 1 if args.kv_asym else 0
+    cross = not args.no_cross_head
+    log(f"decode workload {dcfg.name}: generating inputs")
+    inp = workloads.make_kv_inputs(cfg)
+    q16 = workloads.make_decode_query(dcfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    signs = dev(inp["signs"])
+    zero_kw = {"mode": 1, "clip_ratio": 0.95} if mode == 1 else {}
+
+    def new_cache():
+        c = {"kq": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda"),
+             "vq": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda"),
+             "ks": torch.empty((B, H, S), dtype=torch.float16, device="cuda"),
+             "vs": torch.empty((B, H, S), dtype=torch.float16, device="cuda")}
+        c["kz"] = torch.empty_like(c["ks"]) if mode == 1 else None
+        c["vz"] = torch.empty_like(c["vs"]) if mode == 1 else None
+        return c
+
+    # the cache of all S positions, written by the library's KV quantiser; the
+    # decode step re-appends position S - 1 (the new token) and attends to S
+    k_all, v_all = dev(inp["k"]), dev(inp["v"])
+    c0 = new_cache()
+    qr.kv_had_quant(k_all, v_all, signs, c0["kq"], c0["ks"], c0["vq"], c0["vs"],
+                    k_zero=c0["kz"], v_zero=c0["vz"], **zero_kw)
+    k_new = k_all[:, :, S - 1:S].contiguous()
+    v_new = v_all[:, :, S - 1:S].contiguous()
+    del k_all, v_all
+    att_bytes = decode_call_bytes(B, H, Hq, S, D, mode)
+    app_bytes = 2 * B * H * (D * 2 + D // 2 + 2 + (2 if mode == 1 else 0))
+    nsets = args.sets or max(2, -(-CACHE_DEFEAT_BYTES // att_bytes))
+    sets = []
+    for i in range(nsets):
+        c = c0 if i == 0 else {k: (v.clone() if v is not None else None) for k, v in c0.items()}
+        c["q"] = dev(q16)
+        c["out"] = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+        sets.append(c)
+    ws = torch.empty(qr.kv_decode_workspace_bytes(B, Hq, H, D, S), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def append(i):
+        c = sets[i % nsets]
+        qr.kv_had_quant(k_new, v_new, signs, c["kq"], c["ks"], c["vq"], c["vs"], pos0=S - 1,
+                        k_zero=c["kz"], v_zero=c["vz"], stream=stream, **zero_kw)
+
+    def attend(i):
+        c = sets[i % nsets]
+        qr.kv_decode_attention(c["q"], signs, c["kq"], c["ks"], c["vq"], c["vs"], S, mode=mode,
+                               k_zero=c["kz"], v_zero=c["vz"], cross_head=cross, out=c["out"],
+                               workspace=ws, stream=stream)
+
+    def step(i):
+        append(i)
+        attend(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = time_kernel(torch, stream, step, args.steps)
+    ms_att = time_kernel(torch, stream, attend, args.steps)
+    ms_app = time_kernel(torch, stream, append, args.steps)
+    step_gbs = (att_bytes + app_bytes) / (ms_step * 1e-3) / 1e9
+    att_gbs = att_bytes / (ms_att * 1e-3) / 1e9
+    log(f"decode step {ms_step * 1e3:.2f} us ({step_gbs:.0f} GB/s); attention call "
+        f"{ms_att * 1e3:.2f} us ({att_gbs:.0f} GB/s); append {ms_app * 1e3:.2f} us")
+    out = {
+        "metric": "decode step GB/s (% HBM peak): append + attention over the int4 KV cache"
+                  + (" [asymmetric, zero point]" if mode == 1 else ""),
+        "value": round(step_gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 cache, fp32-class attention (fp16 MFMA with hi/lo operand split)",
+        "data": "synthetic",
+        "config": {"workload": f"{dcfg.name}: q fp16 [{B} x {Hq} x {D}] against K and V caches "
+                               f"[{B} x {H} x {S} x {D // 2}] uint8 + fp16 scales"
+                               + (" + zero points" if mode == 1 else "")
+                               + f", head-wise query rotation H_{D} with random signs"
+                               + (f", cross-head H_{Hq}" if cross else ""),
+                   "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+                   "buffer_sets": nsets},
+        "kernels_us": {"kv_decode_attention": round(ms_att * 1e3, 3),
+                       "kv_had_quant_append": round(ms_app * 1e3, 3)},
+        "roofline": {"kernel": "kv_decode_attention (split + combine kernels)", "bound": "hbm",
+                     "achieved": round(att_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(att_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dcfg.name + ("_asym" if mode == 1 else ""),
+                                                 "kv_decode"),
+                     "algorithmic_bytes": att_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_decode(dcfg, inp, q16, mode, cross)
+    return out
+
+
 def calibrate_copy(torch) -> dict:
     """A plain device copy of known size, for scaling the HBM byte counters."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -432,7 +580,12 @@ def main() -> int:
     if args.calibrate_copy:
         out = calibrate_copy(torch)
     else:
-        out = bench_kv(args, torch, qr) if args.kv else bench_act(args, torch, qr)
+        if args.decode:
+            out = bench_decode(args, torch, qr)
+        elif args.kv:
+            out = bench_kv(args, torch, qr)
+        else:
+            out = bench_act(args, torch, qr)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -170,6 +170,77 @@ int quarot_kv_had_quant(const void* k, const void* v,
                         int64_t S_cache, int64_t pos0, void* stream);
 
 /*
+ * One decode step of attention over the INT4 cache written by
+ * quarot_kv_had_quant, with the query rotation and, optionally, the
+ * cross-head transform.
+ *
+ * Follows [S] section 3.4 Stage 1d (the new query is rotated head-wise by
+ * the same Hadamard as the cached keys, after RoPE, so q k^T is unchanged;
+ * P = softmax(q K^T / sqrt(d_h))), Stage 2c (the decode-time list: rotate
+ * the query, load the quantised keys and values of all previous positions,
+ * dequantise every group on the fly, attend) and Stage 1c (the online
+ * cross-head transform Z <- Z (H_{n_h} (x) I_{d_h}) on the concatenated
+ * attention output).
+ *
+ * For batch row b and query head j (KV head h = j / (Hq / Hkv): consecutive
+ * query heads share a KV head), with L = min(lengths[b], max_len) (max_len
+ * when lengths is NULL) and positions p < L:
+ *   q~ = H_128 diag(signs_h) q[b][j] / sqrt(128)          (fp32)
+ *   k^_p = S_p * c_p  (mode 0)  or  S_p * (u_p - z_p)  (mode 1), likewise v^_p
+ *   out[b][j] = sum_p softmax_p(sm_scale * q~ . k^_p) v^_p
+ * in fp32-class arithmetic (scores and P V on fp16 matrix cores with the
+ * fp32 operand split into fp16 high and low parts).  The output stays in the
+ * rotated basis of the values.  With cross_head != 0 the Hq outputs of each
+ * batch row are then mixed by the normalised Sylvester H_Hq over the head
+ * index: out'[b][a][d] = sum_a' H[a][a'] out[b][a'][d] / sqrt(Hq).  A row
+ * with L = 0 gives 0.
+ *
+ * Arguments:
+ *   q            fp16 [B x Hq x 128], contiguous, 16-byte aligned (post-RoPE
+ *                queries, not rotated).
+ *   signs        int8 +1/-1, KV head h uses signs + h*signs_stride_h; must be
+ *                what the cache was written with.  NULL = all +1.
+ *   mode         0 = symmetric cache, 1 = zero-point cache (k_zero, v_zero
+ *                required).
+ *   k_q, v_q     uint8 [B x Hkv x S_cache x 64], 16-byte aligned;
+ *   k_scale, v_scale, k_zero, v_zero  fp16 [B x Hkv x S_cache].
+ *   D            head dimension; 128 only.
+ *   Hq, Hkv      Hq a multiple of Hkv, Hq / Hkv <= 8.
+ *   max_len      1 <= max_len <= S_cache: positions attended at most.
+ *   lengths      optional int32 [B] device array of per-row lengths (values
+ *                above max_len are clamped to it, negative ones to 0).
+ *   sm_scale     softmax scale, finite and > 0 (1/sqrt(128) in the pages).
+ *   cross_head   0 or 1; 1 needs Hq a power of two <= 256.
+ *   out          fp16 [B x Hq x 128], 2-byte aligned; out_f32 optional fp32
+ *                copy (same layout, 4-byte aligned) for parity checks.
+ *   workspace    device scratch of at least
+ *                quarot_kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
+ *                bytes, 16-byte aligned, owned by the caller; its contents
+ *                on entry do not matter.  Calls that share a workspace must
+ *                be ordered (one stream).
+ * Errors: INVALID for bad sizes, mode, scale, missing buffers or a short
+ * workspace; UNSUPPORTED for D != 128, Hq / Hkv > 8, or cross_head with Hq
+ * not a power of two <= 256; MISALIGNED as stated.
+ */
+int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                               const int8_t* signs, int64_t signs_stride_h, int32_t mode,
+                               const uint8_t* k_q, const void* k_scale, const void* k_zero,
+                               const uint8_t* v_q, const void* v_scale, const void* v_zero,
+                               int64_t S_cache, int64_t max_len, const int32_t* lengths,
+                               float sm_scale, int32_t cross_head,
+                               void* out, float* out_f32,
+                               void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Host-only: bytes of workspace quarot_kv_decode_attention needs for these
+ * sizes (per position split: the running max, softmax sum and unnormalised
+ * output of every query head).  Returns a negative status for sizes the
+ * entry point would reject.  Makes no HIP call.
+ */
+int64_t quarot_kv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                         int64_t max_len);
+
+/*
  * Host-only: copy the built-in small Hadamard factor H_m (entries +1/-1,
  * row-major int8 [m x m], HOST memory of m*m bytes) that quarot_had_quant
  * uses for d = 2^n * m.  m = 1 gives [1]; 12 and 28 give the Paley type-I

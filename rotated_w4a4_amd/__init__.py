@@ -11,14 +11,17 @@ Calls (same names as the C entry points, without the ``quarot_`` prefix):
 * ``had_quant(x, signs, m, clip_ratio)``   -> (codes uint8 [rows, d/2], scales fp16 [rows])
 * ``w4a4_gemm(a_q, a_scale, b_q, b_scale, k)`` -> fp16 [M, N]
 * ``kv_had_quant(k, v, signs, k_cache, k_scale, v_cache, v_scale, pos0)``
+* ``kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len)``
+  -> fp16 [B, Hq, 128] (one decode step over the int4 cache)
+* ``kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len)``
 * ``hadamard_factor(m)``                  -> the built-in H_m (numpy int8)
 
 Tensors are torch tensors on the current HIP device; torch provides device
 memory and streams only.
 """
 
-from ._lib import (QuarotError, had_quant, hadamard_factor, kv_had_quant, lib,
-                   library_path, w4a4_gemm)
+from ._lib import (QuarotError, had_quant, hadamard_factor, kv_decode_attention,
+                   kv_decode_workspace_bytes, kv_had_quant, lib, library_path, w4a4_gemm)
 
-__all__ = ["QuarotError", "had_quant", "hadamard_factor", "kv_had_quant", "lib",
-           "library_path", "w4a4_gemm"]
+__all__ = ["QuarotError", "had_quant", "hadamard_factor", "kv_decode_attention",
+           "kv_decode_workspace_bytes", "kv_had_quant", "lib", "library_path", "w4a4_gemm"]

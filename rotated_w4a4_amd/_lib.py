@@ -25,6 +25,10 @@ _SIGNATURES = {
     "quarot_kv_had_quant": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                            _vp, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _i64, _i64, _vp]),
+    "quarot_kv_decode_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32,
+                                                  _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                                                  _f32, _i32, _vp, _vp, _vp, _i64, _vp]),
+    "quarot_kv_decode_workspace_bytes": (ctypes.c_int64, [_i64, _i64, _i64, _i64, _i64]),
     "quarot_hadamard_factor": (ctypes.c_int, [_i32, _vp]),
     "quarot_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "quarot_last_error": (ctypes.c_char_p, []),
@@ -219,3 +223,67 @@ def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0
     if mode == 1:
         return k_cache, k_scale, k_zero, v_cache, v_scale, v_zero
     return k_cache, k_scale, v_cache, v_scale
+
+
+def kv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_len: int) -> int:
+    """Workspace bytes kv_decode_attention needs for these sizes."""
+    n = int(lib().quarot_kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len))
+    _check("quarot_kv_decode_workspace_bytes", n if n < 0 else 0)
+    return n
+
+
+def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: int,
+                        lengths=None, mode: int = 0, k_zero=None, v_zero=None,
+                        sm_scale: Optional[float] = None, cross_head: bool = False,
+                        signs_stride_h: int = 0, out=None, out_f32=None, workspace=None,
+                        stream=None):
+    """One decode step: q fp16 [B, Hq, 128] against the int4 caches
+    [B, Hkv, S_cache, 64] (+ fp16 scales [B, Hkv, S_cache], and zero points in
+    mode 1).  Returns fp16 [B, Hq, 128] (``out``); ``out_f32`` optionally
+    receives an fp32 copy.  ``workspace`` (uint8, device) is allocated here
+    when not given."""
+    torch = _torch()
+    _need(q, torch.float16, "q", 3)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    B, Hq, D = q.shape
+    _need(k_cache, torch.uint8, "k_cache", 4)
+    _need(v_cache, torch.uint8, "v_cache", 4)
+    _need(k_scale, torch.float16, "k_scale", 3)
+    _need(v_scale, torch.float16, "v_scale", 3)
+    Hkv, S_cache = k_cache.shape[1], k_cache.shape[2]
+    for name, c, sc in (("k", k_cache, k_scale), ("v", v_cache, v_scale)):
+        if not c.is_contiguous() or not sc.is_contiguous():
+            raise ValueError(f"{name} cache buffers must be contiguous")
+        if tuple(c.shape) != (B, Hkv, S_cache, D // 2) or tuple(sc.shape) != (B, Hkv, S_cache):
+            raise ValueError(f"{name}_cache must be [B, Hkv, S_cache, D/2] with scales [B, Hkv, S_cache]")
+    if mode == 1:
+        for name, z in (("k_zero", k_zero), ("v_zero", v_zero)):
+            _need(z, torch.float16, name, 3)
+            if not z.is_contiguous() or tuple(z.shape) != (B, Hkv, S_cache):
+                raise ValueError(f"{name} must be contiguous [B, Hkv, S_cache]")
+    if signs is not None:
+        _need(signs, torch.int8, "signs")
+    if lengths is not None:
+        _need(lengths, torch.int32, "lengths", 1)
+        if lengths.shape[0] != B or not lengths.is_contiguous():
+            raise ValueError("lengths must be a contiguous int32 [B]")
+    if sm_scale is None:
+        sm_scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    _need(out, torch.float16, "out", 3)
+    if out_f32 is not None:
+        _need(out_f32, torch.float32, "out_f32", 3)
+    need = kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    st = lib().quarot_kv_decode_attention(
+        _ptr(q), B, Hq, Hkv, D, _ptr(signs), int(signs_stride_h), int(mode),
+        _ptr(k_cache), _ptr(k_scale), _ptr(k_zero) if mode == 1 else None,
+        _ptr(v_cache), _ptr(v_scale), _ptr(v_zero) if mode == 1 else None,
+        S_cache, int(max_len), _ptr(lengths), float(sm_scale), int(bool(cross_head)),
+        _ptr(out), _ptr(out_f32), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("quarot_kv_decode_attention", st)
+    return out

@@ -4,6 +4,7 @@
 #include <cstring>
 
 #include "common.h"
+#include "decode.h"
 
 namespace quarot {
 
@@ -182,6 +183,93 @@ int quarot_kv_had_quant(const void* k, const void* v,
   return launch_kv_had_quant(t, nt, B, H, S, int(D), stride_b, stride_h, stride_s, signs,
                              signs_stride_h, int(mode), clip_ratio, S_cache, pos0,
                              static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the decode entry point and its workspace query.
+int decode_shape_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_len) {
+  QR_CHECK_ARG(B >= 0, QUAROT_ERR_INVALID, "B = %lld < 0", (long long)B);
+  QR_CHECK_ARG(Hq > 0 && Hkv > 0, QUAROT_ERR_INVALID, "Hq and Hkv must be > 0");
+  QR_CHECK_ARG(Hq % Hkv == 0, QUAROT_ERR_INVALID, "Hq = %lld is not a multiple of Hkv = %lld",
+               (long long)Hq, (long long)Hkv);
+  QR_CHECK_ARG(D == 128, QUAROT_ERR_UNSUPPORTED, "D = %lld: the decode kernel needs D = 128",
+               (long long)D);
+  QR_CHECK_ARG(Hq / Hkv <= 8, QUAROT_ERR_UNSUPPORTED, "Hq / Hkv = %lld > 8",
+               (long long)(Hq / Hkv));
+  QR_CHECK_ARG(max_len >= 1 && max_len < (int64_t(1) << 30), QUAROT_ERR_INVALID,
+               "max_len = %lld out of range", (long long)max_len);
+  QR_CHECK_ARG(B * Hkv < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED, "B * Hkv too large");
+  return QUAROT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t quarot_kv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                         int64_t max_len) {
+  clear_error();
+  const int st = decode_shape_ok(B, Hq, Hkv, D, max_len);
+  if (st != QUAROT_OK) return st;
+  return decode_workspace_bytes(B, Hq, Hkv, max_len);
+}
+
+int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                               const int8_t* signs, int64_t signs_stride_h, int32_t mode,
+                               const uint8_t* k_q, const void* k_scale, const void* k_zero,
+                               const uint8_t* v_q, const void* v_scale, const void* v_zero,
+                               int64_t S_cache, int64_t max_len, const int32_t* lengths,
+                               float sm_scale, int32_t cross_head,
+                               void* out, float* out_f32,
+                               void* workspace, int64_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = decode_shape_ok(B, Hq, Hkv, D, max_len);
+  if (st != QUAROT_OK) return st;
+  QR_CHECK_ARG(mode == 0 || mode == 1, QUAROT_ERR_INVALID, "mode must be 0 or 1");
+  QR_CHECK_ARG(cross_head == 0 || cross_head == 1, QUAROT_ERR_INVALID, "cross_head must be 0 or 1");
+  QR_CHECK_ARG(sm_scale > 0.0f && sm_scale < INFINITY, QUAROT_ERR_INVALID,
+               "sm_scale must be finite and > 0");
+  QR_CHECK_ARG(signs_stride_h >= 0, QUAROT_ERR_INVALID, "signs_stride_h must be >= 0");
+  QR_CHECK_ARG(max_len <= S_cache, QUAROT_ERR_INVALID, "max_len = %lld > S_cache = %lld",
+               (long long)max_len, (long long)S_cache);
+  QR_CHECK_ARG(cross_head == 0 || (is_pow2(Hq) && Hq <= 256), QUAROT_ERR_UNSUPPORTED,
+               "cross_head needs Hq a power of two <= 256 (Hq = %lld)", (long long)Hq);
+  if (B == 0) return QUAROT_OK;
+  QR_CHECK_ARG(q && k_q && k_scale && v_q && v_scale && out, QUAROT_ERR_INVALID,
+               "q, k_q, k_scale, v_q, v_scale and out are required");
+  QR_CHECK_ARG(mode == 0 || (k_zero && v_zero), QUAROT_ERR_INVALID, "mode 1 needs k_zero and v_zero");
+  const int64_t need = decode_workspace_bytes(B, Hq, Hkv, max_len);
+  QR_CHECK_ARG(workspace && workspace_bytes >= need, QUAROT_ERR_INVALID,
+               "workspace of %lld bytes needed, %lld given", (long long)need,
+               (long long)workspace_bytes);
+  QR_CHECK_ARG(aligned(q, 16) && aligned(k_q, 16) && aligned(v_q, 16) && aligned(workspace, 16),
+               QUAROT_ERR_MISALIGNED, "q, k_q, v_q and workspace must be 16-byte aligned");
+  QR_CHECK_ARG(aligned(k_scale, 2) && aligned(v_scale, 2) && aligned(out, 2) &&
+                   (mode == 0 || (aligned(k_zero, 2) && aligned(v_zero, 2))),
+               QUAROT_ERR_MISALIGNED, "fp16 buffers must be 2-byte aligned");
+  QR_CHECK_ARG(out_f32 == nullptr || aligned(out_f32, 4), QUAROT_ERR_MISALIGNED,
+               "out_f32 must be 4-byte aligned");
+  QR_CHECK_ARG(lengths == nullptr || aligned(lengths, 4), QUAROT_ERR_MISALIGNED,
+               "lengths must be 4-byte aligned");
+  DecodeTensors t{};
+  t.q = static_cast<const __half*>(q);
+  t.signs = signs;
+  t.signs_stride_h = signs_stride_h;
+  t.k_q = k_q;
+  t.k_scale = static_cast<const __half*>(k_scale);
+  t.k_zero = mode == 1 ? static_cast<const __half*>(k_zero) : nullptr;
+  t.v_q = v_q;
+  t.v_scale = static_cast<const __half*>(v_scale);
+  t.v_zero = mode == 1 ? static_cast<const __half*>(v_zero) : nullptr;
+  t.lengths = lengths;
+  t.out = static_cast<__half*>(out);
+  t.out_f32 = out_f32;
+  t.workspace = workspace;
+  return launch_kv_decode(t, B, Hq, Hkv, S_cache, max_len, sm_scale, int(mode), cross_head != 0,
+                          static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

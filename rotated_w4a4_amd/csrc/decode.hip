@@ -1,0 +1,560 @@
+// quarot_kv_decode_attention: one decode step of attention over the INT4
+// KV cache written by quarot_kv_had_quant.
+//
+// "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
+// summary), section 3.4: Stage 1d (the new query is rotated head-wise by the
+// same Hadamard as the cached keys, so the scores q k^T are unchanged;
+// softmax(q k^T / sqrt(d_h))), Stage 2c (at decode every cached group is
+// dequantised on the fly) and Stage 1c (the online cross-head transform
+// Z (H_{n_h} (x) I_{d_h}) on the attention output before the output
+// projection).
+//
+// Two kernels:
+//   decode_split_kernel    one workgroup per (batch, KV head, position split)
+//                          with all query heads of the KV head's group
+//                          (<= 8): rotate the queries (signs, FWHT-128 by
+//                          shuffles), then per wave a loop over 32-position
+//                          steps with an online softmax; scores and P V run
+//                          on v_mfma_f32_16x16x32_f16 with the fp32 operand
+//                          split into fp16 hi + lo rows (products of fp16
+//                          values with small integers are exact, so the result
+//                          keeps about 22 bits).  Writes (max, sum, unscaled
+//                          output) per split.
+//   decode_combine_kernel  merges the splits, divides by the softmax sum,
+//                          optionally applies the cross-head Walsh-Hadamard
+//                          transform over the query heads, writes fp16.
+//
+// Operand layouts of v_mfma_f32_16x16x32_f16 (lane = column + 16 * group):
+//   A[m][k] at lane m + 16 (k / 8), item k % 8; B[k][n] at lane n + 16 (k / 8),
+//   item k % 8; D[m][n] at lane n + 16 (m / 4), item m % 4.
+// A rows are (head, part) pairs: row m = head m / 2, part m % 2 (0 hi, 1 lo),
+// so a D lane holds hi and lo of two heads side by side.
+//
+// Nibbles become fp16 as (1024 + u) - offset: OR-ing a nibble u into the
+// mantissa of 1024.0 and subtracting 1024 + 8 (two's complement codes,
+// flipped to offset binary first) or 1024 + z (zero-point codes); both steps
+// are exact.  The 8 nibbles of a dword come out in the order
+// 0, 4, 1, 5, 2, 6, 3, 7, and the other operand uses the same order.
+#include "decode.h"
+#include "wave_rows.h"
+
+namespace quarot {
+
+namespace {
+
+constexpr int kDecD = 128;
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kDecStep = 32;    // positions per wave step
+constexpr int kDecHeads = 8;    // query heads per KV head (at most)
+constexpr int kDecUnit = kDecWaves * kDecStep;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+struct DecodeArgs {
+  const __half* q;  // [B, Hq, 128]
+  const int8_t* signs;
+  int64_t signs_stride_h;
+  const uint8_t* kq;
+  const __half* ks;
+  const __half* kz;
+  const uint8_t* vq;
+  const __half* vs;
+  const __half* vz;
+  int hkv, hq, group;
+  int64_t s_cache;
+  int max_len;
+  const int32_t* lengths;
+  int splits, split_len;
+  float score_mul;  // softmax scale * log2(e)
+  float* part_o;    // [B * Hkv * splits][group][128]
+  float* part_ml;   // [B * Hkv * splits][group][2]: running max (log2 units), sum
+};
+
+// k-slot s of an 8-value operand holds nibble / element perm8(s).
+__device__ __forceinline__ constexpr int perm8(int s) { return (s >> 1) + 4 * (s & 1); }
+
+// 8 nibbles -> 8 exact fp16 values (nibble - offset), slot order perm8.
+__device__ __forceinline__ half8_t nibbles_to_half8(uint32_t w, half2_t off) {
+  constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x64006400u;  // fp16 1024.0 twice
+  const half2_t h0 = __builtin_bit_cast(half2_t, (w & kMask) | kExp) - off;
+  const half2_t h1 = __builtin_bit_cast(half2_t, ((w >> 4) & kMask) | kExp) - off;
+  const half2_t h2 = __builtin_bit_cast(half2_t, ((w >> 8) & kMask) | kExp) - off;
+  const half2_t h3 = __builtin_bit_cast(half2_t, ((w >> 12) & kMask) | kExp) - off;
+  half8_t r;
+  r[0] = h0[0];
+  r[1] = h0[1];
+  r[2] = h1[0];
+  r[3] = h1[1];
+  r[4] = h2[0];
+  r[5] = h2[1];
+  r[6] = h3[0];
+  r[7] = h3[1];
+  return r;
+}
+
+// 8 x 8 nibble transpose: on entry nibble j of r[i] is element (i, j), on
+// exit nibble i of r[j].  Three exchanges of index bits: bit 2 (halfwords),
+// bit 1 (bytes), bit 0 (nibbles), each between a pair of registers.
+__device__ __forceinline__ void transpose_nibbles8(uint32_t (&r)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = r[i], b = r[i + 4];
+    r[i] = __builtin_amdgcn_perm(b, a, 0x05040100u);      // a.lo16 | b.lo16 << 16
+    r[i + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi16 | b.hi16 << 16
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((i & 2) == 0) {
+      const uint32_t a = r[i], b = r[i + 2];
+      r[i] = __builtin_amdgcn_perm(b, a, 0x06020400u);      // bytes a0 b0 a2 b2
+      r[i + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);  // bytes a1 b1 a3 b3
+    }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t a = r[i], b = r[i + 1];
+    r[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
+  v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_mov<0x122>(v));  // row_ror:2
+  v = fmaxf(v, dpp_mov<0x121>(v));  // row_ror:1
+  return v;
+}
+
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0x128>(v);
+  v += dpp_mov<0x124>(v);
+  v += dpp_mov<0x122>(v);
+  v += dpp_mov<0x121>(v);
+  return v;
+}
+
+// One step's loads for a lane.  K: lane (n, g) holds bytes 16 g .. 16 g + 15
+// (head dims 32 g .. 32 g + 31) of positions base + n and base + 16 + n.
+// V: lane (c, g) holds dword c (dims 8 c .. 8 c + 7) of positions
+// base + g + 4 i, i = 0..7.  Scales (and zeros) of positions base + n and
+// base + 16 + n.  Positions at or past the valid length are clamped to the
+// last valid one (in bounds; their scores are masked).
+template <int MODE>
+struct StepData {
+  uint4 k[2];
+  uint32_t v[8];
+  __half ks[2], vs[2], kz[2], vz[2];
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_step(StepData<MODE>& d, const uint8_t* kq, const uint8_t* vq,
+                                          const __half* ks, const __half* vs, const __half* kz,
+                                          const __half* vz, int base, int last, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int p = min(base + 16 * t + n, last);
+    d.k[t] = *reinterpret_cast<const uint4*>(kq + int64_t(p) * 64 + 16 * g);
+    d.ks[t] = ks[p];
+    d.vs[t] = vs[p];
+    if (MODE == 1) {
+      d.kz[t] = kz[p];
+      d.vz[t] = vz[p];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = min(base + g + 4 * i, last);
+    d.v[i] = *reinterpret_cast<const uint32_t*>(vq + int64_t(p) * 64 + 4 * n);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p) {
+  __shared__ float q_rot[kDecHeads][kDecD];
+  __shared__ float q_mul[kDecHeads];
+  __shared__ __attribute__((aligned(16))) uint32_t wbuf[kDecWaves][16 * 16];
+  __shared__ __attribute__((aligned(16))) float cmb_o[kDecWaves][kDecHeads][kDecD];
+  __shared__ float cmb_ml[kDecWaves][kDecHeads][2];
+
+  const int bh = blockIdx.x;
+  const int split = blockIdx.y;
+  const int b = bh / p.hkv, kv = bh - b * p.hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int len = p.max_len;
+  if (p.lengths) len = max(0, min(p.lengths[b], p.max_len));
+  const int pos_begin = split * p.split_len;
+  const int pos_end = min(pos_begin + p.split_len, len);
+
+  // ---- rotate the group's queries: q~ = H_128 diag(s) q / sqrt(128) ------
+  {
+    const int hh = tid >> 5, c = tid & 31;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (hh < p.group) {
+      const __half* src = p.q + (int64_t(b) * p.hq + kv * p.group + hh) * kDecD + 4 * c;
+      const uint2 raw = *reinterpret_cast<const uint2*>(src);
+      const half2_t h01 = __builtin_bit_cast(half2_t, raw.x);
+      const half2_t h23 = __builtin_bit_cast(half2_t, raw.y);
+      v[0] = float(h01[0]);
+      v[1] = float(h01[1]);
+      v[2] = float(h23[0]);
+      v[3] = float(h23[1]);
+      if (p.signs) {
+        const int8_t* sg = p.signs + kv * p.signs_stride_h + 4 * c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= float(sg[i]);
+      }
+    }
+    // element e = 4 c + i: bits 0, 1 in registers, bits 2 .. 6 across lanes
+    const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+    v[0] = a0 + a2;
+    v[2] = a0 - a2;
+    v[1] = a1 + a3;
+    v[3] = a1 - a3;
+#pragma unroll
+    for (int k = 1; k < 32; k <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float o = __shfl_xor(v[i], k, 32);
+        v[i] = (c & k) ? o - v[i] : v[i] + o;
+      }
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] *= 0.08838834764831845f;  // 1 / sqrt(128)
+      q_rot[hh][4 * c + i] = v[i];
+      mx = fmaxf(mx, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int k = 1; k < 32; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 32));
+    if (c == 0) {
+      // power of two that brings the head's largest |q~| into [128, 256):
+      // the fp16 hi part cannot overflow and the lo part stays normal
+      int e = 0;
+      (void)frexpf(mx, &e);
+      q_mul[hh] = mx > 0.0f ? ldexpf(1.0f, 8 - e) : 1.0f;
+    }
+  }
+  __syncthreads();
+
+  const int n = lane & 15, g = lane >> 4;  // also (column, row group a) of D
+  // A operands of the score MFMAs: row m = (head m / 2, hi / lo), k-chunk t
+  // covers head dims 32 g + 8 t + perm8(s)
+  half8_t a_q[4];
+  {
+    const int head = n >> 1;
+    const bool lo = n & 1;
+    const float qm = q_mul[head];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float x = q_rot[head][32 * g + 8 * t + perm8(s)] * qm;
+        const _Float16 hi = _Float16(x);
+        a_q[t][s] = lo ? _Float16(x - float(hi)) : hi;
+      }
+  }
+  // per D lane: heads 2 g and 2 g + 1
+  float cs[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) cs[hh] = p.score_mul / q_mul[2 * g + hh];
+
+  const int64_t row0 = (int64_t(b) * p.hkv + kv) * p.s_cache;
+  const uint8_t* kq = p.kq + row0 * 64;
+  const uint8_t* vq = p.vq + row0 * 64;
+  const __half* ks = p.ks + row0;
+  const __half* vs = p.vs + row0;
+  const __half* kz = MODE == 1 ? p.kz + row0 : nullptr;
+  const __half* vz = MODE == 1 ? p.vz + row0 : nullptr;
+  const int last = len - 1;
+
+  half2_t koff, voff;
+  if (MODE == 0) {
+    koff = half2_t{_Float16(1032.0f), _Float16(1032.0f)};
+    voff = koff;
+  } else {
+    voff = half2_t{_Float16(1024.0f), _Float16(1024.0f)};
+  }
+
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.0f, 0.0f}, corr[2] = {0.0f, 0.0f};
+  float4_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t* wb = wbuf[wave];
+
+  int base = pos_begin + kDecStep * wave;
+  StepData<MODE> cur;
+  if (base < pos_end) load_step<MODE>(cur, kq, vq, ks, vs, kz, vz, base, last, lane);
+  for (; base < pos_end; base += kDecUnit) {
+    StepData<MODE> nxt;
+    load_step<MODE>(nxt, kq, vq, ks, vs, kz, vz, base + kDecUnit, last, lane);
+
+    // ---- scores: D[row][position] over two 16-position tiles --------------
+    float4_t sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (MODE == 1) {
+        const _Float16 z = _Float16(1024.0f) + _Float16(__half2float(cur.kz[t]));
+        koff = half2_t{z, z};
+      }
+      const uint32_t w[4] = {cur.k[t].x, cur.k[t].y, cur.k[t].z, cur.k[t].w};
+      sc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t x = MODE == 0 ? w[c] ^ 0x88888888u : w[c];
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_q[c], nibbles_to_half8(x, koff), sc[t],
+                                                       0, 0, 0);
+      }
+    }
+    // ---- online softmax (log2 domain).  u = score + e(v scale): the
+    // weights w = 2^(u - m) * mant(v scale) carry the value scale and stay
+    // <= 1, while the softmax sum takes 2^(u - m - e) -----------------------
+    float u[2][2], vm[2], ve[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      int e = 0;
+      vm[t] = frexpf(__half2float(cur.vs[t]), &e);
+      ve[t] = float(e);
+      const float ksf = __half2float(cur.ks[t]);
+      const bool valid = base + 16 * t + n < pos_end;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float s = (sc[t][2 * hh] + sc[t][2 * hh + 1]) * (ksf * cs[hh]);
+        u[t][hh] = valid ? s + ve[t] : -INFINITY;
+      }
+    }
+    float alpha[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const float mx = row_max16(fmaxf(u[0][hh], u[1][hh]));
+      const float mn = fmaxf(m_run[hh], mx);
+      alpha[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mn);
+      m_run[hh] = mn;
+    }
+    float wt[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float ex = __builtin_amdgcn_exp2f(u[t][hh] - m_run[hh]);
+        wt[t][hh] = ex * vm[t];
+        lsum += ldexpf(ex, -int(ve[t]));
+      }
+      l_run[hh] = l_run[hh] * alpha[hh] + lsum;
+      if (MODE == 1)
+        corr[hh] = corr[hh] * alpha[hh] + wt[0][hh] * __half2float(cur.vz[0]) +
+                   wt[1][hh] * __half2float(cur.vz[1]);
+    }
+    // ---- weights to LDS in the A layout of the P V MFMAs ------------------
+    // row 4 g + 2 hh (+1 for lo), k-slot of position q: group q & 3, slot
+    // inverse-perm8(q >> 2); positions n and 16 + n share one dword
+    {
+      const int off = (n & 3) * 4 + (n >> 2);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float w0 = wt[0][hh] * 256.0f, w1 = wt[1][hh] * 256.0f;
+        const _Float16 h0 = _Float16(w0), h1 = _Float16(w1);
+        const _Float16 l0 = _Float16(w0 - float(h0)), l1 = _Float16(w1 - float(h1));
+        const int row = 4 * g + 2 * hh;
+        wb[row * 16 + off] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+        wb[(row + 1) * 16 + off] = __builtin_bit_cast(uint32_t, half2_t{l0, l1});
+      }
+    }
+    if (alpha[0] != 1.0f || alpha[1] != 1.0f) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[j][0] *= alpha[0];
+        acc[j][1] *= alpha[0];
+        acc[j][2] *= alpha[1];
+        acc[j][3] *= alpha[1];
+      }
+    }
+    const half8_t a_w = *reinterpret_cast<const half8_t*>(&wb[n * 16 + g * 4]);
+    // ---- P V: V nibbles transposed to (dim, 8 positions) per register -----
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = MODE == 0 ? cur.v[i] ^ 0x88888888u : cur.v[i];
+    transpose_nibbles8(r);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_w, nibbles_to_half8(r[j], voff), acc[j],
+                                                      0, 0, 0);
+    cur = nxt;
+  }
+
+  // ---- merge the four waves, write the split's partial result -------------
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    l_run[hh] = row_sum16(l_run[hh]);
+    if (MODE == 1) corr[hh] = row_sum16(corr[hh]);
+    const int head = 2 * g + hh;
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (acc[j][2 * hh] + acc[j][2 * hh + 1]) * (1.0f / 256.0f) - corr[hh];
+    float4* dst = reinterpret_cast<float4*>(&cmb_o[wave][head][8 * n]);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    if (n == 0) {
+      cmb_ml[wave][head][0] = m_run[hh];
+      cmb_ml[wave][head][1] = l_run[hh];
+    }
+  }
+  __syncthreads();
+  {
+    const int head = tid >> 5, c = tid & 31;
+    if (head < p.group) {
+      float mw[kDecWaves], big = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        mw[w] = cmb_ml[w][head][0];
+        big = fmaxf(big, mw[w]);
+      }
+      float lsum = 0.0f;
+      float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(mw[w] - big);
+        lsum += f * cmb_ml[w][head][1];
+        const float4 x = reinterpret_cast<const float4*>(cmb_o[w][head])[c];
+        o.x += f * x.x;
+        o.y += f * x.y;
+        o.z += f * x.z;
+        o.w += f * x.w;
+      }
+      const int64_t slot = (int64_t(bh) * p.splits + split) * p.group + head;
+      reinterpret_cast<float4*>(p.part_o + slot * kDecD)[c] = o;
+      if (c == 0) {
+        p.part_ml[2 * slot] = big;
+        p.part_ml[2 * slot + 1] = lsum;
+      }
+    }
+  }
+}
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  int hkv, hq, group, splits;
+  __half* out;     // [B, Hq, 128]
+  float* out_f32;  // optional, same layout
+};
+
+// Block (b, 16-dim chunk): every query head's 16 outputs.  With CROSS the
+// Walsh-Hadamard transform over the head index runs in LDS (Sylvester order,
+// normalised by 1 / sqrt(Hq)).
+template <bool CROSS>
+__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs p) {
+  extern __shared__ float zs[];  // [Hq][16]
+  const int b = blockIdx.x, d0 = 16 * blockIdx.y;
+  const int total = p.hq * 16;
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int hq = idx >> 4, dl = idx & 15;
+    const int kv = hq / p.group, gi = hq - kv * p.group;
+    const int64_t s0 = (int64_t(b) * p.hkv + kv) * p.splits;
+    float big = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) big = fmaxf(big, p.part_ml[2 * ((s0 + s) * p.group + gi)]);
+    float lsum = 0.0f, o = 0.0f;
+    for (int s = 0; s < p.splits; ++s) {
+      const int64_t slot = (s0 + s) * p.group + gi;
+      const float f = __builtin_amdgcn_exp2f(p.part_ml[2 * slot] - big);
+      lsum += f * p.part_ml[2 * slot + 1];
+      o += f * p.part_o[slot * kDecD + d0 + dl];
+    }
+    const float res = lsum > 0.0f ? o / lsum : 0.0f;
+    if (CROSS) {
+      zs[idx] = res;
+    } else {
+      const int64_t at = (int64_t(b) * p.hq + hq) * kDecD + d0 + dl;
+      p.out[at] = __float2half_rn(res);
+      if (p.out_f32) p.out_f32[at] = res;
+    }
+  }
+  if (!CROSS) return;
+  __syncthreads();
+  const int half_total = total / 2;
+  for (int h = 1; h < p.hq; h <<= 1) {
+    for (int idx = threadIdx.x; idx < half_total; idx += blockDim.x) {
+      const int i = idx >> 4, dl = idx & 15;
+      const int lo = (i / h) * 2 * h + (i % h), hi = lo + h;
+      const float a = zs[lo * 16 + dl], c = zs[hi * 16 + dl];
+      zs[lo * 16 + dl] = a + c;
+      zs[hi * 16 + dl] = a - c;
+    }
+    __syncthreads();
+  }
+  const float norm = 1.0f / sqrtf(float(p.hq));
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int hq = idx >> 4, dl = idx & 15;
+    const float res = zs[idx] * norm;
+    const int64_t at = (int64_t(b) * p.hq + hq) * kDecD + d0 + dl;
+    p.out[at] = __float2half_rn(res);
+    if (p.out_f32) p.out_f32[at] = res;
+  }
+}
+
+}  // namespace
+
+void decode_plan(int64_t B, int64_t Hkv, int64_t max_len, int& splits, int& split_len) {
+  const int64_t units = (max_len + kDecUnit - 1) / kDecUnit;
+  int64_t s = 1;
+  // split positions until the grid has about 1024 workgroups, keeping at
+  // least two 128-position units per split
+  while (B * Hkv * s < 1024 && (units + 2 * s - 1) / (2 * s) >= 2) s *= 2;
+  const int64_t per = (units + s - 1) / s;
+  splits = int((units + per - 1) / per);
+  split_len = int(per * kDecUnit);
+}
+
+int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len) {
+  int splits = 0, split_len = 0;
+  decode_plan(B, Hkv, max_len, splits, split_len);
+  const int64_t slots = B * Hkv * splits * (Hq / Hkv);
+  return slots * (kDecD + 2) * int64_t(sizeof(float));
+}
+
+int launch_kv_decode(const DecodeTensors& t, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t S_cache, int64_t max_len, float sm_scale, int mode, bool cross,
+                     hipStream_t stream) {
+  DecodeArgs p{};
+  p.q = t.q;
+  p.signs = t.signs;
+  p.signs_stride_h = t.signs_stride_h;
+  p.kq = t.k_q;
+  p.ks = t.k_scale;
+  p.kz = t.k_zero;
+  p.vq = t.v_q;
+  p.vs = t.v_scale;
+  p.vz = t.v_zero;
+  p.hkv = int(Hkv);
+  p.hq = int(Hq);
+  p.group = int(Hq / Hkv);
+  p.s_cache = S_cache;
+  p.max_len = int(max_len);
+  p.lengths = t.lengths;
+  decode_plan(B, Hkv, max_len, p.splits, p.split_len);
+  p.score_mul = sm_scale * 1.4426950408889634f;
+  const int64_t slots = B * Hkv * p.splits * p.group;
+  p.part_o = static_cast<float*>(t.workspace);
+  p.part_ml = p.part_o + slots * kDecD;
+
+  const dim3 grid{unsigned(B * Hkv), unsigned(p.splits)}, block{unsigned(kDecThreads)};
+  if (mode == 1)
+    hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<0>, grid, block, 0, stream, p);
+  int st = check_launch("kv_decode split");
+  if (st != QUAROT_OK) return st;
+
+  CombineArgs c{p.part_o, p.part_ml, p.hkv, p.hq, p.group, p.splits, t.out, t.out_f32};
+  const dim3 cgrid{unsigned(B), unsigned(kDecD / 16)};
+  const size_t lds = cross ? size_t(Hq) * 16 * sizeof(float) : 0;
+  if (cross)
+    hipLaunchKernelGGL(decode_combine_kernel<true>, cgrid, dim3(256), lds, stream, c);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<false>, cgrid, dim3(256), 0, stream, c);
+  return check_launch("kv_decode combine");
+}
+
+}  // namespace quarot

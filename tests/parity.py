@@ -115,3 +115,29 @@ def check_asym(codes_gpu: np.ndarray, scales_gpu16: np.ndarray, zeros_gpu16: np.
     f = float((diff > 0).mean())
     assert f <= code_frac, f"{f:.2e} of the codes differ (> {code_frac:.0e})"
     return differ, f
+
+
+# Decode attention.  The kernel works in fp32-class arithmetic (fp32 query
+# rotation, hi+lo fp16 operand splits keeping ~22 bits, fp32 accumulation and
+# softmax); its error on an output element is a small multiple of 2^-22
+# times the magnitude of the terms it sums, sum_p p_p |v^_p[d]| (the output
+# itself can be far smaller after cancellation).  1e-5 of that magnitude
+# (the largest over the row) leaves a margin of about 40.
+ATT_TOL = 1e-5
+
+
+def check_attention(gpu32, gpu16, ref, mag, tol: float = ATT_TOL) -> float:
+    """gpu32 / gpu16 [B, H, D] against the oracle ``ref`` with ``mag`` = sum_p p_p |v^_p|
+    (same shape): |gpu32 - ref| <= tol * max_d mag per (b, h) row, and the fp16
+    output within that bound or one fp16 ulp of the reference."""
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = tol * np.maximum(np.asarray(mag, dtype=np.float64).max(axis=-1, keepdims=True), 1e-30)
+    e32 = np.abs(np.asarray(gpu32, dtype=np.float64) - ref)
+    worst = float((e32 / bound).max())
+    assert worst <= 1.0, f"attention output: error {worst:.2f} x the bound"
+    r16 = ref.astype(np.float16).astype(np.float64)
+    ulp = np.abs(np.spacing(ref.astype(np.float16)).astype(np.float64))
+    e16 = np.abs(np.asarray(gpu16, dtype=np.float64) - ref)
+    ok16 = (e16 <= bound + np.abs(r16 - ref)) | (e16 <= ulp)
+    assert ok16.all(), f"fp16 output: {int((~ok16).sum())} elements off"
+    return worst * tol

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(lib):
     with open(os.path.join(ROOT, "include", "quarot.h")) as f:
         text = f.read()
     names = set(re.findall(r"\b(quarot_[a-z0-9_]+)\s*\(", text))
-    assert {"quarot_had_quant", "quarot_w4a4_gemm", "quarot_kv_had_quant"} <= names
+    assert {"quarot_had_quant", "quarot_w4a4_gemm", "quarot_kv_had_quant",
+            "quarot_kv_decode_attention", "quarot_kv_decode_workspace_bytes"} <= names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -164,3 +165,63 @@ def test_kv_rejects(lib, kw, status):
 
 def test_kv_empty_is_noop(lib):
     assert _kv(lib, S=0, k=None) == OK
+
+
+def _dec(lib, **kw):
+    a = dict(q=FAKE, B=2, Hq=8, Hkv=2, D=128, signs=None, ssh=0, mode=0, kq=FAKE, ks=FAKE,
+             kz=None, vq=FAKE, vs=FAKE, vz=None, S_cache=512, max_len=300, lengths=None,
+             sm=0.088, cross=0, out=FAKE, out32=None, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.quarot_kv_decode_attention(a["q"], a["B"], a["Hq"], a["Hkv"], a["D"], a["signs"],
+                                          a["ssh"], a["mode"], a["kq"], a["ks"], a["kz"], a["vq"],
+                                          a["vs"], a["vz"], a["S_cache"], a["max_len"],
+                                          a["lengths"], a["sm"], a["cross"], a["out"],
+                                          a["out32"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID),
+    (dict(Hq=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID),
+    (dict(D=64), UNSUPPORTED),
+    (dict(Hq=32, Hkv=2), UNSUPPORTED),       # group of 16 query heads
+    (dict(mode=2), INVALID),
+    (dict(mode=1), INVALID),                 # zero points missing
+    (dict(mode=1, kz=FAKE, vz=FAKE + 1), MISALIGNED),
+    (dict(cross=2), INVALID),
+    (dict(cross=1, Hq=6, Hkv=2), UNSUPPORTED),
+    (dict(cross=1, Hq=512, Hkv=64), UNSUPPORTED),
+    (dict(sm=0.0), INVALID),
+    (dict(sm=float("inf")), INVALID),
+    (dict(sm=float("nan")), INVALID),
+    (dict(max_len=0), INVALID),
+    (dict(max_len=513), INVALID),
+    (dict(ssh=-1), INVALID),
+    (dict(q=None), INVALID),
+    (dict(vs=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(ws_bytes=64), INVALID),
+    (dict(q=FAKE + 8), MISALIGNED),
+    (dict(kq=FAKE + 4), MISALIGNED),
+    (dict(ws=FAKE + 4), MISALIGNED),
+    (dict(out=FAKE + 1), MISALIGNED),
+    (dict(out32=FAKE + 2), MISALIGNED),
+    (dict(lengths=FAKE + 2), MISALIGNED),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _dec(lib, **kw) == status
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _dec(lib, B=0, q=None, out=None, ws=None) == OK
+
+
+def test_decode_workspace_size(lib):
+    # (B * Hkv * splits) slots per query head of the group, 130 floats each
+    n = lib.quarot_kv_decode_workspace_bytes(16, 64, 8, 128, 4096)
+    assert n > 0 and n % (130 * 4 * 8) == 0
+    assert lib.quarot_kv_decode_workspace_bytes(1, 16, 1, 128, 100) == UNSUPPORTED
+    assert lib.quarot_kv_decode_workspace_bytes(1, 8, 1, 128, 0) == INVALID
+    sizes = [lib.quarot_kv_decode_workspace_bytes(2, 8, 2, 128, n) for n in range(1, 3000, 37)]
+    assert all(s > 0 for s in sizes)

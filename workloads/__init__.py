@@ -41,6 +41,9 @@ __all__ = [
     "KV_CONFIG",
     "make_act_inputs",
     "make_kv_inputs",
+    "DecodeConfig",
+    "DECODE_CONFIGS",
+    "make_decode_query",
     "random_signs",
     "config_by_name",
 ]
@@ -102,11 +105,43 @@ class KVConfig:
 KV_CONFIG = KVConfig("kv_70b_gqa", 16, 8, 4096, 128, 2, 30.0)
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    """One decode step: the new query of every (batch row, query head) against
+    a cache of ``kv.positions`` positions (the cache is the KV workload's)."""
+
+    name: str
+    kv: KVConfig
+    q_heads: int
+
+
+# LLaMA-2-70B-shaped grouped-query decode (8 KV heads, 64 query heads) on the
+# KV workload's cache, and the LLaMA-2-7B attention of the pages' decode
+# timing table (32 heads x 128, 2047 cached tokens + the new one, batch 16).
+DECODE_CONFIGS = {
+    "decode_70b_gqa": DecodeConfig("decode_70b_gqa", KV_CONFIG, 64),
+    "decode_7b_mha": DecodeConfig("decode_7b_mha",
+                                  KVConfig("kv_7b_mha", 16, 32, 2048, 128, 2, 30.0), 32),
+}
+
+
+def make_decode_query(cfg: DecodeConfig, seed: int = 0, batch: Optional[int] = None) -> np.ndarray:
+    """Post-RoPE queries fp16 [batch, q_heads, head_dim] ~ N(0, 1), drawn from
+    default_rng(seed + 1) so that the cache's own draws (default_rng(seed))
+    stay those of the KV workload."""
+    rng = np.random.default_rng(seed + 1)
+    bsz = cfg.kv.batch if batch is None else batch
+    q = rng.standard_normal((bsz, cfg.q_heads, cfg.kv.head_dim), dtype=np.float32)
+    return q.astype(np.float16)
+
+
 def config_by_name(name: str):
     if name in ACT_CONFIGS:
         return ACT_CONFIGS[name]
     if name == KV_CONFIG.name:
         return KV_CONFIG
+    if name in DECODE_CONFIGS:
+        return DECODE_CONFIGS[name]
     raise KeyError(name)
 
 
