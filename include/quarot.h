@@ -206,7 +206,8 @@ int quarot_kv_had_quant(const void* k, const void* v,
  *   k_scale, v_scale, k_zero, v_zero  fp16 [B x Hkv x S_cache].
  *   D            head dimension; 128 only.
  *   Hq, Hkv      Hq a multiple of Hkv, Hq / Hkv <= 8.
- *   max_len      1 <= max_len <= S_cache: positions attended at most.
+ *   max_len      1 <= max_len <= S_cache (and <= 2^24): positions attended
+ *                at most.
  *   lengths      optional int32 [B] device array of per-row lengths (values
  *                above max_len are clamped to it, negative ones to 0).
  *   sm_scale     softmax scale, finite and > 0 (1/sqrt(128) in the pages).
@@ -219,8 +220,8 @@ int quarot_kv_had_quant(const void* k, const void* v,
  *                on entry do not matter.  Calls that share a workspace must
  *                be ordered (one stream).
  * Errors: INVALID for bad sizes, mode, scale, missing buffers or a short
- * workspace; UNSUPPORTED for D != 128, Hq / Hkv > 8, or cross_head with Hq
- * not a power of two <= 256; MISALIGNED as stated.
+ * workspace; UNSUPPORTED for D != 128, Hq / Hkv > 8, max_len > 2^24, or
+ * cross_head with Hq not a power of two <= 256; MISALIGNED as stated.
  */
 int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
                                const int8_t* signs, int64_t signs_stride_h, int32_t mode,

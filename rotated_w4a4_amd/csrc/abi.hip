@@ -199,8 +199,9 @@ int decode_shape_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_l
                (long long)D);
   QR_CHECK_ARG(Hq / Hkv <= 8, QUAROT_ERR_UNSUPPORTED, "Hq / Hkv = %lld > 8",
                (long long)(Hq / Hkv));
-  QR_CHECK_ARG(max_len >= 1 && max_len < (int64_t(1) << 30), QUAROT_ERR_INVALID,
-               "max_len = %lld out of range", (long long)max_len);
+  QR_CHECK_ARG(max_len >= 1, QUAROT_ERR_INVALID, "max_len = %lld < 1", (long long)max_len);
+  QR_CHECK_ARG(max_len <= (int64_t(1) << 24), QUAROT_ERR_UNSUPPORTED,
+               "max_len = %lld > 2^24 (32-bit buffer offsets)", (long long)max_len);
   QR_CHECK_ARG(B * Hkv < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED, "B * Hkv too large");
   return QUAROT_OK;
 }

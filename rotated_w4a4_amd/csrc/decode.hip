@@ -74,13 +74,32 @@ struct DecodeArgs {
 // k-slot s of an 8-value operand holds nibble / element perm8(s).
 __device__ __forceinline__ constexpr int perm8(int s) { return (s >> 1) + 4 * (s & 1); }
 
-// 8 nibbles -> 8 exact fp16 values (nibble - offset), slot order perm8.
-__device__ __forceinline__ half8_t nibbles_to_half8(uint32_t w, half2_t off) {
-  constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x64006400u;  // fp16 1024.0 twice
-  const half2_t h0 = __builtin_bit_cast(half2_t, (w & kMask) | kExp) - off;
-  const half2_t h1 = __builtin_bit_cast(half2_t, ((w >> 4) & kMask) | kExp) - off;
-  const half2_t h2 = __builtin_bit_cast(half2_t, ((w >> 8) & kMask) | kExp) - off;
-  const half2_t h3 = __builtin_bit_cast(half2_t, ((w >> 12) & kMask) | kExp) - off;
+// Slots 2, 3, 6, 7 (nibbles 1, 5, 3, 7) are taken from bits 4..7 of a
+// halfword, i.e. at 16 times their value; the other operand divides those
+// slots by 16 (a power of two: exact).
+__device__ __forceinline__ constexpr bool slot_x16(int s) { return (s & 2) != 0; }
+
+// (x & m) ^ c on the bits of m, c elsewhere: v_bitop3 with table 0x6A.  With
+// c = the fp16 exponent of 1024 outside m and an XOR pattern inside m it
+// builds 1024 + u (or 1024 + 16 u) straight from a nibble, flipping
+// two's-complement codes to offset binary on the way when asked.
+__device__ __forceinline__ uint32_t nib_bits(uint32_t x, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(x, m, c, 0x6A);
+}
+
+// 8 nibbles -> 8 exact fp16 values in slot order perm8:
+//   slots 0, 1, 4, 5: (1024 + u) - off1 ;  slots 2, 3, 6, 7: (1024 + 16 u) - off16,
+// with u the nibble, XOR 8 when FLIP (two's complement -> offset binary).
+template <bool FLIP>
+__device__ __forceinline__ half8_t nibbles_to_half8(uint32_t w, half2_t off1, half2_t off16) {
+  constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u;
+  constexpr uint32_t cLo = 0x64006400u | (FLIP ? 0x00080008u : 0u);
+  constexpr uint32_t cHi = 0x64006400u | (FLIP ? 0x00800080u : 0u);
+  const uint32_t w8 = w >> 8;
+  const half2_t h0 = __builtin_bit_cast(half2_t, nib_bits(w, kLo, cLo)) - off1;     // nibbles 0, 4
+  const half2_t h1 = __builtin_bit_cast(half2_t, nib_bits(w, kHi, cHi)) - off16;    // 1, 5
+  const half2_t h2 = __builtin_bit_cast(half2_t, nib_bits(w8, kLo, cLo)) - off1;    // 2, 6
+  const half2_t h3 = __builtin_bit_cast(half2_t, nib_bits(w8, kHi, cHi)) - off16;   // 3, 7
   half8_t r;
   r[0] = h0[0];
   r[1] = h0[1];
@@ -134,44 +153,66 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over [base, base + bytes): loads at offsets >= bytes return 0
+// and touch no memory.
+__device__ __forceinline__ rsrc_t buffer_of(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Per workgroup: buffers over the split's positions [0, pos_end) of its
+// (batch, KV head) cache rows.
+struct SplitBuffers {
+  rsrc_t k, v, ks, vs, kz, vz;
+};
+
 // One step's loads for a lane.  K: lane (n, g) holds bytes 16 g .. 16 g + 15
 // (head dims 32 g .. 32 g + 31) of positions base + n and base + 16 + n.
 // V: lane (c, g) holds dword c (dims 8 c .. 8 c + 7) of positions
 // base + g + 4 i, i = 0..7.  Scales (and zeros) of positions base + n and
-// base + 16 + n.  Positions at or past the valid length are clamped to the
-// last valid one (in bounds; their scores are masked).
+// base + 16 + n.  Positions past the split read as 0 (masked later).
 template <int MODE>
 struct StepData {
   uint4 k[2];
   uint32_t v[8];
-  __half ks[2], vs[2], kz[2], vz[2];
+  uint16_t ks[2], vs[2], kz[2], vz[2];
 };
 
 template <int MODE>
-__device__ __forceinline__ void load_step(StepData<MODE>& d, const uint8_t* kq, const uint8_t* vq,
-                                          const __half* ks, const __half* vs, const __half* kz,
-                                          const __half* vz, int base, int last, int lane) {
-  const int n = lane & 15, g = lane >> 4;
+__device__ __forceinline__ void load_step(StepData<MODE>& d, const SplitBuffers& r, int base,
+                                          int voff_k, int voff_v, int voff_s) {
+  // the step's offset goes into the per-lane offset (the range check covers
+  // the per-lane and instruction offsets)
+  const int vk = voff_k + base * 64, vv = voff_v + base * 64, vs = voff_s + base * 2;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int p = min(base + 16 * t + n, last);
-    d.k[t] = *reinterpret_cast<const uint4*>(kq + int64_t(p) * 64 + 16 * g);
-    d.ks[t] = ks[p];
-    d.vs[t] = vs[p];
+    const auto kk = __builtin_amdgcn_raw_buffer_load_b128(r.k, vk + 1024 * t, 0, 0);
+    d.k[t] = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+    d.ks[t] = __builtin_amdgcn_raw_buffer_load_b16(r.ks, vs + 32 * t, 0, 0);
+    d.vs[t] = __builtin_amdgcn_raw_buffer_load_b16(r.vs, vs + 32 * t, 0, 0);
     if (MODE == 1) {
-      d.kz[t] = kz[p];
-      d.vz[t] = vz[p];
+      d.kz[t] = __builtin_amdgcn_raw_buffer_load_b16(r.kz, vs + 32 * t, 0, 0);
+      d.vz[t] = __builtin_amdgcn_raw_buffer_load_b16(r.vz, vs + 32 * t, 0, 0);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = min(base + g + 4 * i, last);
-    d.v[i] = *reinterpret_cast<const uint32_t*>(vq + int64_t(p) * 64 + 4 * n);
-  }
+  for (int i = 0; i < 8; ++i)
+    d.v[i] = __builtin_amdgcn_raw_buffer_load_b32(r.v, vv + 256 * i, 0, 0);
 }
 
+__device__ __forceinline__ float f16_bits_to_float(uint16_t h) {
+  return float(__builtin_bit_cast(_Float16, h));
+}
+
+// The online softmax keeps its reference m until a step's maximum exceeds it
+// by more than this (log2 units); weights then stay below 2^6.
+constexpr float kRescaleSlack = 6.0f;
+// Weights are scaled by 2^8 before the fp16 hi / lo split (w * 2^8 < 2^14).
+constexpr float kWeightScale = 256.0f;
+
 template <int MODE>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs p) {
   __shared__ float q_rot[kDecHeads][kDecD];
   __shared__ float q_mul[kDecHeads];
   __shared__ __attribute__((aligned(16))) uint32_t wbuf[kDecWaves][16 * 16];
@@ -181,7 +222,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
   const int bh = blockIdx.x;
   const int split = blockIdx.y;
   const int b = bh / p.hkv, kv = bh - b * p.hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int len = p.max_len;
   if (p.lengths) len = max(0, min(p.lengths[b], p.max_len));
   const int pos_begin = split * p.split_len;
@@ -240,7 +282,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
 
   const int n = lane & 15, g = lane >> 4;  // also (column, row group a) of D
   // A operands of the score MFMAs: row m = (head m / 2, hi / lo), k-chunk t
-  // covers head dims 32 g + 8 t + perm8(s)
+  // covers head dims 32 g + 8 t + perm8(s); x16 slots divided by 16
   half8_t a_q[4];
   {
     const int head = n >> 1;
@@ -250,7 +292,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const float x = q_rot[head][32 * g + 8 * t + perm8(s)] * qm;
+        const float x = q_rot[head][32 * g + 8 * t + perm8(s)] * (slot_x16(s) ? qm * 0.0625f : qm);
         const _Float16 hi = _Float16(x);
         a_q[t][s] = lo ? _Float16(x - float(hi)) : hi;
       }
@@ -261,21 +303,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
   for (int hh = 0; hh < 2; ++hh) cs[hh] = p.score_mul / q_mul[2 * g + hh];
 
   const int64_t row0 = (int64_t(b) * p.hkv + kv) * p.s_cache;
-  const uint8_t* kq = p.kq + row0 * 64;
-  const uint8_t* vq = p.vq + row0 * 64;
-  const __half* ks = p.ks + row0;
-  const __half* vs = p.vs + row0;
-  const __half* kz = MODE == 1 ? p.kz + row0 : nullptr;
-  const __half* vz = MODE == 1 ? p.vz + row0 : nullptr;
-  const int last = len - 1;
-
-  half2_t koff, voff;
-  if (MODE == 0) {
-    koff = half2_t{_Float16(1032.0f), _Float16(1032.0f)};
-    voff = koff;
-  } else {
-    voff = half2_t{_Float16(1024.0f), _Float16(1024.0f)};
+  const int nrec = max(pos_end, 0);
+  SplitBuffers bufs;
+  bufs.k = buffer_of(p.kq + row0 * 64, nrec * 64);
+  bufs.v = buffer_of(p.vq + row0 * 64, nrec * 64);
+  bufs.ks = buffer_of(p.ks + row0, nrec * 2);
+  bufs.vs = buffer_of(p.vs + row0, nrec * 2);
+  if (MODE == 1) {
+    bufs.kz = buffer_of(p.kz + row0, nrec * 2);
+    bufs.vz = buffer_of(p.vz + row0, nrec * 2);
   }
+  const int voff_k = n * 64 + 16 * g, voff_v = g * 64 + 4 * n, voff_s = 2 * n;
+
+  // fp16 offsets subtracted after the nibble -> fp16 step (see nibbles_to_half8)
+  const half2_t v_off1 = MODE == 0 ? half2_t{_Float16(1032.0f), _Float16(1032.0f)}
+                                   : half2_t{_Float16(1024.0f), _Float16(1024.0f)};
+  const half2_t v_off16 = MODE == 0 ? half2_t{_Float16(1152.0f), _Float16(1152.0f)}
+                                    : half2_t{_Float16(1024.0f), _Float16(1024.0f)};
+  // weights of positions n and 16 + n sit in x16 slots when (n >> 2) is odd
+  const float w_scale = ((n >> 2) & 1) ? kWeightScale * 0.0625f : kWeightScale;
 
   float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.0f, 0.0f}, corr[2] = {0.0f, 0.0f};
   float4_t acc[8];
@@ -285,52 +331,61 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
 
   int base = pos_begin + kDecStep * wave;
   StepData<MODE> cur;
-  if (base < pos_end) load_step<MODE>(cur, kq, vq, ks, vs, kz, vz, base, last, lane);
+  if (base < pos_end) load_step<MODE>(cur, bufs, base, voff_k, voff_v, voff_s);
   for (; base < pos_end; base += kDecUnit) {
     StepData<MODE> nxt;
-    load_step<MODE>(nxt, kq, vq, ks, vs, kz, vz, base + kDecUnit, last, lane);
+    load_step<MODE>(nxt, bufs, base + kDecUnit, voff_k, voff_v, voff_s);
 
     // ---- scores: D[row][position] over two 16-position tiles --------------
     float4_t sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if (MODE == 1) {
-        const _Float16 z = _Float16(1024.0f) + _Float16(__half2float(cur.kz[t]));
-        koff = half2_t{z, z};
+      half2_t k_off1, k_off16;
+      if (MODE == 0) {
+        k_off1 = v_off1;
+        k_off16 = v_off16;
+      } else {
+        const float z = f16_bits_to_float(cur.kz[t]);
+        const _Float16 z1 = _Float16(1024.0f + z), z16 = _Float16(1024.0f + 16.0f * z);
+        k_off1 = half2_t{z1, z1};
+        k_off16 = half2_t{z16, z16};
       }
       const uint32_t w[4] = {cur.k[t].x, cur.k[t].y, cur.k[t].z, cur.k[t].w};
       sc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t x = MODE == 0 ? w[c] ^ 0x88888888u : w[c];
-        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_q[c], nibbles_to_half8(x, koff), sc[t],
-                                                       0, 0, 0);
-      }
+      for (int c = 0; c < 4; ++c)
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            a_q[c], nibbles_to_half8<MODE == 0>(w[c], k_off1, k_off16), sc[t], 0, 0, 0);
     }
     // ---- online softmax (log2 domain).  u = score + e(v scale): the
-    // weights w = 2^(u - m) * mant(v scale) carry the value scale and stay
-    // <= 1, while the softmax sum takes 2^(u - m - e) -----------------------
-    float u[2][2], vm[2], ve[2];
+    // weights w = 2^(u - m) * mant(v scale) carry the value scale, while the
+    // softmax sum takes 2^(u - m - e) -----------------------------------------
+    float u[2][2], vm[2];
+    int ve[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      int e = 0;
-      vm[t] = frexpf(__half2float(cur.vs[t]), &e);
-      ve[t] = float(e);
-      const float ksf = __half2float(cur.ks[t]);
+      vm[t] = frexpf(f16_bits_to_float(cur.vs[t]), &ve[t]);
+      const float ksf = f16_bits_to_float(cur.ks[t]);
       const bool valid = base + 16 * t + n < pos_end;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const float s = (sc[t][2 * hh] + sc[t][2 * hh + 1]) * (ksf * cs[hh]);
-        u[t][hh] = valid ? s + ve[t] : -INFINITY;
+        u[t][hh] = valid ? s + float(ve[t]) : -INFINITY;
       }
     }
+    // the reference m moves only when a step's maximum exceeds it by more
+    // than kRescaleSlack; the accumulators are rescaled then
     float alpha[2];
+    bool moved = false;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const float mx = row_max16(fmaxf(u[0][hh], u[1][hh]));
-      const float mn = fmaxf(m_run[hh], mx);
-      alpha[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mn);
-      m_run[hh] = mn;
+      alpha[hh] = 1.0f;
+      if (mx > m_run[hh] + kRescaleSlack) {
+        alpha[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mx);
+        m_run[hh] = mx;
+        moved = true;
+      }
     }
     float wt[2][2];
 #pragma unroll
@@ -340,12 +395,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
       for (int t = 0; t < 2; ++t) {
         const float ex = __builtin_amdgcn_exp2f(u[t][hh] - m_run[hh]);
         wt[t][hh] = ex * vm[t];
-        lsum += ldexpf(ex, -int(ve[t]));
+        lsum += ldexpf(ex, -ve[t]);
       }
       l_run[hh] = l_run[hh] * alpha[hh] + lsum;
       if (MODE == 1)
-        corr[hh] = corr[hh] * alpha[hh] + wt[0][hh] * __half2float(cur.vz[0]) +
-                   wt[1][hh] * __half2float(cur.vz[1]);
+        corr[hh] = corr[hh] * alpha[hh] + wt[0][hh] * f16_bits_to_float(cur.vz[0]) +
+                   wt[1][hh] * f16_bits_to_float(cur.vz[1]);
     }
     // ---- weights to LDS in the A layout of the P V MFMAs ------------------
     // row 4 g + 2 hh (+1 for lo), k-slot of position q: group q & 3, slot
@@ -354,7 +409,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
       const int off = (n & 3) * 4 + (n >> 2);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const float w0 = wt[0][hh] * 256.0f, w1 = wt[1][hh] * 256.0f;
+        const float w0 = wt[0][hh] * w_scale, w1 = wt[1][hh] * w_scale;
         const _Float16 h0 = _Float16(w0), h1 = _Float16(w1);
         const _Float16 l0 = _Float16(w0 - float(h0)), l1 = _Float16(w1 - float(h1));
         const int row = 4 * g + 2 * hh;
@@ -362,7 +417,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
         wb[(row + 1) * 16 + off] = __builtin_bit_cast(uint32_t, half2_t{l0, l1});
       }
     }
-    if (alpha[0] != 1.0f || alpha[1] != 1.0f) {
+    if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         acc[j][0] *= alpha[0];
@@ -375,12 +430,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
     // ---- P V: V nibbles transposed to (dim, 8 positions) per register -----
     uint32_t r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = MODE == 0 ? cur.v[i] ^ 0x88888888u : cur.v[i];
+    for (int i = 0; i < 8; ++i) r[i] = cur.v[i];
     transpose_nibbles8(r);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_w, nibbles_to_half8(r[j], voff), acc[j],
-                                                      0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          a_w, nibbles_to_half8<MODE == 0>(r[j], v_off1, v_off16), acc[j], 0, 0, 0);
     cur = nxt;
   }
 
@@ -392,7 +447,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs p)
     const int head = 2 * g + hh;
     float o[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = (acc[j][2 * hh] + acc[j][2 * hh + 1]) * (1.0f / 256.0f) - corr[hh];
+    for (int j = 0; j < 8; ++j)
+      o[j] = (acc[j][2 * hh] + acc[j][2 * hh + 1]) * (1.0f / kWeightScale) - corr[hh];
     float4* dst = reinterpret_cast<float4*>(&cmb_o[wave][head][8 * n]);
     dst[0] = make_float4(o[0], o[1], o[2], o[3]);
     dst[1] = make_float4(o[4], o[5], o[6], o[7]);
@@ -441,11 +497,15 @@ struct CombineArgs {
   float* out_f32;  // optional, same layout
 };
 
-// Block (b, 16-dim chunk): every query head's 16 outputs.  With CROSS the
-// Walsh-Hadamard transform over the head index runs in LDS (Sylvester order,
-// normalised by 1 / sqrt(Hq)).
+constexpr int kCombineBatch = 8;  // split partials loaded together
+
+// Block (b, 16-dim chunk): every query head's 16 outputs, one per thread.
+// Each thread merges its head's splits (loads issued kCombineBatch at a
+// time, so a few memory round trips cover all splits).  With CROSS the
+// Walsh-Hadamard transform over the head index runs in LDS (Sylvester
+// order, normalised by 1 / sqrt(Hq)).
 template <bool CROSS>
-__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs p) {
+__global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
   extern __shared__ float zs[];  // [Hq][16]
   const int b = blockIdx.x, d0 = 16 * blockIdx.y;
   const int total = p.hq * 16;
@@ -453,14 +513,34 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs p) {
     const int hq = idx >> 4, dl = idx & 15;
     const int kv = hq / p.group, gi = hq - kv * p.group;
     const int64_t s0 = (int64_t(b) * p.hkv + kv) * p.splits;
-    float big = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) big = fmaxf(big, p.part_ml[2 * ((s0 + s) * p.group + gi)]);
-    float lsum = 0.0f, o = 0.0f;
-    for (int s = 0; s < p.splits; ++s) {
-      const int64_t slot = (s0 + s) * p.group + gi;
-      const float f = __builtin_amdgcn_exp2f(p.part_ml[2 * slot] - big);
-      lsum += f * p.part_ml[2 * slot + 1];
-      o += f * p.part_o[slot * kDecD + d0 + dl];
+    float big = -INFINITY, lsum = 0.0f, o = 0.0f;
+    for (int sb = 0; sb < p.splits; sb += kCombineBatch) {
+      float mv[kCombineBatch], lv[kCombineBatch], ov[kCombineBatch];
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) {
+        mv[i] = -INFINITY;
+        lv[i] = 0.0f;
+        ov[i] = 0.0f;
+        if (sb + i < p.splits) {
+          const int64_t slot = (s0 + sb + i) * p.group + gi;
+          mv[i] = p.part_ml[2 * slot];
+          lv[i] = p.part_ml[2 * slot + 1];
+          ov[i] = p.part_o[slot * kDecD + d0 + dl];
+        }
+      }
+      float nb = big;
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) nb = fmaxf(nb, mv[i]);
+      const float f0 = __builtin_amdgcn_exp2f(big - nb);
+      lsum *= f0;
+      o *= f0;
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) {
+        const float f = __builtin_amdgcn_exp2f(mv[i] - nb);
+        lsum += f * lv[i];
+        o += f * ov[i];
+      }
+      big = nb;
     }
     const float res = lsum > 0.0f ? o / lsum : 0.0f;
     if (CROSS) {
@@ -496,15 +576,29 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs p) {
 
 }  // namespace
 
+// Workgroups of the split kernel resident at once on MI355X: 256 CUs x 4
+// (the kernel's register use allows four 4-wave groups per CU).
+constexpr int64_t kDecResident = 1024;
+
 void decode_plan(int64_t B, int64_t Hkv, int64_t max_len, int& splits, int& split_len) {
-  const int64_t units = (max_len + kDecUnit - 1) / kDecUnit;
-  int64_t s = 1;
-  // split positions until the grid has about 1024 workgroups, keeping at
-  // least two 128-position units per split
-  while (B * Hkv * s < 1024 && (units + 2 * s - 1) / (2 * s) >= 2) s *= 2;
-  const int64_t per = (units + s - 1) / s;
-  splits = int((units + per - 1) / per);
-  split_len = int(per * kDecUnit);
+  // Choose the split count that minimises (rounds of resident workgroups) x
+  // (steps per wave + one step's worth of per-group overhead); ties go to
+  // fewer splits (less partial traffic).  Splits are whole 32-position steps.
+  const int64_t steps = (max_len + kDecStep - 1) / kDecStep;
+  const int64_t pairs = B * Hkv;
+  int64_t best = 1, best_cost = -1;
+  for (int64_t s = 1; s <= steps && s <= 256; ++s) {
+    const int64_t per = (steps + s - 1) / s;
+    const int64_t rounds = (pairs * s + kDecResident - 1) / kDecResident;
+    const int64_t cost = rounds * ((per + kDecWaves - 1) / kDecWaves + 1);
+    if (best_cost < 0 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  const int64_t per = (steps + best - 1) / best;
+  splits = int((steps + per - 1) / per);
+  split_len = int(per * kDecStep);
 }
 
 int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_len) {
@@ -549,11 +643,12 @@ int launch_kv_decode(const DecodeTensors& t, int64_t B, int64_t Hq, int64_t Hkv,
 
   CombineArgs c{p.part_o, p.part_ml, p.hkv, p.hq, p.group, p.splits, t.out, t.out_f32};
   const dim3 cgrid{unsigned(B), unsigned(kDecD / 16)};
+  const unsigned cthreads = unsigned(std::min<int64_t>(Hq * 16, 1024));
   const size_t lds = cross ? size_t(Hq) * 16 * sizeof(float) : 0;
   if (cross)
-    hipLaunchKernelGGL(decode_combine_kernel<true>, cgrid, dim3(256), lds, stream, c);
+    hipLaunchKernelGGL(decode_combine_kernel<true>, cgrid, dim3(cthreads), lds, stream, c);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<false>, cgrid, dim3(256), 0, stream, c);
+    hipLaunchKernelGGL(decode_combine_kernel<false>, cgrid, dim3(cthreads), 0, stream, c);
   return check_launch("kv_decode combine");
 }
 

@@ -196,6 +196,7 @@ def _dec(lib, **kw):
     (dict(sm=float("nan")), INVALID),
     (dict(max_len=0), INVALID),
     (dict(max_len=513), INVALID),
+    (dict(max_len=(1 << 24) + 1, S_cache=1 << 25), UNSUPPORTED),
     (dict(ssh=-1), INVALID),
     (dict(q=None), INVALID),
     (dict(vs=None), INVALID),
