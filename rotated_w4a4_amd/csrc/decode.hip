@@ -229,6 +229,24 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs
   const int pos_begin = split * p.split_len;
   const int pos_end = min(pos_begin + p.split_len, len);
 
+  // cache buffers over this split's positions [0, pos_end) of the (batch,
+  // KV head) rows; lane offsets of the step loads (see load_step)
+  const int64_t row0 = (int64_t(b) * p.hkv + kv) * p.s_cache;
+  const int nrec = max(pos_end, 0);
+  SplitBuffers bufs;
+  bufs.k = buffer_of(p.kq + row0 * 64, nrec * 64);
+  bufs.v = buffer_of(p.vq + row0 * 64, nrec * 64);
+  bufs.ks = buffer_of(p.ks + row0, nrec * 2);
+  bufs.vs = buffer_of(p.vs + row0, nrec * 2);
+  if (MODE == 1) {
+    bufs.kz = buffer_of(p.kz + row0, nrec * 2);
+    bufs.vz = buffer_of(p.vz + row0, nrec * 2);
+  }
+  const int n = lane & 15, g = lane >> 4;  // also (column, row group a) of D
+  const int voff_k = n * 64 + 16 * g, voff_v = g * 64 + 4 * n, voff_s = 2 * n;
+  int base = pos_begin + kDecStep * wave;
+  StepData<MODE> cur;
+
   // ---- rotate the group's queries: q~ = H_128 diag(s) q / sqrt(128) ------
   {
     const int hh = tid >> 5, c = tid & 31;
@@ -248,6 +266,9 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs
         for (int i = 0; i < 4; ++i) v[i] *= float(sg[i]);
       }
     }
+    // the first step's cache loads go out now, behind the query loads, so
+    // their latency overlaps the rotation
+    if (base < pos_end) load_step<MODE>(cur, bufs, base, voff_k, voff_v, voff_s);
     // element e = 4 c + i: bits 0, 1 in registers, bits 2 .. 6 across lanes
     const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
     v[0] = a0 + a2;
@@ -280,7 +301,6 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs
   }
   __syncthreads();
 
-  const int n = lane & 15, g = lane >> 4;  // also (column, row group a) of D
   // A operands of the score MFMAs: row m = (head m / 2, hi / lo), k-chunk t
   // covers head dims 32 g + 8 t + perm8(s); x16 slots divided by 16
   half8_t a_q[4];
@@ -302,18 +322,6 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) cs[hh] = p.score_mul / q_mul[2 * g + hh];
 
-  const int64_t row0 = (int64_t(b) * p.hkv + kv) * p.s_cache;
-  const int nrec = max(pos_end, 0);
-  SplitBuffers bufs;
-  bufs.k = buffer_of(p.kq + row0 * 64, nrec * 64);
-  bufs.v = buffer_of(p.vq + row0 * 64, nrec * 64);
-  bufs.ks = buffer_of(p.ks + row0, nrec * 2);
-  bufs.vs = buffer_of(p.vs + row0, nrec * 2);
-  if (MODE == 1) {
-    bufs.kz = buffer_of(p.kz + row0, nrec * 2);
-    bufs.vz = buffer_of(p.vz + row0, nrec * 2);
-  }
-  const int voff_k = n * 64 + 16 * g, voff_v = g * 64 + 4 * n, voff_s = 2 * n;
 
   // fp16 offsets subtracted after the nibble -> fp16 step (see nibbles_to_half8)
   const half2_t v_off1 = MODE == 0 ? half2_t{_Float16(1032.0f), _Float16(1032.0f)}
@@ -329,9 +337,6 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs
   for (int j = 0; j < 8; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   uint32_t* wb = wbuf[wave];
 
-  int base = pos_begin + kDecStep * wave;
-  StepData<MODE> cur;
-  if (base < pos_end) load_step<MODE>(cur, bufs, base, voff_k, voff_v, voff_s);
   for (; base < pos_end; base += kDecUnit) {
     StepData<MODE> nxt;
     load_step<MODE>(nxt, bufs, base + kDecUnit, voff_k, voff_v, voff_s);
@@ -498,19 +503,21 @@ struct CombineArgs {
 };
 
 constexpr int kCombineBatch = 8;  // split partials loaded together
+constexpr int kCombineDims = 4;   // head dims per combine block
 
-// Block (b, 16-dim chunk): every query head's 16 outputs, one per thread.
-// Each thread merges its head's splits (loads issued kCombineBatch at a
-// time, so a few memory round trips cover all splits).  With CROSS the
-// Walsh-Hadamard transform over the head index runs in LDS (Sylvester
-// order, normalised by 1 / sqrt(Hq)).
+// Block (b, kCombineDims-dim chunk): every query head's outputs in the
+// chunk, one per thread.  Each thread merges its head's splits (loads issued
+// kCombineBatch at a time, so a few memory round trips cover all splits).
+// With CROSS the Walsh-Hadamard transform over the head index runs in LDS
+// (Sylvester order, normalised by 1 / sqrt(Hq)).
 template <bool CROSS>
 __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
-  extern __shared__ float zs[];  // [Hq][16]
-  const int b = blockIdx.x, d0 = 16 * blockIdx.y;
-  const int total = p.hq * 16;
+  extern __shared__ float zs[];  // [Hq][kCombineDims]
+  constexpr int W = kCombineDims;
+  const int b = blockIdx.x, d0 = W * blockIdx.y;
+  const int total = p.hq * W;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int hq = idx >> 4, dl = idx & 15;
+    const int hq = idx / W, dl = idx % W;
     const int kv = hq / p.group, gi = hq - kv * p.group;
     const int64_t s0 = (int64_t(b) * p.hkv + kv) * p.splits;
     float big = -INFINITY, lsum = 0.0f, o = 0.0f;
@@ -556,17 +563,17 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
   const int half_total = total / 2;
   for (int h = 1; h < p.hq; h <<= 1) {
     for (int idx = threadIdx.x; idx < half_total; idx += blockDim.x) {
-      const int i = idx >> 4, dl = idx & 15;
+      const int i = idx / W, dl = idx % W;
       const int lo = (i / h) * 2 * h + (i % h), hi = lo + h;
-      const float a = zs[lo * 16 + dl], c = zs[hi * 16 + dl];
-      zs[lo * 16 + dl] = a + c;
-      zs[hi * 16 + dl] = a - c;
+      const float a = zs[lo * W + dl], c = zs[hi * W + dl];
+      zs[lo * W + dl] = a + c;
+      zs[hi * W + dl] = a - c;
     }
     __syncthreads();
   }
   const float norm = 1.0f / sqrtf(float(p.hq));
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int hq = idx >> 4, dl = idx & 15;
+    const int hq = idx / W, dl = idx % W;
     const float res = zs[idx] * norm;
     const int64_t at = (int64_t(b) * p.hq + hq) * kDecD + d0 + dl;
     p.out[at] = __float2half_rn(res);
@@ -642,9 +649,9 @@ int launch_kv_decode(const DecodeTensors& t, int64_t B, int64_t Hq, int64_t Hkv,
   if (st != QUAROT_OK) return st;
 
   CombineArgs c{p.part_o, p.part_ml, p.hkv, p.hq, p.group, p.splits, t.out, t.out_f32};
-  const dim3 cgrid{unsigned(B), unsigned(kDecD / 16)};
-  const unsigned cthreads = unsigned(std::min<int64_t>(Hq * 16, 1024));
-  const size_t lds = cross ? size_t(Hq) * 16 * sizeof(float) : 0;
+  const dim3 cgrid{unsigned(B), unsigned(kDecD / kCombineDims)};
+  const unsigned cthreads = unsigned(std::min<int64_t>(Hq * kCombineDims, 1024));
+  const size_t lds = cross ? size_t(Hq) * kCombineDims * sizeof(float) : 0;
   if (cross)
     hipLaunchKernelGGL(decode_combine_kernel<true>, cgrid, dim3(cthreads), lds, stream, c);
   else
