@@ -355,7 +355,7 @@ def bench_kv(args, torch, qr) -> dict:
     }
 
 
-def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows: int = 2) -> dict:
+def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows: int = 4) -> dict:
     """The oracle, as it stands, on `rows` batch rows of the decode step (its
     cache built by the oracle's KV quantiser, untimed)."""
     import oracle

@@ -137,12 +137,26 @@ __device__ __forceinline__ void transpose_nibbles8(uint32_t (&r)[8]) {
   }
 }
 
-__device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
-  v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
-  v = fmaxf(v, dpp_mov<0x122>(v));  // row_ror:2
-  v = fmaxf(v, dpp_mov<0x121>(v));  // row_ror:1
-  return v;
+// Maximum over each row of 16 lanes, for two values at once: each stage is
+// one v_max_f32 with a DPP row rotation on its first operand.  The two chains
+// alternate, and an s_nop 0 between pairs completes the two wait states a
+// DPP read needs after the VALU write of its source.
+__device__ __forceinline__ void row_max16x2(float& a, float& b) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 0\n"
+      "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 0\n"
+      "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_ror:2 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 0\n"
+      "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1"
+      : "+v"(a), "+v"(b));
 }
 
 __device__ __forceinline__ float row_sum16(float v) {
@@ -382,9 +396,11 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_split_kernel(DecodeArgs
     // than kRescaleSlack; the accumulators are rescaled then
     float alpha[2];
     bool moved = false;
+    float mxs[2] = {fmaxf(u[0][0], u[1][0]), fmaxf(u[0][1], u[1][1])};
+    row_max16x2(mxs[0], mxs[1]);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const float mx = row_max16(fmaxf(u[0][hh], u[1][hh]));
+      const float mx = mxs[hh];
       alpha[hh] = 1.0f;
       if (mx > m_run[hh] + kRescaleSlack) {
         alpha[hh] = __builtin_amdgcn_exp2f(m_run[hh] - mx);

@@ -137,19 +137,33 @@ def test_decode_flat_softmax(mode):
 
 
 def test_decode_deterministic_and_workspace_reuse():
+    """Bitwise-identical repeats on one workspace (filled with 0xFF first: its
+    contents on entry do not matter), reused across shapes."""
     cfg = workloads.KV_CONFIG
     B, Hkv, Hq, S = 2, 2, 16, 700
     say(f"determinism B={B} Hkv={Hkv} Hq={Hq} S={S}")
     inp = workloads.make_kv_inputs(cfg, seed=5, batch=B, heads=Hkv, positions=S)
     cache = oracle_cache(inp["k"], inp["v"], inp["signs"], 0)
     q16 = workloads.make_decode_query(workloads.DecodeConfig("t", cfg, Hq), seed=5, batch=B)
-    ws = torch.full((qr.kv_decode_workspace_bytes(B, Hq, Hkv, 128, S),), 0xFF, dtype=torch.uint8,
-                    device="cuda")
+    ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device="cuda")
     args = (dev(q16), dev(inp["signs"]), dev(cache["k_q"]), dev(cache["k_scale"]),
             dev(cache["v_q"]), dev(cache["v_scale"]), S)
     a = host(qr.kv_decode_attention(*args, workspace=ws, cross_head=True)).copy()
     b = host(qr.kv_decode_attention(*args, workspace=ws, cross_head=True))
     np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
+    # a different shape on the same workspace, then the first again
+    say("  workspace reuse across shapes")
+    B2, Hkv2, Hq2, S2 = 3, 4, 4, 300
+    inp2 = workloads.make_kv_inputs(cfg, seed=6, batch=B2, heads=Hkv2, positions=S2)
+    cache2 = oracle_cache(inp2["k"], inp2["v"], inp2["signs"], 0)
+    q2 = workloads.make_decode_query(workloads.DecodeConfig("t", cfg, Hq2), seed=6, batch=B2)
+    out2 = host(qr.kv_decode_attention(dev(q2), dev(inp2["signs"]), dev(cache2["k_q"]),
+                                       dev(cache2["k_scale"]), dev(cache2["v_q"]),
+                                       dev(cache2["v_scale"]), S2, workspace=ws))
+    ref2, mag2 = expected(q2, inp2["signs"], cache2, [S2] * B2, 0, False)
+    check_attention(out2.astype(np.float32), out2, ref2, mag2, tol=1e-3)
+    c = host(qr.kv_decode_attention(*args, workspace=ws, cross_head=True))
+    np.testing.assert_array_equal(a.view(np.uint16), c.view(np.uint16))
 
 
 def test_decode_workload_sampled():
