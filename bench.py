@@ -518,8 +518,10 @@ def counter_means(path: str, counter: str) -> dict:
     return {k: float(np.median(v)) for k, v in acc.items()}
 
 
+# kernel-name fragment -> traffic key; kernels sharing a key (the decode
+# call's split and combine kernels) are summed
 KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant": "kv_had_quant",
-               "decode_split": "kv_decode"}
+               "decode_split": "kv_decode", "decode_combine": "kv_decode"}
 
 
 def summarize_counters(args) -> dict:
@@ -549,9 +551,15 @@ def summarize_counters(args) -> dict:
                         not (k == "had_quant" and "kv_had_quant" in kname)), None)
             if key is None or kname not in w:
                 continue
-            ent[key] = {"kernel": kname.split("(")[0], "source_sha256": source_digest(key),
-                        "fetch_kib": fv, "write_kib": w[kname],
-                        "fetch_bytes": fv * 1024.0 * kf, "write_bytes": w[kname] * 1024.0 * kw}
+            e = ent.setdefault(key, {"kernel": "", "source_sha256": source_digest(key),
+                                     "fetch_kib": 0.0, "write_kib": 0.0,
+                                     "fetch_bytes": 0.0, "write_bytes": 0.0})
+            short = kname.replace("(anonymous namespace)::", "").split("(")[0]
+            e["kernel"] = (e["kernel"] + " + " if e["kernel"] else "") + short
+            e["fetch_kib"] += fv
+            e["write_kib"] += w[kname]
+            e["fetch_bytes"] += fv * 1024.0 * kf
+            e["write_bytes"] += w[kname] * 1024.0 * kw
         out["kernels"][name] = ent
     return out
 
