@@ -7,6 +7,10 @@
   Guide", step 1 of "Deep Dive"): the same R is applied to each output
   channel's row of W [n_out x d] (W~ = W R^T), so X~ W~^T = X W^T; then one
   symmetric scale per output channel (max/7, round to nearest) and pack.
+* RMSNorm producer ("QuaRot Guide", step 2 of "Deep Dive", "Online Activation
+  Rotation Fused into RMSNorm"): the normalised row x / sqrt(mean(x^2) + eps)
+  is rotated and quantised per token.  The RMSNorm gain is absorbed into the
+  next weights (paper-graph-ui summary, Stage 1a), so no gain is applied.
 * KV cache (same page, Stage 1d "online head-wise rotation after RoPE" and
   Stage 2c; "QuaRot Guide", step 4 of "Deep Dive"): each (batch, head,
   position) vector of head_dim values is rotated by the head-wise Hadamard and
@@ -23,7 +27,8 @@ from .gemm import w4a4_reference
 from .quant import pack_int4, pack_uint4, quantize_rows, quantize_rows_asym
 from .rotate import rotate_rows
 
-__all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant", "kv_had_quant_asym"]
+__all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant", "kv_had_quant_asym",
+           "rmsnorm", "rmsnorm_had_quant"]
 
 
 def had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0):
@@ -84,3 +89,16 @@ def kv_had_quant_asym(t: np.ndarray, signs: np.ndarray, clip_ratio: float = 0.95
         "scales": scales.reshape(b, h, s),
         "zeros": zeros.reshape(b, h, s),
     }
+
+
+def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
+    """Row-wise x / sqrt(mean(x^2) + eps) in float64 (gain absorbed: none)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return x / np.sqrt(ms + eps)
+
+
+def rmsnorm_had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0,
+                      eps: float = 1e-5):
+    """RMSNorm, then rotate+quant: had_quant(rmsnorm(x, eps))."""
+    return had_quant(rmsnorm(x, eps), signs, m, clip_ratio)
