@@ -69,6 +69,8 @@ def parse_args():
                    choices=sorted(workloads.DECODE_CONFIGS))
     p.add_argument("--no-cross-head", action="store_true",
                    help="with --decode: leave out the cross-head transform")
+    p.add_argument("--rmsnorm", action="store_true",
+                   help="with an activation workload: the RMSNorm-fused rotate+quant")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for 1 GiB)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -205,10 +207,18 @@ def bench_act(args, torch, qr) -> dict:
             "y": torch.empty((T, N), dtype=torch.float16, device="cuda"),
         })
     stream = torch.cuda.current_stream()
+    rms = args.rmsnorm
+
+    def rotate_quant(s):
+        if rms:
+            qr.rmsnorm_had_quant(s["x"], 1e-5, signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"],
+                                 stream=stream)
+        else:
+            qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
 
     def step(i):
         s = sets[i % nsets]
-        qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
+        rotate_quant(s)
         qr.w4a4_gemm(s["qx"], s["sx"], s["qw"], s["sw"], d, out=s["y"], stream=stream)
 
     for i in range(args.warmup):
@@ -227,8 +237,7 @@ def bench_act(args, torch, qr) -> dict:
     # between two events, behind a spin kernel so the host has queued them
     # all before the first starts.
     def launch_rq(i):
-        s = sets[i % nsets]
-        qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
+        rotate_quant(sets[i % nsets])
 
     def launch_gemm(i):
         s = sets[i % nsets]
@@ -258,7 +267,8 @@ def bench_act(args, torch, qr) -> dict:
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: X fp16 [{T} x {d}] with {cfg.outlier_count} outlier "
-                        f"channels, rotation H_{d // cfg.m}" + (f" (x) H_{cfg.m}" if cfg.m > 1 else "")
+                        f"channels, " + ("RMSNorm (eps 1e-5, gain absorbed) fused, " if rms else "")
+                        + f"rotation H_{d // cfg.m}" + (f" (x) H_{cfg.m}" if cfg.m > 1 else "")
                         + f" with random signs, W int4 [{N} x {d}], Y fp16 [{T} x {N}]",
             "tokens": T, "d": d, "n_out": N, "buffer_sets": nsets,
         },
@@ -274,13 +284,13 @@ def bench_act(args, torch, qr) -> dict:
             "note": "integer ops (TOPS) against the dense INT8 MFMA peak; 2*M*N*K per launch",
         },
         "roofline_rotate_quant": {
-            "kernel": "had_quant",
+            "kernel": "rmsnorm_had_quant" if rms else "had_quant",
             "bound": "hbm",
             "achieved": round(rq_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg.name, "had_quant"),
+            "traffic": measured_traffic(cfg.name + ("_rmsnorm" if rms else ""), "had_quant"),
             "algorithmic_bytes": rq_bytes,
         },
     }

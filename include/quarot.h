@@ -82,6 +82,26 @@ int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
                      float* x_rot_out, void* stream);
 
 /*
+ * RMSNorm fused into rotate+quant: each row is first normalised,
+ * y = x / sqrt(mean(x^2) + eps), then rotated and quantised exactly as
+ * quarot_had_quant does with y in place of x.
+ *
+ * Follows [G] step 2 of "Deep Dive" (the online rotation fused into the
+ * RMSNorm kernel: normalise, rotate in registers, quantise per token); the
+ * RMSNorm gain is absorbed into the next weights ([S] §3.4 Stage 1a), so no
+ * gain is applied.  The rotation keeps the norm, so the kernels take
+ * mean(x^2) from the rotated values and fold 1 / sqrt(mean + eps) into the
+ * scale and codes; x_rot_out (optional) receives R y.
+ *
+ * Arguments as quarot_had_quant, plus eps (finite, > 0).
+ * Errors: as quarot_had_quant; INVALID for a bad eps.
+ */
+int quarot_rmsnorm_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x, float eps,
+                             const int8_t* signs, int32_t m, float clip_ratio,
+                             uint8_t* q_out, int64_t ld_q, void* scale_out,
+                             float* x_rot_out, void* stream);
+
+/*
  * W4A4 GEMM with INT32 accumulation and the per-token x per-channel dequant.
  *
  * Follows [S] section 3.4 Stage 2b (dequantised output

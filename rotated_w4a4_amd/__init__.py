@@ -9,6 +9,8 @@ step of the computation runs in the HIP kernels; there is no fallback.
 Calls (same names as the C entry points, without the ``quarot_`` prefix):
 
 * ``had_quant(x, signs, m, clip_ratio)``   -> (codes uint8 [rows, d/2], scales fp16 [rows])
+* ``rmsnorm_had_quant(x, eps, signs, m, clip_ratio)`` -> (codes, scales) of
+  the RMS-normalised rows
 * ``w4a4_gemm(a_q, a_scale, b_q, b_scale, k)`` -> fp16 [M, N]
 * ``kv_had_quant(k, v, signs, k_cache, k_scale, v_cache, v_scale, pos0)``
 * ``kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len)``
@@ -21,7 +23,9 @@ memory and streams only.
 """
 
 from ._lib import (QuarotError, had_quant, hadamard_factor, kv_decode_attention,
-                   kv_decode_workspace_bytes, kv_had_quant, lib, library_path, w4a4_gemm)
+                   kv_decode_workspace_bytes, kv_had_quant, lib, library_path,
+                   rmsnorm_had_quant, w4a4_gemm)
 
 __all__ = ["QuarotError", "had_quant", "hadamard_factor", "kv_decode_attention",
-           "kv_decode_workspace_bytes", "kv_had_quant", "lib", "library_path", "w4a4_gemm"]
+           "kv_decode_workspace_bytes", "kv_had_quant", "lib", "library_path",
+           "rmsnorm_had_quant", "w4a4_gemm"]

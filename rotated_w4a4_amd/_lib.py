@@ -20,6 +20,8 @@ _f32 = ctypes.c_float
 _SIGNATURES = {
     "quarot_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _f32,
                                         _vp, _i64, _vp, _vp, _vp]),
+    "quarot_rmsnorm_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _f32, _vp, _i32, _f32,
+                                                _vp, _i64, _vp, _vp, _vp]),
     "quarot_w4a4_gemm": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                                         _vp, _i64, _vp, _i64, _vp]),
     "quarot_kv_had_quant": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -105,9 +107,7 @@ def hadamard_factor(m: int) -> np.ndarray:
     return out
 
 
-def had_quant(x, signs=None, m: int = 1, clip_ratio: float = 1.0, q_out=None, scale_out=None,
-              x_rot_out=None, stream=None):
-    """Rotate+quant rows of fp16 x [rows, d]; returns (codes, scales)."""
+def _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out):
     torch = _torch()
     _need(x, torch.float16, "x", 2)
     if x.stride(1) != 1:
@@ -129,10 +129,29 @@ def had_quant(x, signs=None, m: int = 1, clip_ratio: float = 1.0, q_out=None, sc
             raise ValueError("x_rot_out must be contiguous float32 [rows, d]")
     if q_out.stride(1) != 1 or q_out.shape[0] != rows or scale_out.shape[0] != rows:
         raise ValueError("bad output shapes")
+    return rows, d, q_out, scale_out
+
+
+def had_quant(x, signs=None, m: int = 1, clip_ratio: float = 1.0, q_out=None, scale_out=None,
+              x_rot_out=None, stream=None):
+    """Rotate+quant rows of fp16 x [rows, d]; returns (codes, scales)."""
+    rows, d, q_out, scale_out = _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out)
     st = lib().quarot_had_quant(_ptr(x), rows, d, x.stride(0), _ptr(signs), m,
                                 float(clip_ratio), _ptr(q_out), q_out.stride(0),
                                 _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
     _check("quarot_had_quant", st)
+    return q_out, scale_out
+
+
+def rmsnorm_had_quant(x, eps: float = 1e-5, signs=None, m: int = 1, clip_ratio: float = 1.0,
+                      q_out=None, scale_out=None, x_rot_out=None, stream=None):
+    """RMSNorm (gain absorbed) then rotate+quant of rows of fp16 x [rows, d];
+    returns (codes, scales)."""
+    rows, d, q_out, scale_out = _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out)
+    st = lib().quarot_rmsnorm_had_quant(_ptr(x), rows, d, x.stride(0), float(eps), _ptr(signs),
+                                        m, float(clip_ratio), _ptr(q_out), q_out.stride(0),
+                                        _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
+    _check("quarot_rmsnorm_had_quant", st)
     return q_out, scale_out
 
 

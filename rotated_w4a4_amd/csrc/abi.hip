@@ -75,11 +75,11 @@ int quarot_hadamard_factor(int32_t m, int8_t* out_host) {
   }
 }
 
-int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
-                     const int8_t* signs, int32_t m, float clip_ratio,
-                     uint8_t* q_out, int64_t ld_q, void* scale_out,
-                     float* x_rot_out, void* stream) {
-  clear_error();
+namespace {
+
+int had_quant_checked(const void* x, int64_t rows, int64_t d, int64_t ld_x, const int8_t* signs,
+                      int32_t m, float clip_ratio, uint8_t* q_out, int64_t ld_q, void* scale_out,
+                      float* x_rot_out, float rms_eps, void* stream) {
   QR_CHECK_ARG(rows >= 0, QUAROT_ERR_INVALID, "rows = %lld < 0", (long long)rows);
   QR_CHECK_ARG(d > 0, QUAROT_ERR_INVALID, "d = %lld <= 0", (long long)d);
   QR_CHECK_ARG(clip_ok(clip_ratio), QUAROT_ERR_INVALID, "clip_ratio must be in (0, 1]");
@@ -104,7 +104,28 @@ int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
   const int n = log2_exact(d / m);
   return launch_had_quant(static_cast<const __half*>(x), rows, int(d), n, m, ld_x, signs,
                           clip_ratio, q_out, ld_q, static_cast<__half*>(scale_out), x_rot_out,
-                          static_cast<hipStream_t>(stream));
+                          rms_eps, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
+                     const int8_t* signs, int32_t m, float clip_ratio,
+                     uint8_t* q_out, int64_t ld_q, void* scale_out,
+                     float* x_rot_out, void* stream) {
+  clear_error();
+  return had_quant_checked(x, rows, d, ld_x, signs, m, clip_ratio, q_out, ld_q, scale_out,
+                           x_rot_out, -1.0f, stream);
+}
+
+int quarot_rmsnorm_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x, float eps,
+                             const int8_t* signs, int32_t m, float clip_ratio,
+                             uint8_t* q_out, int64_t ld_q, void* scale_out,
+                             float* x_rot_out, void* stream) {
+  clear_error();
+  QR_CHECK_ARG(eps > 0.0f && eps < INFINITY, QUAROT_ERR_INVALID, "eps must be finite and > 0");
+  return had_quant_checked(x, rows, d, ld_x, signs, m, clip_ratio, q_out, ld_q, scale_out,
+                           x_rot_out, eps, stream);
 }
 
 int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,

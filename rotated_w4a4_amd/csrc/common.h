@@ -156,9 +156,11 @@ static_assert(had_factor_ok<28>(), "H_28 is not Hadamard");
 // ---------------------------------------------------------------------------
 // Kernel launchers (one per .hip file); arguments already validated.
 // ---------------------------------------------------------------------------
+// rms_eps < 0: plain rotate+quant; rms_eps >= 0: each row is first divided
+// by sqrt(mean(x^2) + rms_eps).
 int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t ld_x,
                      const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
-                     __half* scale_out, float* x_rot_out, hipStream_t stream);
+                     __half* scale_out, float* x_rot_out, float rms_eps, hipStream_t stream);
 
 int launch_w4a4_gemm(const uint8_t* a_q, int64_t lda, const __half* a_scale,
                      const uint8_t* b_q, int64_t ldb, const __half* b_scale,

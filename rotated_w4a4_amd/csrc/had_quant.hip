@@ -30,11 +30,11 @@ namespace {
 
 constexpr int kQuadBlock = 256;  // 64 rows per block iteration
 
-template <int D, bool CLAMP>
+template <int D, bool CLAMP, bool RMS>
 __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
-    float* __restrict__ x_rot) {
+    float* __restrict__ x_rot, float rms_eps) {
   constexpr int NC = D / 32;
   const int lane_q = threadIdx.x & 3;
   uint4 mask[NC];
@@ -48,8 +48,9 @@ __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     const int64_t rr = active ? r : 0;
     uint4 raw[NC];
     quad_load<D>(x + rr * ld_x, lane_q, raw);
-    quad_row<D, CLAMP>(raw, q_out + rr * ld_q, scale_out + rr, x_rot ? x_rot + rr * D : nullptr,
-                       mask, lane_q, clip_ratio, active);
+    quad_row<D, CLAMP, RMS>(raw, q_out + rr * ld_q, scale_out + rr,
+                            x_rot ? x_rot + rr * D : nullptr, mask, lane_q, clip_ratio, active,
+                            rms_eps);
   }
 }
 
@@ -112,13 +113,14 @@ __device__ __forceinline__ void fwht_pass(float* buf, int n, int s) {
   }
 }
 
-template <int M>
+template <int M, bool RMS>
 __global__ __launch_bounds__(kLdsBlock) void had_quant_lds(
     const __half* __restrict__ x, int64_t rows, int d, int n, int64_t ld_x,
     const int8_t* __restrict__ signs, float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q,
-    __half* __restrict__ scale_out, float* __restrict__ x_rot, float norm) {
+    __half* __restrict__ scale_out, float* __restrict__ x_rot, float norm, float rms_eps) {
   extern __shared__ float buf[];
   __shared__ float red[kLdsBlock / 64];
+  __shared__ float red_ss[kLdsBlock / 64];
   const int chunks = d / 8;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const __half* src = x + row * ld_x;
@@ -154,24 +156,39 @@ __global__ __launch_bounds__(kLdsBlock) void had_quant_lds(
       __syncthreads();
     }
     // 4. row absmax
-    float amax = 0.0f;
+    float amax = 0.0f, ss = 0.0f;
     for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(buf[pidx(8 * c + i)] * norm));
+      for (int i = 0; i < 8; ++i) {
+        const float y = buf[pidx(8 * c + i)] * norm;
+        amax = fmaxf(amax, fabsf(y));
+        if (RMS) ss = fmaf(y, y, ss);
+      }
     }
     amax = wave_max(amax);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    if (RMS) ss = wave_sum_dpp(ss);
+    if ((threadIdx.x & 63) == 0) {
+      red[threadIdx.x >> 6] = amax;
+      if (RMS) red_ss[threadIdx.x >> 6] = ss;
+    }
     __syncthreads();
     amax = red[0];
     for (int w = 1; w < int(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
-    const __half s16 = row_scale_fp16(amax, clip_ratio);
+    // RMS: normalise by 1 / sqrt(mean(x^2) + eps); the rotation keeps the norm
+    float rs = 1.0f;
+    if (RMS) {
+      float tot = 0.0f;
+      for (int w = 0; w < int(blockDim.x >> 6); ++w) tot += red_ss[w];
+      rs = rsqrtf(tot / float(d) + rms_eps);
+    }
+    const __half s16 = row_scale_fp16(amax * rs, clip_ratio);
     const float k = inv_scale(s16);
     // 5. quantise, pack, store
     uint8_t* qrow = q_out + row * ld_q;
     for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
       float f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = buf[pidx(8 * c + i)] * norm;
+      for (int i = 0; i < 8; ++i) f[i] = buf[pidx(8 * c + i)] * (norm * rs);
       *reinterpret_cast<uint32_t*>(qrow + 4 * c) = pack8(f, k);
       if (x_rot) {
         float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(d) + 8 * c);
@@ -199,24 +216,34 @@ int sm_count_cached() {
 
 int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t ld_x,
                      const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
-                     __half* scale_out, float* x_rot_out, hipStream_t stream) {
+                     __half* scale_out, float* x_rot_out, float rms_eps, hipStream_t stream) {
   const int cus = sm_count_cached();
+  const bool rms = rms_eps >= 0.0f;  // normalise each row by its RMS first
+  const bool clamp = clip_ratio != 1.0f;
   if (m == 1 && d <= 256) {
     const int64_t rpb = kQuadBlock / 4;
     int64_t blocks = (rows + rpb - 1) / rpb;
     const int64_t cap = int64_t(1) << 24;  // grid limit; beyond it blocks loop
     if (blocks > cap) blocks = cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kQuadBlock)};
-#define QR_QUAD(DD, CL)                                                                 \
-  hipLaunchKernelGGL((had_quant_quad<DD, CL>), grid, block, 0, stream, x, rows, ld_x, signs, \
-                     clip_ratio, q_out, ld_q, scale_out, x_rot_out)
-    const bool clamp = clip_ratio != 1.0f;
+#define QR_QUAD(DD, CL, RM)                                                                    \
+  hipLaunchKernelGGL((had_quant_quad<DD, CL, RM>), grid, block, 0, stream, x, rows, ld_x, signs, \
+                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, rms_eps)
+#define QR_QUAD_D(DD)                   \
+  if (rms) {                            \
+    if (clamp) QR_QUAD(DD, true, true); \
+    else QR_QUAD(DD, false, true);      \
+  } else {                              \
+    if (clamp) QR_QUAD(DD, true, false); \
+    else QR_QUAD(DD, false, false);     \
+  }
     switch (d) {
-      case 32: if (clamp) QR_QUAD(32, true); else QR_QUAD(32, false); break;
-      case 64: if (clamp) QR_QUAD(64, true); else QR_QUAD(64, false); break;
-      case 128: if (clamp) QR_QUAD(128, true); else QR_QUAD(128, false); break;
-      default: if (clamp) QR_QUAD(256, true); else QR_QUAD(256, false); break;
+      case 32: QR_QUAD_D(32); break;
+      case 64: QR_QUAD_D(64); break;
+      case 128: QR_QUAD_D(128); break;
+      default: QR_QUAD_D(256); break;
     }
+#undef QR_QUAD_D
 #undef QR_QUAD
     return check_launch("had_quant_quad");
   }
@@ -224,29 +251,33 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
     const int64_t cap = int64_t(cus) * 8;  // 16 KiB LDS, two waves per block
     const int64_t blocks = rows < cap ? rows : cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kSplitBlock)};
-    if (clip_ratio == 1.0f)
-      hipLaunchKernelGGL(had_quant_4096_split<false>, grid, block, 0, stream, x, rows, ld_x, signs,
-                         clip_ratio, q_out, ld_q, scale_out, x_rot_out);
-    else
-      hipLaunchKernelGGL(had_quant_4096_split<true>, grid, block, 0, stream, x, rows, ld_x, signs,
-                         clip_ratio, q_out, ld_q, scale_out, x_rot_out);
+#define QR_SPLIT(CL, RM)                                                                       \
+  hipLaunchKernelGGL((had_quant_4096_split<CL, RM>), grid, block, 0, stream, x, rows, ld_x, signs, \
+                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, rms_eps)
+    if (rms) {
+      if (clamp) QR_SPLIT(true, true); else QR_SPLIT(false, true);
+    } else {
+      if (clamp) QR_SPLIT(true, false); else QR_SPLIT(false, false);
+    }
+#undef QR_SPLIT
     return check_launch("had_quant_4096_split");
   }
   if ((m == 12 || m == 28) && d == 1024 * m) {
     static const bool kron_attr_ok = [] {
       bool ok = true;
-      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<12, false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                KronCfg<12>::LDS_BYTES) == hipSuccess;
-      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<12, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                KronCfg<12>::LDS_BYTES) == hipSuccess;
-      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<28, false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                KronCfg<28>::LDS_BYTES) == hipSuccess;
-      ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<28, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                KronCfg<28>::LDS_BYTES) == hipSuccess;
+#define QR_ATTR(MM, CL, RM)                                                                  \
+  ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<MM, CL, RM>),       \
+                            hipFuncAttributeMaxDynamicSharedMemorySize,                      \
+                            KronCfg<MM>::LDS_BYTES) == hipSuccess
+      QR_ATTR(12, false, false);
+      QR_ATTR(12, true, false);
+      QR_ATTR(12, false, true);
+      QR_ATTR(12, true, true);
+      QR_ATTR(28, false, false);
+      QR_ATTR(28, true, false);
+      QR_ATTR(28, false, true);
+      QR_ATTR(28, true, true);
+#undef QR_ATTR
       return ok;
     }();
     if (!kron_attr_ok) {
@@ -258,29 +289,41 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
     const int64_t blocks = rows < cap ? rows : cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kKronBlock)};
     const float norm = 1.0f / sqrtf(float(d));
-    const bool clamp = clip_ratio != 1.0f;
-#define QR_KRON(MM, CL)                                                                      \
-  hipLaunchKernelGGL((had_quant_kron<MM, CL>), grid, block, lds, stream, x, rows, ld_x, signs, \
-                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm)
+#define QR_KRON(MM, CL, RM)                                                                     \
+  hipLaunchKernelGGL((had_quant_kron<MM, CL, RM>), grid, block, lds, stream, x, rows, ld_x, signs, \
+                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm, rms_eps)
+#define QR_KRON_M(MM)                    \
+  if (rms) {                             \
+    if (clamp) QR_KRON(MM, true, true);  \
+    else QR_KRON(MM, false, true);       \
+  } else {                               \
+    if (clamp) QR_KRON(MM, true, false); \
+    else QR_KRON(MM, false, false);      \
+  }
     if (m == 12) {
-      if (clamp) QR_KRON(12, true); else QR_KRON(12, false);
+      QR_KRON_M(12);
     } else {
-      if (clamp) QR_KRON(28, true); else QR_KRON(28, false);
+      QR_KRON_M(28);
     }
+#undef QR_KRON_M
 #undef QR_KRON
     return check_launch("had_quant_kron");
   }
   const size_t lds = size_t(d + d / 32) * sizeof(float);
-  // rows above 16K elements need more than the default 64 KiB of dynamic LDS
+  // the generic kernel stages up to 32768 + 1024 floats (132 KiB) in LDS
   static const bool lds_attr_ok = [] {
     const int bytes = (32768 + 1024) * int(sizeof(float));
     bool ok = true;
-    ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<1>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
-    ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<12>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
-    ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<28>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
+#define QR_ATTR(MM, RM)                                                                       \
+  ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<MM, RM>),             \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess
+    QR_ATTR(1, false);
+    QR_ATTR(12, false);
+    QR_ATTR(28, false);
+    QR_ATTR(1, true);
+    QR_ATTR(12, true);
+    QR_ATTR(28, true);
+#undef QR_ATTR
     return ok;
   }();
   if (!lds_attr_ok && lds > 65536) {
@@ -291,17 +334,21 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
   int64_t blocks = rows < int64_t(cus) * per_cu ? rows : int64_t(cus) * per_cu;
   const dim3 grid{unsigned(blocks)}, block{unsigned(kLdsBlock)};
   const float norm = 1.0f / sqrtf(float(d));
+#define QR_LDS(MM, RM)                                                                         \
+  hipLaunchKernelGGL((had_quant_lds<MM, RM>), grid, block, lds, stream, x, rows, d, n, ld_x,   \
+                     signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm, rms_eps)
   switch (m) {
     case 1:
-      hipLaunchKernelGGL(had_quant_lds<1>, grid, block, lds, stream, x, rows, d, n, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm);
+      if (rms) QR_LDS(1, true); else QR_LDS(1, false);
       break;
     case 12:
-      hipLaunchKernelGGL(had_quant_lds<12>, grid, block, lds, stream, x, rows, d, n, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm);
+      if (rms) QR_LDS(12, true); else QR_LDS(12, false);
       break;
     default:
-      hipLaunchKernelGGL(had_quant_lds<28>, grid, block, lds, stream, x, rows, d, n, ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm);
+      if (rms) QR_LDS(28, true); else QR_LDS(28, false);
       break;
   }
+#undef QR_LDS
   return check_launch("had_quant_lds");
 }
 

@@ -117,15 +117,19 @@ struct KronCfg {
   static_assert(TASKS <= kKronBlock, "one phase-2 task per thread");
 };
 
-template <int M, bool CLAMP>
+// RMS: the row is normalised by 1 / sqrt(mean(x^2) + rms_eps) first (the
+// rotation fused into RMSNorm, gain absorbed); the factor comes from the
+// rotated values (the rotation keeps the norm) and scales the quantiser.
+template <int M, bool CLAMP, bool RMS>
 __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
-    float* __restrict__ x_rot, float norm) {
+    float* __restrict__ x_rot, float norm, float rms_eps) {
   using C = KronCfg<M>;
   extern __shared__ float4 kron_lds[];  // the row in fp32 (phase 1 -> phase 2), then its codes
   float* buf = reinterpret_cast<float*>(kron_lds);
   __shared__ float red[kKronBlock / 64];
+  __shared__ float red_ss[kKronBlock / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     }
     __syncthreads();
     // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
-    float amax = 0.0f;
+    float amax = 0.0f, ss = 0.0f;
     if (task_on) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -270,17 +274,31 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
             v[r + h] = a - b;
           }
 #pragma unroll
-      for (int r = 0; r < 64; ++r) amax = fmaxf(amax, fabsf(v[r]));
+      for (int r = 0; r < 64; ++r) {
+        amax = fmaxf(amax, fabsf(v[r]));
+        if (RMS) ss = fmaf(v[r], v[r], ss);
+      }
     }
     amax = wave_max_dpp(amax);
-    if (lane == 0) red[wave] = amax;
+    if (RMS) ss = wave_sum_dpp(ss);
+    if (lane == 0) {
+      red[wave] = amax;
+      if (RMS) red_ss[wave] = ss;
+    }
     __syncthreads();  // phase-2 reads of buf are done; red is complete
     amax = red[0];
 #pragma unroll
     for (int w = 1; w < kKronBlock / 64; ++w) amax = fmaxf(amax, red[w]);
-    const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
-    const float kq = inv_scale(s16) * norm * sigma;
-    const float xnorm = norm * sigma;
+    float rs = 1.0f;
+    if (RMS) {
+      float tot = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kKronBlock / 64; ++w) tot += red_ss[w];
+      rs = rsqrtf(tot * (norm * norm / float(C::D)) + rms_eps);  // mean(x^2) = sum(v^2) / d^2
+    }
+    const __half s16 = row_scale_fp16(amax * norm * rs, clip_ratio);
+    const float kq = inv_scale(s16) * norm * rs * sigma;
+    const float xnorm = norm * rs * sigma;
     uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
     if (task_on) {
 #pragma unroll

@@ -143,26 +143,46 @@ __device__ __forceinline__ float quad_sigma(int q) {
 // Rotate+quant (symmetric) of one row held by a quad, its raw chunks already
 // loaded.  qrow: code row (D/2 bytes); scale: where the fp16 scale goes;
 // xrot: optional fp32 row.
-template <int D, bool CLAMP>
+template <int LB>
+__device__ __forceinline__ float quad_sum(float v) {
+  constexpr int ctrl = (LB == 0) ? 0xB1 : 0x4E;
+  return v + __builtin_bit_cast(
+                 float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+}
+
+// With RMS the row is first normalised by 1 / sqrt(mean(x^2) + rms_eps)
+// ("QuaRot Guide", step 2 of "Deep Dive": the rotation fused into RMSNorm,
+// its gain absorbed into the next weights).  The rotation keeps the norm, so
+// the factor comes from the rotated values and scales the quantiser.
+template <int D, bool CLAMP, bool RMS = false>
 __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __restrict__ qrow,
                                          __half* __restrict__ scale, float* __restrict__ xrot,
                                          const uint4 (&mask)[D / 32], int q, float clip_ratio,
-                                         bool active) {
+                                         bool active, float rms_eps = 0.0f) {
   constexpr int NC = D / 32;
   constexpr int E = 8 * NC;
   constexpr float kNorm = quad_norm<D>();
   float v[E];
   quad_transform<D>(raw, mask, q, active, v);
   // the transform is unnormalised: max|x~| = max|v| / sqrt(D)
-  float amax = 0.0f;
+  float amax = 0.0f, ss = 0.0f;
 #pragma unroll
-  for (int r = 0; r < E; ++r) amax = fmaxf(amax, fabsf(v[r]));
+  for (int r = 0; r < E; ++r) {
+    amax = fmaxf(amax, fabsf(v[r]));
+    if (RMS) ss = fmaf(v[r], v[r], ss);
+  }
   amax = quad_max<0>(amax);
   amax = quad_max<1>(amax);
-  const __half s16 = row_scale_fp16(amax * kNorm, clip_ratio);
+  float rs = 1.0f;
+  if (RMS) {
+    ss = quad_sum<0>(ss);
+    ss = quad_sum<1>(ss);
+    rs = rsqrtf(ss * (kNorm * kNorm / float(D)) + rms_eps);
+  }
+  const __half s16 = row_scale_fp16(amax * kNorm * rs, clip_ratio);
   if (!active) return;
   const float sigma = quad_sigma(q);
-  const float kq = inv_scale(s16) * kNorm * sigma;
+  const float kq = inv_scale(s16) * kNorm * rs * sigma;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     float t8[8];
@@ -177,7 +197,7 @@ __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __
   }
   if (q == 0) *scale = s16;
   if (xrot) {
-    const float xn = kNorm * sigma;
+    const float xn = kNorm * rs * sigma;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       float4* dst = reinterpret_cast<float4*>(xrot + 8 * (q + 4 * j));

@@ -26,6 +26,16 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<kDppQuadX1>(v);
+  v += dpp_mov<kDppQuadX2>(v);
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 

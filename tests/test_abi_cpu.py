@@ -226,3 +226,30 @@ def test_decode_workspace_size(lib):
     assert lib.quarot_kv_decode_workspace_bytes(1, 8, 1, 128, 0) == INVALID
     sizes = [lib.quarot_kv_decode_workspace_bytes(2, 8, 2, 128, n) for n in range(1, 3000, 37)]
     assert all(s > 0 for s in sizes)
+
+
+def _rms(lib, **kw):
+    a = dict(x=FAKE, rows=4, d=256, ld_x=256, eps=1e-5, signs=None, m=1, clip=1.0, q=FAKE,
+             ld_q=128, s=FAKE, xr=None)
+    a.update(kw)
+    return lib.quarot_rmsnorm_had_quant(a["x"], a["rows"], a["d"], a["ld_x"], a["eps"], a["signs"],
+                                        a["m"], a["clip"], a["q"], a["ld_q"], a["s"], a["xr"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(eps=0.0), INVALID),
+    (dict(eps=-1e-5), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(eps=float("inf")), INVALID),
+    (dict(d=100), UNSUPPORTED),
+    (dict(m=5), UNSUPPORTED),
+    (dict(clip=1.5), INVALID),
+    (dict(x=None), INVALID),
+    (dict(x=FAKE + 2), MISALIGNED),
+])
+def test_rmsnorm_had_quant_rejects(lib, kw, status):
+    assert _rms(lib, **kw) == status
+
+
+def test_rmsnorm_had_quant_zero_rows_is_noop(lib):
+    assert _rms(lib, rows=0, x=None, q=None, s=None) == OK
