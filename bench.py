@@ -514,9 +514,10 @@ def calibrate_copy(torch) -> dict:
     return {"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": 5}
 
 
-def counter_means(path: str, counter: str) -> dict:
-    """Median of one counter per kernel name in a rocprofv3 counter CSV (the
-    median drops the one-off launches, e.g. the weight preparation)."""
+def counter_means(path: str, counter: str, min_dispatches: int = 3) -> dict:
+    """Median of one counter per kernel name in a rocprofv3 counter CSV.
+    Kernels dispatched fewer than `min_dispatches` times (one-off launches
+    such as the weight preparation) are left out."""
     import csv
 
     acc = {}
@@ -525,7 +526,7 @@ def counter_means(path: str, counter: str) -> dict:
             if r["Counter_Name"] != counter:
                 continue
             acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    return {k: float(np.median(v)) for k, v in acc.items()}
+    return {k: float(np.median(v)) for k, v in acc.items() if len(v) >= min_dispatches}
 
 
 # kernel-name fragment -> traffic key; kernels sharing a key (the decode
@@ -541,8 +542,8 @@ def summarize_counters(args) -> dict:
     (CSV paths).  FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by
     the ratio of known bytes to what the same counter reads for the plain
     copy kernel of the calibration run."""
-    cal_f = counter_means(args.traffic_from[0], "FETCH_SIZE")
-    cal_w = counter_means(args.traffic_from[1], "WRITE_SIZE")
+    cal_f = counter_means(args.traffic_from[0], "FETCH_SIZE", 1)
+    cal_w = counter_means(args.traffic_from[1], "WRITE_SIZE", 1)
     copy_f = max(v for k, v in cal_f.items() if "copy" in k.lower())
     copy_w = max(v for k, v in cal_w.items() if "copy" in k.lower())
     kf = COPY_BYTES / (copy_f * 1024.0)
