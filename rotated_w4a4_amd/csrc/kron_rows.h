@@ -19,11 +19,12 @@
 //            lands as b = 4 g + (0..3) and 16 + 4 g + (0..3).  Butterflies
 //            over a4-a6 (tile t) run in registers, over a0, a1, a3 (lane bits
 //            0, 1, 3) through DPP.  Valid outputs go to LDS as fp32.
-//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of four
-//            consecutive b.  The task reads the 16 values of a2, a7, a8, a9
-//            (float4 each), runs those four butterfly stages in registers,
-//            joins the workgroup maximum, quantises and writes 16-bit code
-//            units to LDS; the row's codes then leave in 16-byte stores.
+//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of BW
+//            consecutive b (4, or 2 for m = 12).  The task reads the 16
+//            values of a2, a7, a8, a9 (a float4 or float2 each), runs those
+//            four butterfly stages in registers, joins the workgroup maximum,
+//            quantises and writes 16- or 8-bit code units to LDS; the row's
+//            codes then leave in 16-byte stores.
 #pragma once
 
 #include "wave_rows.h"
@@ -109,11 +110,14 @@ __device__ __forceinline__ void dpp_fmac_stage(float (&v)[64], float c) {
 template <int M>
 struct KronCfg {
   static constexpr int D = 1024 * M;
-  static constexpr int UNITS = M / 4;       // runs of 4 consecutive b per group
+  // b per phase-2 task: 4 for m = 28 (448 tasks), 2 for m = 12 (384 tasks
+  // rather than 192, so six of the eight waves share phase 2)
+  static constexpr int BW = (M == 12) ? 2 : 4;
+  static constexpr int UNITS = M / BW;      // runs of BW consecutive b per group
   static constexpr int TASKS = 64 * UNITS;  // phase-2 tasks per row
   static constexpr int HALVES = (M > 16) ? 2 : 1;
   static constexpr int LDS_BYTES = D * 4 + D / 2;  // fp32 row, then its codes
-  static_assert(M % 4 == 0 && M <= 32, "m must be a multiple of 4 up to 32");
+  static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
   static_assert(TASKS <= kKronBlock, "one phase-2 task per thread");
 };
 
@@ -253,28 +257,36 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     }
     __syncthreads();
     // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
+    // register r = BW q + i holds b = BW unit + i of group a(q)
+    constexpr int BW = C::BW;
     float amax = 0.0f, ss = 0.0f;
     if (task_on) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int a = kron_row(abase + ((q & 1) << 2) + ((q >> 1) << 7));
-        const float4 f = *reinterpret_cast<const float4*>(buf + a * M + 4 * unit);
-        v[4 * q] = f.x;
-        v[4 * q + 1] = f.y;
-        v[4 * q + 2] = f.z;
-        v[4 * q + 3] = f.w;
+        if (BW == 4) {
+          const float4 f = *reinterpret_cast<const float4*>(buf + a * M + 4 * unit);
+          v[4 * q] = f.x;
+          v[4 * q + 1] = f.y;
+          v[4 * q + 2] = f.z;
+          v[4 * q + 3] = f.w;
+        } else {
+          const float2 f = *reinterpret_cast<const float2*>(buf + a * M + 2 * unit);
+          v[2 * q] = f.x;
+          v[2 * q + 1] = f.y;
+        }
       }
 #pragma unroll
-      for (int h = 4; h < 64; h <<= 1)
+      for (int h = BW; h < 16 * BW; h <<= 1)
 #pragma unroll
-        for (int r = 0; r < 64; ++r)
+        for (int r = 0; r < 16 * BW; ++r)
           if ((r & h) == 0) {
             const float a = v[r], b = v[r + h];
             v[r] = a + b;
             v[r + h] = a - b;
           }
 #pragma unroll
-      for (int r = 0; r < 64; ++r) {
+      for (int r = 0; r < 16 * BW; ++r) {
         amax = fmaxf(amax, fabsf(v[r]));
         if (RMS) ss = fmaf(v[r], v[r], ss);
       }
@@ -299,22 +311,33 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     const __half s16 = row_scale_fp16(amax * norm * rs, clip_ratio);
     const float kq = inv_scale(s16) * norm * rs * sigma;
     const float xnorm = norm * rs * sigma;
-    uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
     if (task_on) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int a = abase + ((q & 1) << 2) + ((q >> 1) << 7);
-        const float t0 = magic_code<CLAMP>(v[4 * q], kq), t1 = magic_code<CLAMP>(v[4 * q + 1], kq);
-        const float t2 = magic_code<CLAMP>(v[4 * q + 2], kq), t3 = magic_code<CLAMP>(v[4 * q + 3], kq);
-        const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t2),
-                                                  __builtin_bit_cast(uint32_t, t0), 0x0c0c0400u);
-        const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t3),
-                                                  __builtin_bit_cast(uint32_t, t1), 0x0c0c0400u);
-        codes[(a * M + 4 * unit) >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
-        if (x_rot) {
-          float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + a * M + 4 * unit);
-          *dst = make_float4(v[4 * q] * xnorm, v[4 * q + 1] * xnorm, v[4 * q + 2] * xnorm,
-                             v[4 * q + 3] * xnorm);
+        if (BW == 4) {
+          uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
+          const float t0 = magic_code<CLAMP>(v[4 * q], kq), t1 = magic_code<CLAMP>(v[4 * q + 1], kq);
+          const float t2 = magic_code<CLAMP>(v[4 * q + 2], kq), t3 = magic_code<CLAMP>(v[4 * q + 3], kq);
+          const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t2),
+                                                    __builtin_bit_cast(uint32_t, t0), 0x0c0c0400u);
+          const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t3),
+                                                    __builtin_bit_cast(uint32_t, t1), 0x0c0c0400u);
+          codes[(a * M + 4 * unit) >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
+          if (x_rot) {
+            float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + a * M + 4 * unit);
+            *dst = make_float4(v[4 * q] * xnorm, v[4 * q + 1] * xnorm, v[4 * q + 2] * xnorm,
+                               v[4 * q + 3] * xnorm);
+          }
+        } else {
+          uint8_t* codes = reinterpret_cast<uint8_t*>(buf + C::D);  // 2 codes per unit
+          const uint32_t t0 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * q], kq));
+          const uint32_t t1 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * q + 1], kq));
+          codes[(a * M + 2 * unit) >> 1] = uint8_t(((t1 << 4) | (t0 & 0xFu)) ^ 0x88u);
+          if (x_rot) {
+            float2* dst = reinterpret_cast<float2*>(x_rot + row * int64_t(C::D) + a * M + 2 * unit);
+            *dst = make_float2(v[2 * q] * xnorm, v[2 * q + 1] * xnorm);
+          }
         }
       }
     }
@@ -327,7 +350,7 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     for (int i = 0; i < kIter; ++i) {
       const int c = tid + kKronBlock * i;
       if (i + 1 < kIter || c < kChunks)
-        *reinterpret_cast<uint4*>(qrow + 16 * c) = reinterpret_cast<const uint4*>(codes)[c];
+        *reinterpret_cast<uint4*>(qrow + 16 * c) = reinterpret_cast<const uint4*>(buf + C::D)[c];
     }
     if (tid == 0) scale_out[row] = s16;
   }
