@@ -6,7 +6,8 @@ H_{2^n}, Kronecker with a Paley H_m), per-token symmetric INT4 quantisation
 with nibble packing, the integer GEMM with the per-token x per-channel
 dequantisation, the per-head rotation + INT4 quantisation of K/V
 (symmetric, and the asymmetric zero-point variant), the RMSNorm-fused
-rotate+quant, and the decode attention over the INT4 cache with the
+rotate+quant, the cross-head transform + quantisation of the attention
+output (the out-projection's input), and the decode attention over the INT4 cache with the
 cross-head transform (``oracle.attention``).
 
 Only the test suite (``tests/``), the smoke check in ``__graft_entry__`` and
@@ -28,8 +29,8 @@ from .quant import (ABSMAX_FLOOR, QMAX, QMIN, ZMAX, asym_codes, asym_params, cod
                     pack_int4, pack_uint4, quantize_rows, quantize_rows_asym, row_scales,
                     unpack_int4, unpack_uint4)
 from .gemm import dequant, int_gemm, int_gemm_exact, w4a4_reference
-from .pipeline import (had_quant, kv_had_quant, kv_had_quant_asym, prep_weights, rmsnorm,
-                       rmsnorm_had_quant, w4a4_linear)
+from .pipeline import (cross_head_quant, had_quant, kv_had_quant, kv_had_quant_asym,
+                       prep_weights, rmsnorm, rmsnorm_had_quant, w4a4_linear)
 
 __all__ = [
     "GF", "SUPPORTED_M", "hadamard_m", "paley1", "sylvester",
@@ -39,5 +40,5 @@ __all__ = [
     "ZMAX", "asym_codes", "asym_params", "quantize_rows_asym", "pack_uint4", "unpack_uint4",
     "dequant", "int_gemm", "int_gemm_exact", "w4a4_reference",
     "had_quant", "kv_had_quant", "kv_had_quant_asym", "prep_weights", "w4a4_linear",
-    "rmsnorm", "rmsnorm_had_quant",
+    "rmsnorm", "rmsnorm_had_quant", "cross_head_quant",
 ]

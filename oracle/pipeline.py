@@ -11,6 +11,11 @@
   Rotation Fused into RMSNorm"): the normalised row x / sqrt(mean(x^2) + eps)
   is rotated and quantised per token.  The RMSNorm gain is absorbed into the
   next weights (paper-graph-ui summary, Stage 1a), so no gain is applied.
+* Out-projection input (same page, Stage 1c "Attention Value Projection
+  Rotation"): the concatenated attention output Z gets the online cross-head
+  transform Z (H_{n_h} (x) I_{d_h}) (no random signs: the head-wise factor
+  and the out-projection weights absorb the rest of the rotation offline),
+  then the per-token quantisation of Stage 2b feeds the INT4 out-projection.
 * KV cache (same page, Stage 1d "online head-wise rotation after RoPE" and
   Stage 2c; "QuaRot Guide", step 4 of "Deep Dive"): each (batch, head,
   position) vector of head_dim values is rotated by the head-wise Hadamard and
@@ -23,12 +28,13 @@ from __future__ import annotations
 
 import numpy as np
 
+from .attention import cross_head
 from .gemm import w4a4_reference
 from .quant import pack_int4, pack_uint4, quantize_rows, quantize_rows_asym
 from .rotate import rotate_rows
 
 __all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant", "kv_had_quant_asym",
-           "rmsnorm", "rmsnorm_had_quant"]
+           "rmsnorm", "rmsnorm_had_quant", "cross_head_quant"]
 
 
 def had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0):
@@ -102,3 +108,16 @@ def rmsnorm_had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: 
                       eps: float = 1e-5):
     """RMSNorm, then rotate+quant: had_quant(rmsnorm(x, eps))."""
     return had_quant(rmsnorm(x, eps), signs, m, clip_ratio)
+
+
+def cross_head_quant(z: np.ndarray, n_heads: int, clip_ratio: float = 1.0):
+    """Cross-head transform of each row of z [rows x n_heads*d_h] (heads
+    concatenated, head h at lanes h*d_h .. h*d_h + d_h - 1), then per-token
+    rotate+quant's quantiser.  Returns the same dict as had_quant."""
+    z = np.asarray(z, dtype=np.float64)
+    rows, d = z.shape
+    if n_heads <= 0 or d % n_heads:
+        raise ValueError("n_heads must divide the row length")
+    z_rot = cross_head(z.reshape(rows, n_heads, d // n_heads)).reshape(rows, d)
+    codes, scales = quantize_rows(z_rot, clip_ratio)
+    return {"x_rot": z_rot, "codes": codes, "packed": pack_int4(codes), "scales": scales}

@@ -44,6 +44,9 @@ __all__ = [
     "DecodeConfig",
     "DECODE_CONFIGS",
     "make_decode_query",
+    "CrossHeadConfig",
+    "CROSS_HEAD_CONFIGS",
+    "make_attn_output",
     "random_signs",
     "config_by_name",
 ]
@@ -135,9 +138,50 @@ def make_decode_query(cfg: DecodeConfig, seed: int = 0, batch: Optional[int] = N
     return q.astype(np.float16)
 
 
+@dataclasses.dataclass(frozen=True)
+class CrossHeadConfig:
+    """Attention output Z [tokens x heads*head_dim] of a prefill, the input of
+    the out-projection (cross-head transform, then per-token quantisation)."""
+
+    name: str
+    tokens: int
+    heads: int
+    head_dim: int
+    loud_heads: int  # heads whose every lane is scaled by one U(10, 100) factor
+
+    @property
+    def d(self) -> int:
+        return self.heads * self.head_dim
+
+
+# LLaMA-2-7B (32 heads) and LLaMA-2-70B (64 heads) of 128 lanes, at the token
+# counts of the activation workloads of the same models.
+CROSS_HEAD_CONFIGS = {
+    "attn_out_7b": CrossHeadConfig("attn_out_7b", 2048, 32, 128, 2),
+    "attn_out_70b": CrossHeadConfig("attn_out_70b", 4096, 64, 128, 4),
+}
+
+
+def make_attn_output(cfg: CrossHeadConfig, seed: int = 0, tokens: Optional[int] = None) -> dict:
+    """Z fp16 [tokens x heads*head_dim] ~ N(0, 1) with ``loud_heads`` heads
+    (drawn without replacement) scaled by one U(10, 100) factor each: value
+    vectors whose heads carry very different energies.  Draw order: loud
+    heads -> their factors -> Z."""
+    rng = np.random.default_rng(seed)
+    t = cfg.tokens if tokens is None else tokens
+    loud = np.sort(rng.choice(cfg.heads, size=cfg.loud_heads, replace=False))
+    factors = rng.uniform(10.0, 100.0, size=cfg.loud_heads).astype(np.float32)
+    z = rng.standard_normal((t, cfg.heads, cfg.head_dim), dtype=np.float32)
+    z[:, loud, :] *= factors[None, :, None]
+    return {"z": z.reshape(t, cfg.d).astype(np.float16), "loud_heads": loud,
+            "loud_factors": factors}
+
+
 def config_by_name(name: str):
     if name in ACT_CONFIGS:
         return ACT_CONFIGS[name]
+    if name in CROSS_HEAD_CONFIGS:
+        return CROSS_HEAD_CONFIGS[name]
     if name == KV_CONFIG.name:
         return KV_CONFIG
     if name in DECODE_CONFIGS:
