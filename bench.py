@@ -71,6 +71,10 @@ def parse_args():
                    help="with --decode: leave out the cross-head transform")
     p.add_argument("--rmsnorm", action="store_true",
                    help="with an activation workload: the RMSNorm-fused rotate+quant")
+    p.add_argument("--cross-head", action="store_true",
+                   help="benchmark the cross-head transform + quantisation of the attention output")
+    p.add_argument("--cross-head-workload", default="attn_out_70b",
+                   choices=sorted(workloads.CROSS_HEAD_CONFIGS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough for 1 GiB)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -115,7 +119,8 @@ def time_kernel(torch, stream, launch, count: int, lead: int = 10) -> float:
 
 # The source file each timed kernel is compiled from.
 KERNEL_FILES = {"had_quant": "had_quant.hip", "w4a4_gemm": "gemm.hip",
-                "kv_had_quant": "kv.hip", "kv_decode": "decode.hip"}
+                "kv_had_quant": "kv.hip", "kv_decode": "decode.hip",
+                "cross_head": "cross_head.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -365,6 +370,75 @@ def bench_kv(args, torch, qr) -> dict:
     }
 
 
+def cpu_baseline_cross_head(cfg, z16, rows=None) -> dict:
+    """The oracle, as it stands, on the first ``rows`` tokens (default: all)."""
+    import oracle
+
+    rows = cfg.tokens if rows is None else rows
+    t0 = time.perf_counter()
+    oracle.cross_head_quant(z16[:rows], cfg.heads)
+    dt = time.perf_counter() - t0
+    nbytes = rows * (2 * cfg.d + cfg.d // 2 + 2)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "seconds": dt, "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of the {cfg.tokens} tokens of {cfg.name} (float64 einsum over the "
+                      f"head index, then the quantiser)"}
+
+
+def bench_cross_head(args, torch, qr) -> dict:
+    cfg = workloads.CROSS_HEAD_CONFIGS[args.cross_head_workload]
+    log(f"cross-head workload {cfg.name}: generating inputs")
+    z16 = workloads.make_attn_output(cfg)["z"]
+    T, d = z16.shape
+    z0 = torch.from_numpy(z16).cuda()
+    per_set = T * (2 * d + d // 2 + 2)
+    nsets = args.sets or max(2, -(-CACHE_DEFEAT_BYTES // per_set))
+    sets = []
+    for i in range(nsets):
+        sets.append({"z": z0 if i == 0 else z0.clone(),
+                     "q": torch.empty((T, d // 2), dtype=torch.uint8, device="cuda"),
+                     "s": torch.empty((T,), dtype=torch.float16, device="cuda")})
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        st = sets[i % nsets]
+        qr.cross_head_had_quant(st["z"], cfg.heads, 1.0, q_out=st["q"], scale_out=st["s"],
+                                stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = time_kernel(torch, stream, step, args.steps)
+    gbs = per_set / (ms * 1e-3) / 1e9
+    log(f"cross-head {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
+    out = {
+        "metric": "cross-head transform + quant GB/s (% HBM peak)",
+        "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32 transform / int4 codes",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: attention output Z fp16 [{T} x {cfg.heads} x "
+                               f"{cfg.head_dim}], {cfg.loud_heads} heads x U(10,100); "
+                               f"H_{cfg.heads} over the head index, per-token int4",
+                   "buffer_sets": nsets},
+        "kernels_us": {"cross_head": round(ms * 1e3, 3)},
+        "roofline": {"kernel": "cross_head_quant", "bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, "cross_head"),
+                     "algorithmic_bytes": per_set},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_cross_head(cfg, z16)
+    return out
+
+
 def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows: int = 4) -> dict:
     """The oracle, as it stands, on `rows` batch rows of the decode step (its
     cache built by the oracle's KV quantiser, untimed)."""
@@ -532,7 +606,8 @@ def counter_means(path: str, counter: str, min_dispatches: int = 3) -> dict:
 # kernel-name fragment -> traffic key; kernels sharing a key (the decode
 # call's split and combine kernels) are summed
 KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant": "kv_had_quant",
-               "decode_split": "kv_decode", "decode_combine": "kv_decode"}
+               "decode_split": "kv_decode", "decode_combine": "kv_decode",
+               "cross_head_quant": "cross_head"}
 
 
 def summarize_counters(args) -> dict:
@@ -599,7 +674,9 @@ def main() -> int:
     if args.calibrate_copy:
         out = calibrate_copy(torch)
     else:
-        if args.decode:
+        if args.cross_head:
+            out = bench_cross_head(args, torch, qr)
+        elif args.decode:
             out = bench_decode(args, torch, qr)
         elif args.kv:
             out = bench_kv(args, torch, qr)

@@ -102,6 +102,40 @@ int quarot_rmsnorm_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_
                              float* x_rot_out, void* stream);
 
 /*
+ * Cross-head transform + per-token symmetric INT4 quantisation of the
+ * attention output (the input of the INT4 out-projection).
+ *
+ * Follows [S] section 3.4 Stage 1c (the head-wise factor I_{n_h} (x) H_{d_h}
+ * of the full Hadamard is folded into W_v and W_out offline; the online block
+ * after attention computes Z <- Z (H_{n_h} (x) I_{d_h}), a Walsh-Hadamard
+ * transform of length n_h over the head index for every head-dim lane) and
+ * Stage 2b (per-token scale clip * max|z~| / 7).  No random signs: the
+ * out-projection weights absorb the same plain Hadamard offline.
+ *
+ * For every row r of z (fp16 [rows x n_heads*head_dim], head h at elements
+ * h*head_dim .. h*head_dim + head_dim - 1, row stride ld_z elements):
+ *   z~[a*head_dim + c] = sum_a' H[a', a] z[a'*head_dim + c] / sqrt(n_heads)
+ * with H the Sylvester matrix H[i][j] = (-1)^popcount(i & j), then S_r and
+ * the codes exactly as quarot_had_quant (fp32 arithmetic, ties to even).
+ *
+ * Arguments:
+ *   z          fp16, 4-byte aligned, ld_z >= n_heads*head_dim, ld_z even.
+ *   n_heads    a power of two, 1 .. 64 (1 = quantisation only).
+ *   head_dim   128.
+ *   clip_ratio in (0, 1].
+ *   q_out      uint8 [rows x ld_q], ld_q >= n_heads*head_dim/2.
+ *   scale_out  fp16 [rows], 2-byte aligned.
+ *   z_rot_out  optional fp32 [rows x n_heads*head_dim] (dense, 8-byte
+ *              aligned) receiving z~; NULL in production.
+ * Errors: INVALID for negative rows, bad strides, clip or a missing required
+ * pointer; UNSUPPORTED for other head_dim or n_heads; MISALIGNED as stated.
+ * rows == 0 is a no-op.  Non-finite inputs are outside the contract.
+ */
+int quarot_cross_head_had_quant(const void* z, int64_t rows, int64_t n_heads, int64_t head_dim,
+                                int64_t ld_z, float clip_ratio, uint8_t* q_out, int64_t ld_q,
+                                void* scale_out, float* z_rot_out, void* stream);
+
+/*
  * W4A4 GEMM with INT32 accumulation and the per-token x per-channel dequant.
  *
  * Follows [S] section 3.4 Stage 2b (dequantised output

@@ -11,6 +11,8 @@ Calls (same names as the C entry points, without the ``quarot_`` prefix):
 * ``had_quant(x, signs, m, clip_ratio)``   -> (codes uint8 [rows, d/2], scales fp16 [rows])
 * ``rmsnorm_had_quant(x, eps, signs, m, clip_ratio)`` -> (codes, scales) of
   the RMS-normalised rows
+* ``cross_head_had_quant(z, n_heads, clip_ratio)`` -> (codes, scales) of the
+  attention output after the cross-head transform (out-projection input)
 * ``w4a4_gemm(a_q, a_scale, b_q, b_scale, k)`` -> fp16 [M, N]
 * ``kv_had_quant(k, v, signs, k_cache, k_scale, v_cache, v_scale, pos0)``
 * ``kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len)``
@@ -22,10 +24,10 @@ Tensors are torch tensors on the current HIP device; torch provides device
 memory and streams only.
 """
 
-from ._lib import (QuarotError, had_quant, hadamard_factor, kv_decode_attention,
-                   kv_decode_workspace_bytes, kv_had_quant, lib, library_path,
-                   rmsnorm_had_quant, w4a4_gemm)
+from ._lib import (QuarotError, cross_head_had_quant, had_quant, hadamard_factor,
+                   kv_decode_attention, kv_decode_workspace_bytes, kv_had_quant, lib,
+                   library_path, rmsnorm_had_quant, w4a4_gemm)
 
-__all__ = ["QuarotError", "had_quant", "hadamard_factor", "kv_decode_attention",
-           "kv_decode_workspace_bytes", "kv_had_quant", "lib", "library_path",
-           "rmsnorm_had_quant", "w4a4_gemm"]
+__all__ = ["QuarotError", "cross_head_had_quant", "had_quant", "hadamard_factor",
+           "kv_decode_attention", "kv_decode_workspace_bytes", "kv_had_quant", "lib",
+           "library_path", "rmsnorm_had_quant", "w4a4_gemm"]

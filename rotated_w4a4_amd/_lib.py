@@ -22,6 +22,8 @@ _SIGNATURES = {
                                         _vp, _i64, _vp, _vp, _vp]),
     "quarot_rmsnorm_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _f32, _vp, _i32, _f32,
                                                 _vp, _i64, _vp, _vp, _vp]),
+    "quarot_cross_head_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _i64,
+                                                   _vp, _vp, _vp]),
     "quarot_w4a4_gemm": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                                         _vp, _i64, _vp, _i64, _vp]),
     "quarot_kv_had_quant": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -152,6 +154,21 @@ def rmsnorm_had_quant(x, eps: float = 1e-5, signs=None, m: int = 1, clip_ratio: 
                                         m, float(clip_ratio), _ptr(q_out), q_out.stride(0),
                                         _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
     _check("quarot_rmsnorm_had_quant", st)
+    return q_out, scale_out
+
+
+def cross_head_had_quant(z, n_heads: int, clip_ratio: float = 1.0, q_out=None, scale_out=None,
+                         z_rot_out=None, stream=None):
+    """Cross-head transform (H_{n_heads} over the head index, normalised) then
+    per-token INT4 of rows of fp16 z [rows, n_heads * 128]; returns (codes, scales)."""
+    rows, d, q_out, scale_out = _had_quant_outputs(z, None, q_out, scale_out, z_rot_out)
+    if n_heads <= 0 or d % n_heads:
+        raise ValueError("n_heads must divide the row length")
+    st = lib().quarot_cross_head_had_quant(_ptr(z), rows, int(n_heads), d // int(n_heads),
+                                           z.stride(0), float(clip_ratio), _ptr(q_out),
+                                           q_out.stride(0), _ptr(scale_out), _ptr(z_rot_out),
+                                           _stream(stream))
+    _check("quarot_cross_head_had_quant", st)
     return q_out, scale_out
 
 

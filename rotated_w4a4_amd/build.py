@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libquarot.so")
-SOURCES = ["abi.hip", "had_quant.hip", "gemm.hip", "kv.hip", "decode.hip"]
+SOURCES = ["abi.hip", "had_quant.hip", "gemm.hip", "kv.hip", "decode.hip", "cross_head.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -4,6 +4,7 @@
 #include <cstring>
 
 #include "common.h"
+#include "cross_head.h"
 #include "decode.h"
 
 namespace quarot {
@@ -126,6 +127,34 @@ int quarot_rmsnorm_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_
   QR_CHECK_ARG(eps > 0.0f && eps < INFINITY, QUAROT_ERR_INVALID, "eps must be finite and > 0");
   return had_quant_checked(x, rows, d, ld_x, signs, m, clip_ratio, q_out, ld_q, scale_out,
                            x_rot_out, eps, stream);
+}
+
+int quarot_cross_head_had_quant(const void* z, int64_t rows, int64_t n_heads, int64_t head_dim,
+                                int64_t ld_z, float clip_ratio, uint8_t* q_out, int64_t ld_q,
+                                void* scale_out, float* z_rot_out, void* stream) {
+  clear_error();
+  QR_CHECK_ARG(rows >= 0, QUAROT_ERR_INVALID, "rows = %lld < 0", (long long)rows);
+  QR_CHECK_ARG(n_heads > 0 && head_dim > 0, QUAROT_ERR_INVALID, "n_heads and head_dim must be > 0");
+  QR_CHECK_ARG(clip_ok(clip_ratio), QUAROT_ERR_INVALID, "clip_ratio must be in (0, 1]");
+  QR_CHECK_ARG(head_dim == 128, QUAROT_ERR_UNSUPPORTED, "head_dim = %lld: supported is 128",
+               (long long)head_dim);
+  QR_CHECK_ARG(is_pow2(n_heads) && n_heads <= 64, QUAROT_ERR_UNSUPPORTED,
+               "n_heads = %lld: need a power of two <= 64", (long long)n_heads);
+  const int64_t d = n_heads * head_dim;
+  QR_CHECK_ARG(ld_z >= d, QUAROT_ERR_INVALID, "ld_z = %lld < n_heads * head_dim", (long long)ld_z);
+  QR_CHECK_ARG(ld_q >= d / 2, QUAROT_ERR_INVALID, "ld_q = %lld < n_heads * head_dim / 2",
+               (long long)ld_q);
+  if (rows == 0) return QUAROT_OK;
+  QR_CHECK_ARG(z && q_out && scale_out, QUAROT_ERR_INVALID, "z, q_out and scale_out are required");
+  QR_CHECK_ARG(aligned(z, 4) && ld_z % 2 == 0, QUAROT_ERR_MISALIGNED,
+               "z must be 4-byte aligned with an even ld_z");
+  QR_CHECK_ARG(aligned(scale_out, 2), QUAROT_ERR_MISALIGNED, "scale_out must be 2-byte aligned");
+  QR_CHECK_ARG(z_rot_out == nullptr || aligned(z_rot_out, 8), QUAROT_ERR_MISALIGNED,
+               "z_rot_out must be 8-byte aligned");
+  QR_CHECK_ARG(rows <= (int64_t(1) << 31) - 1, QUAROT_ERR_UNSUPPORTED, "rows too large");
+  return launch_cross_head_quant(static_cast<const __half*>(z), rows, int(n_heads), ld_z,
+                                 clip_ratio, q_out, ld_q, static_cast<__half*>(scale_out),
+                                 z_rot_out, static_cast<hipStream_t>(stream));
 }
 
 int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,

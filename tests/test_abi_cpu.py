@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(lib):
         text = f.read()
     names = set(re.findall(r"\b(quarot_[a-z0-9_]+)\s*\(", text))
     assert {"quarot_had_quant", "quarot_w4a4_gemm", "quarot_kv_had_quant",
-            "quarot_kv_decode_attention", "quarot_kv_decode_workspace_bytes"} <= names
+            "quarot_kv_decode_attention", "quarot_kv_decode_workspace_bytes",
+            "quarot_rmsnorm_had_quant", "quarot_cross_head_had_quant"} <= names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -253,3 +254,38 @@ def test_rmsnorm_had_quant_rejects(lib, kw, status):
 
 def test_rmsnorm_had_quant_zero_rows_is_noop(lib):
     assert _rms(lib, rows=0, x=None, q=None, s=None) == OK
+
+
+def _ch(lib, **kw):
+    a = dict(z=FAKE, rows=4, nh=8, dh=128, ld_z=1024, clip=1.0, q=FAKE, ld_q=512, s=FAKE, zr=None)
+    a.update(kw)
+    return lib.quarot_cross_head_had_quant(a["z"], a["rows"], a["nh"], a["dh"], a["ld_z"],
+                                           a["clip"], a["q"], a["ld_q"], a["s"], a["zr"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), INVALID),
+    (dict(nh=0), INVALID),
+    (dict(dh=0), INVALID),
+    (dict(clip=0.0), INVALID),
+    (dict(clip=float("nan")), INVALID),
+    (dict(dh=64, ld_z=512, ld_q=256), UNSUPPORTED),
+    (dict(nh=6, ld_z=768, ld_q=384), UNSUPPORTED),
+    (dict(nh=128, ld_z=16384, ld_q=8192), UNSUPPORTED),
+    (dict(ld_z=1000), INVALID),
+    (dict(ld_q=500), INVALID),
+    (dict(z=None), INVALID),
+    (dict(q=None), INVALID),
+    (dict(s=None), INVALID),
+    (dict(z=FAKE + 2), MISALIGNED),
+    (dict(ld_z=1025), MISALIGNED),
+    (dict(s=FAKE + 1), MISALIGNED),
+    (dict(zr=FAKE + 4), MISALIGNED),
+])
+def test_cross_head_had_quant_rejects(lib, kw, status):
+    assert _ch(lib, **kw) == status
+    assert lib.quarot_last_error()
+
+
+def test_cross_head_had_quant_zero_rows_is_noop(lib):
+    assert _ch(lib, rows=0, z=None, q=None, s=None) == OK
