@@ -654,6 +654,12 @@ def main() -> int:
     args = parse_args()
     if args.traffic_from:
         t = summarize_counters(args)
+        # workloads not re-measured in this run keep their earlier entries
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                old = json.load(f).get("kernels", {})
+            for name, ent in old.items():
+                t["kernels"].setdefault(name, ent)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t))

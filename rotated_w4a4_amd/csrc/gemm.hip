@@ -390,12 +390,305 @@ int launch_cfg(const uint8_t* a_q, int64_t lda, const __half* a_scale, const uin
   return check_launch("w4a4_gemm");
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile variant for problems with many output tiles: four waves (one
+// per SIMD), each owning a 128 x 128 block of the output (4 x 4 MFMA blocks,
+// 256 accumulator registers).  Against 64 x 64 wave tiles this halves the
+// LDS bytes and the widening instructions per MFMA; both cost clock under
+// the chip's power limit as well as issue cycles.  K tiles are 128 codes
+// (64 bytes per row, two K-pairs) in a ring of four LDS stages: the copy of
+// tile kt + 3 is issued while tile kt is computed, so each copy has two
+// tiles of compute to land.
+template <int WAVES_M_, int WAVES_N_, int WM_, int WN_, int NST_>
+struct BigCfg {
+  static constexpr int BKB = 64, CPR = 4, NST = NST_, KP = 2;
+  static_assert(NST >= 3, "the ring needs a stage being computed, one landed and one in flight");
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NW = WAVES_M * WAVES_N;
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int ROWS = BM + BN;
+  static constexpr int STAGE = ROWS * BKB;
+  static constexpr int BLK = ROWS / 16;   // 16-row (1 KiB) blocks per tile
+  static constexpr int CH = BLK / NW;     // copy instructions per wave per tile
+  static_assert(BLK % NW == 0 && BM % 16 == 0, "copy blocks must split evenly and not straddle A/B");
+};
+
+using BigCfg4 = BigCfg<2, 2, 128, 128, 4>;  // 256 x 256 workgroup tile
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void w4a4_gemm_big_kernel(
+    const uint8_t* __restrict__ a_q, int64_t lda, const __half* __restrict__ a_scale,
+    const uint8_t* __restrict__ b_q, int64_t ldb, const __half* __restrict__ b_scale,
+    int M, int N, int K, __half* __restrict__ c, int64_t ldc, int32_t* __restrict__ acc_out,
+    int64_t ld_acc, int tiles_m, int tiles_n) {
+  constexpr int FM = C::FM, FN = C::FN, CH = C::CH, BM = C::BM, BN = C::BN;
+  constexpr int BKB = C::BKB, NST = C::NST, NW = C::NW;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE];
+
+  // --- tile assignment: XCD-major, then grouped along M -------------------
+  const int total = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  const int group = pid / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (pid % (GROUP_M * tiles_n)) % gsz;
+  const int tn = (pid % (GROUP_M * tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave / C::WAVES_N) * C::WM;
+  const int wn = (wave % C::WAVES_N) * C::WN;
+  const int kbytes = K >> 1;
+  const int kfull = kbytes / BKB;
+  const bool has_tail = (kbytes % BKB) != 0;
+
+  // Copy i of wave w fills tile rows 16 b .. 16 b + 15, b = NW i + w (A rows,
+  // then B rows): lane l owns row 16 b + l / 4 and LDS slot l % 4 of it, and
+  // fetches the global chunk the swizzle puts in that slot.  Rows past the
+  // matrix edge re-read the last row (their results are never stored).
+  const uint8_t* src[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int r = 16 * (NW * i + wave) + (lane >> 2);
+    const int ch = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * ch
+                      : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb + 16 * ch;
+  }
+  const uint32_t lds0 = lds_address(&smem[0]);
+#define QB_COPY(st, t)                                                                     \
+  {                                                                                        \
+    const int64_t kb0_ = int64_t(min((t), kfull - 1)) * BKB;                               \
+    _Pragma("unroll") for (int i = 0; i < CH; ++i)                                         \
+        lds_copy16(src[i] + kb0_, lds0 + uint32_t((st) * C::STAGE + (NW * i + wave) * 1024)); \
+  }
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
+
+  const int frow = lane & 31;
+  const int fhalf = lane >> 5;
+
+  uint4 ra0[FM], rb0[FN], ra1[FM], rb1[FN];
+  v4i al0[FM], ah0[FM], bl0[FN], bh0[FN], al1[FM], ah1[FM], bl1[FN], bh1[FN];
+#define QB_READ(n, st, kp)                                                                    \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) ra##n[i] =                                  \
+      ld16(smem + (st) * C::STAGE + lds_off<BKB>(wm + i * 32 + frow, 2 * (kp) + fhalf));    \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) rb##n[j] =                                  \
+      ld16(smem + (st) * C::STAGE + BM * BKB + lds_off<BKB>(wn + j * 32 + frow, 2 * (kp) + fhalf))
+#define QB_WIDEN(n)                                                                           \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) widen(ra##n[i], al##n[i], ah##n[i]);        \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) widen(rb##n[j], bl##n[j], bh##n[j])
+#define QB_MFMA(n)                                                                            \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                              \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                              \
+    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al##n[i], bl##n[j], acc[i][j], 0, 0, 0); \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i)                                              \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j)                                              \
+    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah##n[i], bh##n[j], acc[i][j], 0, 0, 0);
+
+  // One step in 2 FM groups, each fenced off for the scheduler: group g runs
+  // the MFMAs of accumulator row g % FM (the low halves first, then the
+  // high halves), and the FM + FN raw fragments are spread over the groups
+  // (fragment f in group f * 2 FM / (FM + FN)): each is read for K-pair
+  // g + 2 into raw set RD and widened from raw set WD.  In the first step
+  // of a tile the CH copies of the next tile are spread the same way.  The
+  // global-to-LDS copies and LDS reads thereby sit between MFMAs instead of
+  // stalling the wave that issues them in a burst.
+  constexpr int NG = 2 * FM, NF = FM + FN;
+#define QB_GSTEP(RD, WD, ST, KP, DO_COPY)                                                          \
+  _Pragma("unroll") for (int g = 0; g < NG; ++g) {                                               \
+    _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                             \
+      if (f * NG / NF != g) continue;                                                             \
+      if (f < FM)                                                                                 \
+        ra##RD[f] = ld16(smem + (ST) * C::STAGE + lds_off<BKB>(wm + f * 32 + frow, 2 * (KP) + fhalf)); \
+      else                                                                                        \
+        rb##RD[f - FM] = ld16(smem + (ST) * C::STAGE + BM * BKB +                                 \
+                              lds_off<BKB>(wn + (f - FM) * 32 + frow, 2 * (KP) + fhalf));         \
+    }                                                                                             \
+    if (g < FM) {                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[g][j] =                                  \
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(al##RD[g], bl##RD[j], acc[g][j], 0, 0, 0);        \
+    } else {                                                                                      \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[g - FM][j] =                             \
+          __builtin_amdgcn_mfma_i32_32x32x32_i8(ah##RD[g - FM], bh##RD[j], acc[g - FM][j], 0, 0, 0); \
+    }                                                                                             \
+    _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                             \
+      if (f * NG / NF != g) continue;                                                             \
+      if (f < FM) widen(ra##WD[f], al##WD[f], ah##WD[f]);                                        \
+      else widen(rb##WD[f - FM], bl##WD[f - FM], bh##WD[f - FM]);                                \
+    }                                                                                             \
+    if (DO_COPY) {                                                                                \
+      _Pragma("unroll") for (int cc = 0; cc < CH; ++cc) {                                        \
+        if (cc * NG / CH != g) continue;                                                          \
+        lds_copy16(src[cc] + kbc, lds0 + uint32_t(stc * C::STAGE + (NW * cc + wave) * 1024));     \
+      }                                                                                           \
+    }                                                                                             \
+    _Pragma("unroll") for (int q = 0; q < FN; ++q) {                                              \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                                         \
+    }                                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+  }
+
+  // K-pair g = 2 kt + kp.  Step g reads K-pair g + 2 (tile kt + 1, same kp)
+  // into register set g % 2, widens K-pair g + 1 into the other widened set
+  // and runs the MFMAs of K-pair g.  Iteration kt starts by waiting until
+  // tile kt + 1 has landed (its copy was issued two iterations earlier; only
+  // tile kt + 2's copy may still be in flight) and a barrier, after which
+  // every wave has consumed tile kt - 1, so its stage takes the copy of
+  // tile kt + 3.  Copies past the last full tile repeat it into stages that
+  // are never read as real data.
+  if (kfull > 0) {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) QB_COPY(t, t);
+    wait_vmcnt<(NST - 2) * CH>();  // tile 0 landed
+    __syncthreads();
+    QB_READ(0, 0, 0);
+    QB_READ(1, 0, 1);
+    QB_WIDEN(0);
+    int st1 = 1 % NST, stc = NST - 1;  // stages of tiles kt + 1 and kt + NST - 1
+    for (int kt = 0; kt < kfull; ++kt) {
+      wait_vmcnt<(NST - 3) * CH>();  // tile kt + 1 landed
+      __syncthreads();
+      {
+        const int64_t kbc = int64_t(min(kt + NST - 1, kfull - 1)) * BKB;
+        // kp0: read tile kt+1 kp0 into set 0, widen tile kt kp1 (set 1), MFMAs tile kt kp0 (set 0)
+        QB_GSTEP(0, 1, st1, 0, true);
+        // kp1: read tile kt+1 kp1 into set 1, widen tile kt+1 kp0 (set 0), MFMAs tile kt kp1 (set 1)
+        QB_GSTEP(1, 0, st1, 1, false);
+      }
+      st1 = st1 == NST - 1 ? 0 : st1 + 1;
+      stc = stc == NST - 1 ? 0 : stc + 1;
+    }
+    wait_vmcnt<0>();
+  }
+#undef QB_COPY
+  if (has_tail) {  // the partial tile at the end of K: chunks past K read as zero
+    __syncthreads();
+    const int kb0 = kfull * BKB;
+    for (int idx = tid; idx < C::ROWS * C::CPR; idx += C::THREADS) {
+      const int r = idx / C::CPR, lchunk = idx % C::CPR;
+      const uint8_t* p = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda
+                                  : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb;
+      const bool ok = kb0 + 16 * lchunk < kbytes;
+      const uint4 v = ok ? ld16(p + kb0 + 16 * lchunk) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(smem + lds_off<BKB>(r, lchunk)) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kp = 0; kp < C::KP; ++kp) {
+      QB_READ(0, 0, kp);
+      QB_WIDEN(0);
+      QB_MFMA(0);
+    }
+  }
+#undef QB_READ
+#undef QB_WIDEN
+#undef QB_MFMA
+#undef QB_GSTEP
+
+  // --- epilogue: acc / 256 -> fp32 * scale_x * scale_w -> fp16 -----------
+  // One 32-row block of the wave tile at a time goes through a per-wave
+  // [32][WN + 8] int32 staging tile, so each lane then owns 8 consecutive
+  // columns of a row (16-byte output stores).
+  constexpr int WN = C::WN, LDS_ROW = WN + 8;
+  static_assert(NW * 32 * LDS_ROW * 4 <= NST * C::STAGE, "staging tiles must fit");
+  constexpr int CG = WN / 8, RSTEP = 64 / CG;
+  const int cg = lane % CG, r0 = lane / CG;
+  const int col0 = n0 + wn + 8 * cg;
+  float sw[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sw[k] = __half2float(b_scale[min(col0 + k, N - 1)]);
+  const bool full_cols = col0 + 8 <= N;
+  const bool vec_c = full_cols && (ldc % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0;
+  const bool vec_acc = full_cols && acc_out && (ld_acc % 4) == 0 &&
+                       (reinterpret_cast<uintptr_t>(acc_out) % 16) == 0;
+  int32_t* stg = reinterpret_cast<int32_t*>(smem) + wave * (32 * LDS_ROW);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    __syncthreads();  // the K loop's reads (first block) or the previous block's reads are done
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        stg[row * LDS_ROW + j * 32 + (lane & 31)] = acc[i][j][r] >> 8;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int sidx = 0; sidx < 32 / RSTEP; ++sidx) {
+      const int lrow_ = r0 + RSTEP * sidx;
+      const int row = m0 + wm + 32 * i + lrow_;
+      if (row >= M) continue;
+      const float sx = __half2float(a_scale[row]);
+      const int4 v0 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg);
+      const int4 v1 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg + 4);
+      const int v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      __half h[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) h[k] = __float2half_rn((float(v[k]) * sx) * sw[k]);
+      __half* crow = c + int64_t(row) * ldc + col0;
+      if (vec_c) {
+        uint4 pk;
+        __builtin_memcpy(&pk, h, 16);
+        *reinterpret_cast<uint4*>(crow) = pk;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (col0 + k < N) crow[k] = h[k];
+      }
+      if (acc_out) {
+        int32_t* arow = acc_out + int64_t(row) * ld_acc + col0;
+        if (vec_acc) {
+          *reinterpret_cast<int4*>(arow) = v0;
+          *reinterpret_cast<int4*>(arow + 4) = v1;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (col0 + k < N) arow[k] = v[k];
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+int launch_big(const uint8_t* a_q, int64_t lda, const __half* a_scale, const uint8_t* b_q,
+               int64_t ldb, const __half* b_scale, int64_t M, int64_t N, int64_t K, __half* c,
+               int64_t ldc, int32_t* acc_out, int64_t ld_acc, hipStream_t stream) {
+  const int tiles_m = int((M + C::BM - 1) / C::BM);
+  const int tiles_n = int((N + C::BN - 1) / C::BN);
+  const int64_t total = int64_t(tiles_m) * tiles_n;
+  if (total > 0x7fffffff) {
+    set_error("too many tiles");
+    return QUAROT_ERR_UNSUPPORTED;
+  }
+  hipLaunchKernelGGL(w4a4_gemm_big_kernel<C>, dim3(unsigned(total)), dim3(C::THREADS), 0, stream,
+                     a_q, lda, a_scale, b_q, ldb, b_scale, int(M), int(N), int(K), c, ldc,
+                     acc_out, ld_acc, tiles_m, tiles_n);
+  return check_launch("w4a4_gemm");
+}
+
 }  // namespace
 
 int launch_w4a4_gemm(const uint8_t* a_q, int64_t lda, const __half* a_scale,
                      const uint8_t* b_q, int64_t ldb, const __half* b_scale,
                      int64_t M, int64_t N, int64_t K, __half* c, int64_t ldc,
                      int32_t* acc_out, int64_t ld_acc, hipStream_t stream) {
+  // 256 x 256 tiles when they alone fill every CU; otherwise 128 x 256 tiles
+  // (e.g. 2048 x 4096 outputs are 128 large tiles but 256 of the smaller).
+  const int64_t big_tiles = ((M + BigCfg4::BM - 1) / BigCfg4::BM) * ((N + BigCfg4::BN - 1) / BigCfg4::BN);
+  if (big_tiles >= 256)
+    return launch_big<BigCfg4>(a_q, lda, a_scale, b_q, ldb, b_scale, M, N, K, c, ldc, acc_out,
+                               ld_acc, stream);
   return launch_cfg<Cfg8>(a_q, lda, a_scale, b_q, ldb, b_scale, M, N, K, c, ldc, acc_out,
                           ld_acc, stream);
 }

@@ -174,6 +174,37 @@ def test_gemm_extreme_codes():
     assert np.all(host(acc) == 64 * K)
 
 
+# Shapes with at least 256 output tiles of 256 x 256 run the large-tile kernel
+# (one wave per SIMD, 64-byte K tiles in a four-stage LDS ring): ragged M and
+# N edges, a partial last K tile (K % 128 != 0) and an aligned case.
+@pytest.mark.parametrize("M,N,K", [(4000, 4100, 1056), (4096, 4096, 2048), (3841, 4353, 672)])
+def test_gemm_large_tile_shapes(M, N, K):
+    rng = np.random.default_rng(M + 3 * N + 5 * K)
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, M).astype(np.float16)
+    sb = rng.uniform(0.001, 0.1, N).astype(np.float16)
+    assert ((M + 255) // 256) * ((N + 255) // 256) >= 256
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    say(f"gemm large tiles M={M} N={N} K={K}")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(sa), dev(oracle.pack_int4(qb)), dev(sb), K,
+                     acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    check_y_elementwise(host(y), y_ref)
+
+
+def test_gemm_large_tile_extreme_codes():
+    # all -8 x all -8 at the 70B down-projection shape: acc = 64 K everywhere
+    M, N, K = 4096, 4096, 28672
+    qa = dev(oracle.pack_int4(np.full((1, K), -8, np.int8))).expand(M, K // 2).contiguous()
+    say("gemm large-tile extreme codes M=N=4096 K=28672")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ones = dev(np.ones(M, np.float16))
+    qr.w4a4_gemm(qa, ones, qa, ones, K, acc_out=acc)
+    assert bool((acc == 64 * K).all())
+
+
 # ---------------------------------------------------------------------------
 # Full-size pipelines, sampled: rotate X and W on the GPU, GEMM on the GPU
 # ---------------------------------------------------------------------------
