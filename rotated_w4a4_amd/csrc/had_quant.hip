@@ -11,7 +11,7 @@
 //
 // Kernels:
 //   * had_quant_quad<D>   d = 32..256: a quad of lanes per row (quad_rows.h).
-//   * had_quant_4096_split  d = 4096: four waves per row, one LDS exchange
+//   * had_quant_4096_split  d = 4096: two waves per row, one LDS exchange
 //                         (split_rows.h).
 //   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
 //                         on the matrix cores, one LDS exchange (kron_rows.h).

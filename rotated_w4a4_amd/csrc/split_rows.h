@@ -18,11 +18,12 @@
 //            16 h + 4 g + i sits in register 8 t + 4 h + i.  Butterflies:
 //            e9, e10 (tile bits) in registers; e5, e6, e8 (lane bits 0, 1,
 //            3) by DPP.  The row goes to LDS as fp32.
-//   phase 2  wave w' = e8, lane = (e1 .. e6), register bits =
-//            (e0, e7, e9, e10, e11): two consecutive elements per read.
-//            Butterflies over e7 and e11 in registers, the row max over the
-//            workgroup, then each lane writes one byte (two codes) per
-//            register pair: 64 consecutive bytes per store instruction.
+//   phase 2  wave w' = e10, lane = (e3, e4, e5, e6, e8, e9), register
+//            bits = (e0, e1, e2, e7, e11): a lane holds runs of eight
+//            consecutive elements (two float4 reads each).  Butterflies over
+//            e7 and e11 in registers, the row max over the workgroup, then
+//            each lane packs a run's eight codes into one 32-bit word: four
+//            stores of 256 consecutive bytes per wave.
 #pragma once
 
 #include "wave_rows.h"
@@ -31,11 +32,12 @@ namespace quarot {
 
 constexpr int kSplitBlock = 128;  // two waves, one row
 
-// Float4 slot of chunk c (= element / 4) in the row's LDS copy: bits 0-3
-// are XORed with bits 3-6, so both the phase-1 writes (chunks 8 n + const
-// for the 16 lanes of a cycle) and the phase-2 reads (16 consecutive
-// chunks) hit 16 distinct 16-byte bank slots.
-__device__ __forceinline__ int split_slot(int c) { return c ^ ((c >> 3) & 15); }
+// Float4 slot of chunk c (= element / 4) in the row's LDS copy: bits 0-2
+// are XORed with bits 4-6.  Over GF(2) the low four slot bits are then a
+// bijection of chunk bits 3-6 (the phase-1 writes: chunks 8 n + const for
+// the 16 lanes of a cycle) and of chunk bits 1-4 (the phase-2 reads: chunks
+// 2 j + const), so both patterns hit 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int split_slot(int c) { return c ^ ((c >> 4) & 7); }
 
 // One DPP butterfly stage over lane bit 0, 1 or 3 (STAGE 0, 1, 2) on 32
 // registers, as v + partner * c in one v_fmac_f32 with DPP (c = +1 on the
@@ -81,10 +83,10 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
   const float c0 = (lane & 1) ? -1.0f : 1.0f;
   const float c1 = (lane & 2) ? -1.0f : 1.0f;
   const float c3 = (lane & 8) ? -1.0f : 1.0f;
-  // phase 2: e1-e6 = lane bits 0-5, e8 = the wave; the DPP stages left the
-  // sign (-1)^(e5 + e6 + e8) on every value of the lane
-  const int e2 = 2 * lane + 256 * wave;
-  const float sigma = ((((lane >> 4) & 1) ^ ((lane >> 5) & 1) ^ wave) != 0) ? -1.0f : 1.0f;
+  // phase 2: e3-e6 = lane bits 0-3, e8, e9 = lane bits 4, 5, e10 = the wave;
+  // the DPP stages left the sign (-1)^(e5 + e6 + e8) on every value of the lane
+  const int e2 = 8 * (lane & 15) + 256 * (lane >> 4) + 1024 * wave;
+  const float sigma = ((((lane >> 2) ^ (lane >> 3) ^ (lane >> 4)) & 1) != 0) ? -1.0f : 1.0f;
 
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const __half* src = x + row * ld_x + e_in;
@@ -151,17 +153,20 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
                                          v[8 * t + 4 * h + 2], v[8 * t + 4 * h + 3]);
       }
     __syncthreads();
-    // ---- phase 2: register r = e0 + 2 e7 + 4 e9 + 8 e10 + 16 e11 ---------
+    // ---- phase 2: register r = e0 + 2 e1 + 4 e2 + 8 e7 + 16 e11 ----------
+    // run u = e7 + 2 e11 starts at element e2 + 128 e7 + 2048 e11
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int e = e2 + 128 * (k & 1) + 512 * (k >> 1);
-      const float2 f = *reinterpret_cast<const float2*>(
-          reinterpret_cast<const float*>(&lds[split_slot(e >> 2)]) + (e & 3));
-      v[2 * k] = f.x;
-      v[2 * k + 1] = f.y;
+    for (int k = 0; k < 8; ++k) {
+      const int u = k >> 1;
+      const int e = e2 + 128 * (u & 1) + 2048 * (u >> 1) + 4 * (k & 1);
+      const float4 f = lds[split_slot(e >> 2)];
+      v[4 * k] = f.x;
+      v[4 * k + 1] = f.y;
+      v[4 * k + 2] = f.z;
+      v[4 * k + 3] = f.w;
     }
 #pragma unroll
-    for (int h = 2; h < 32; h <<= 3)  // e7 (h = 2), e11 (h = 16)
+    for (int h = 8; h < 32; h <<= 1)  // e7 (h = 8), e11 (h = 16)
 #pragma unroll
       for (int r = 0; r < 32; ++r)
         if ((r & h) == 0) {
@@ -190,20 +195,22 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
     const float kq = inv_scale(s16) * (1.0f / 64.0f) * rs * sigma;
     uint8_t* qrow = q_out + row * ld_q;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t t0 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * k], kq));
-      const uint32_t t1 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * k + 1], kq));
-      const int e = e2 + 128 * (k & 1) + 512 * (k >> 1);
-      qrow[e >> 1] = uint8_t(((t1 << 4) | t0) ^ 0x88u);
+    for (int u = 0; u < 4; ++u) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = magic_code<CLAMP>(v[8 * u + i], kq);
+      const int e = e2 + 128 * (u & 1) + 2048 * (u >> 1);
+      *reinterpret_cast<uint32_t*>(qrow + (e >> 1)) = pack8_magic(t);
     }
     if (threadIdx.x == 0) scale_out[row] = s16;
     if (x_rot) {
       const float cn = (1.0f / 64.0f) * rs * sigma;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = e2 + 128 * (k & 1) + 512 * (k >> 1);
-        *reinterpret_cast<float2*>(x_rot + row * 4096 + e) =
-            make_float2(v[2 * k] * cn, v[2 * k + 1] * cn);
+      for (int k = 0; k < 8; ++k) {
+        const int u = k >> 1;
+        const int e = e2 + 128 * (u & 1) + 2048 * (u >> 1) + 4 * (k & 1);
+        *reinterpret_cast<float4*>(x_rot + row * 4096 + e) =
+            make_float4(v[4 * k] * cn, v[4 * k + 1] * cn, v[4 * k + 2] * cn, v[4 * k + 3] * cn);
       }
     }
     __syncthreads();  // lds and red are reused by the next row
