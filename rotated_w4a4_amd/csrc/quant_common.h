@@ -93,12 +93,13 @@ __device__ __forceinline__ uint32_t pack8_magic(const float* t) {
 // XOR masks flipping the fp16 sign bits of 8 consecutive elements whose
 // int8 signs (+1 / -1, sign bit = bit 7) are the bytes of w0 (elements 0-3)
 // and w1 (elements 4-7).
+// Each mask word is one byte permute (sign bytes into bytes 1 and 3) and an AND.
 __device__ __forceinline__ uint4 sign_masks8(uint32_t w0, uint32_t w1) {
   uint4 m;
-  m.x = ((w0 << 8) & 0x8000u) | ((w0 << 16) & 0x80000000u);
-  m.y = ((w0 >> 8) & 0x8000u) | (w0 & 0x80000000u);
-  m.z = ((w1 << 8) & 0x8000u) | ((w1 << 16) & 0x80000000u);
-  m.w = ((w1 >> 8) & 0x8000u) | (w1 & 0x80000000u);
+  m.x = __builtin_amdgcn_perm(w0, w0, 0x010c000cu) & 0x80008000u;
+  m.y = __builtin_amdgcn_perm(w0, w0, 0x030c020cu) & 0x80008000u;
+  m.z = __builtin_amdgcn_perm(w1, w1, 0x010c000cu) & 0x80008000u;
+  m.w = __builtin_amdgcn_perm(w1, w1, 0x030c020cu) & 0x80008000u;
   return m;
 }
 
