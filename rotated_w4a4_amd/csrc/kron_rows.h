@@ -139,25 +139,29 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
   const int n = lane & 15, g = lane >> 4;
 
   // valid elements of this lane's chunk of a group: b = 8 g .. 8 g + cnt - 1
+  // (cnt is 8, 4 or 0 for m = 12 and 28)
   const int cnt = min(8, max(0, M - 8 * g));
-  // A operands: H_m rows n (and 16 + n), columns 8 g + j, zero padded
+  // Each lane loads 16 bytes (8 elements) of its group in one instruction,
+  // always inside the group: a full chunk (cnt = 8) at b = 8 g; a half chunk
+  // (cnt = 4, the group's last four elements) at b = 8 g - 4, so the wanted
+  // values sit in the upper half; lanes past m at the group start.  Halves
+  // that are not wanted are zeroed before the MFMA.
+  const int off16 = cnt == 8 ? 8 * g : (cnt == 4 ? 8 * g - 4 : 0);
+  const uint32_t keep_lo = cnt == 8 ? 0xFFFFFFFFu : 0u;
+  const uint32_t keep_hi = cnt > 0 ? 0xFFFFFFFFu : 0u;
+  // A operands: H_m rows n (and 16 + n) against the lane's K slots, zero
+  // padded: slot j pairs with column 8 g + j, or 8 g + j - 4 for a half chunk
+  const int shift = cnt == 4 ? 4 : 0;
   const HadMasks& hm = kron_masks<M>();
   const uint32_t nz_lo = hm.nz[n] >> (8 * g), neg_lo = hm.neg[n] >> (8 * g);
   const uint32_t nz_hi = hm.nz[n + 16] >> (8 * g), neg_hi = hm.neg[n + 16] >> (8 * g);
   half8_t h_lo, h_hi;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    h_lo[j] = had_entry(nz_lo, neg_lo, j);
-    h_hi[j] = had_entry(nz_hi, neg_hi, j);
+    const bool in = j >= shift;
+    h_lo[j] = in ? had_entry(nz_lo, neg_lo, j - shift) : _Float16(0.0f);
+    h_hi[j] = in ? had_entry(nz_hi, neg_hi, j - shift) : _Float16(0.0f);
   }
-  // Element offsets of this lane's phase-1 chunk in group a: lo covers
-  // b = 8 g .. 8 g + 3, hi b = 8 g + 4 .. 8 g + 7.  Lanes past m read an
-  // in-row address (the group start) and discard the value, so every load
-  // is unconditional and in bounds.
-  const int off_lo = cnt > 0 ? 8 * g : 0;
-  const int off_hi = cnt > 4 ? 8 * g + 4 : 0;
-  const uint32_t keep_lo = cnt > 0 ? 0xFFFFFFFFu : 0u;
-  const uint32_t keep_hi = cnt > 4 ? 0xFFFFFFFFu : 0u;
   // sign masks of this lane's phase-1 elements (the same for every row)
   uint4 mask[8];
   if (signs) {
@@ -165,8 +169,8 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int a = 128 * wave + 16 * t + n;
-      __builtin_memcpy(&w[t][0], signs + a * M + off_lo, 4);
-      __builtin_memcpy(&w[t][1], signs + a * M + off_hi, 4);
+      __builtin_memcpy(&w[t][0], signs + a * M + off16, 4);
+      __builtin_memcpy(&w[t][1], signs + a * M + off16 + 4, 4);
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) mask[t] = sign_masks8(w[t][0] & keep_lo, w[t][1] & keep_hi);
@@ -192,10 +196,8 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     for (int t = 0; t < 8; ++t) {
       const int a = 128 * wave + 16 * t + n;
       // (the lanes past m are masked at use: masking here would make the
-      // prefetch wait for its own data)
-      const uint2 lo = *reinterpret_cast<const uint2*>(src + a * M + off_lo);
-      const uint2 hi = *reinterpret_cast<const uint2*>(src + a * M + off_hi);
-      raw[t] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      // prefetch wait for its own data; 8-byte aligned, one dwordx4)
+      __builtin_memcpy(&raw[t], src + a * M + off16, 16);
     }
   };
 
