@@ -85,6 +85,27 @@ def test_cross_head_strided_rows():
     check(np.ascontiguousarray(big[:, :d]), nh, 1.0, qf[:, : d // 2], host(s), host(zr), 1e-2)
 
 
+@pytest.mark.parametrize("nh", [4, 32])
+def test_cross_head_unaligned_rows(nh):
+    """ld_z % 8 != 0 (4-byte aligned rows) and an odd ld_q, with clip 0.9: the
+    kernel reads only the first d elements of each row and writes only the
+    first d/2 bytes of each code row."""
+    rows = 29
+    d = nh * DH
+    rng = np.random.default_rng(11 + nh)
+    big = (rng.standard_normal((rows, d + 2)) * 2.0).astype(np.float16)
+    z_dev = dev(big)[:, :d]
+    q_full = torch.full((rows, d // 2 + 1), 0x5A, dtype=torch.uint8, device="cuda")
+    q_view = q_full[:, : d // 2]
+    s = torch.empty((rows,), dtype=torch.float16, device="cuda")
+    zr = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    say(f"unaligned: n_heads={nh} rows={rows} ld_z={d + 2} ld_q={d // 2 + 1}")
+    qr.cross_head_had_quant(z_dev, nh, 0.9, q_out=q_view, scale_out=s, z_rot_out=zr)
+    qf = host(q_full)
+    assert np.all(qf[:, d // 2:] == 0x5A)
+    check(np.ascontiguousarray(big[:, :d]), nh, 0.9, qf[:, : d // 2], host(s), host(zr), 1e-2)
+
+
 def test_cross_head_no_rows():
     z = torch.empty((0, 4 * DH), dtype=torch.float16, device="cuda")
     q, s = qr.cross_head_had_quant(z, 4)
