@@ -285,9 +285,13 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
       return QUAROT_ERR_HIP;
     }
     const size_t lds = m == 12 ? KronCfg<12>::LDS_BYTES : KronCfg<28>::LDS_BYTES;
-    const int64_t cap = cus;  // about 210-255 VGPRs: one 512-thread block per CU
+    // two waves per SIMD (up to 256 VGPRs): two 256-thread blocks per CU for
+    // m = 12, one 512-thread block for m = 28
+    const int64_t cap =
+        int64_t(cus) * (m == 12 ? KronCfg<12>::BLOCKS_PER_CU : KronCfg<28>::BLOCKS_PER_CU);
     const int64_t blocks = rows < cap ? rows : cap;
-    const dim3 grid{unsigned(blocks)}, block{unsigned(kKronBlock)};
+    const unsigned threads = m == 12 ? KronCfg<12>::THREADS : KronCfg<28>::THREADS;
+    const dim3 grid{unsigned(blocks)}, block{threads};
     const float norm = 1.0f / sqrtf(float(d));
 #define QR_KRON(MM, CL, RM)                                                                     \
   hipLaunchKernelGGL((had_quant_kron<MM, CL, RM>), grid, block, lds, stream, x, rows, ld_x, signs, \

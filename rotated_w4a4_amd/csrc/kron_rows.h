@@ -1,5 +1,6 @@
 // Rotate+quant of rows of d = 1024 * m, m = 12 or 28 (H_1024 (x) H_m):
-// one 512-thread workgroup owns one row.
+// one workgroup owns one row (m = 28: 512 threads, one per CU; m = 12: 256
+// threads, two per CU, so two rows are in flight per CU).
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
@@ -9,9 +10,10 @@
 // QuaRot paper-viz explainer builds with a Paley-12 block).
 //
 // Element e = a * m + b, a = 0..1023 (the power-of-two index), b = 0..m-1.
-//   phase 1  wave w (0..7), lane l = n + 16 g, tile t = 0..7 hold group
-//            a = 128 w + 16 t + n.  The lane loads elements b = 8 g .. 8 g + 7
-//            of its group (zero past m): the B operand of
+//   phase 1  wave w (of W = 8 or 4), lane l = n + 16 g, tile t (of 1024 /
+//            (16 W)) hold group a = (1024 / W) w + 16 t + n.  The lane loads
+//            elements b = 8 g .. 8 g + 7 of its group (zero past m) with one
+//            16-byte load inside the group: the B operand of
 //            v_mfma_f32_16x16x32_f16.  H_m (rows 0-15 and, for m = 28,
 //            16-31; zero padded to 32 x 32) is the A operand, so the dense
 //            H_m factor runs on the matrix cores on the raw sign-flipped fp16
@@ -19,9 +21,9 @@
 //            lands as b = 4 g + (0..3) and 16 + 4 g + (0..3).  Butterflies
 //            over a4-a6 (tile t) run in registers, over a0, a1, a3 (lane bits
 //            0, 1, 3) through DPP.  Valid outputs go to LDS as fp32.
-//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of BW
-//            consecutive b (4, or 2 for m = 12).  The task reads the 16
-//            values of a2, a7, a8, a9 (a float4 or float2 each), runs those
+//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of four
+//            consecutive b.  The task reads the 16 values of a2, a7, a8, a9
+//            (a float4 each), runs those
 //            four butterfly stages in registers, joins the workgroup maximum,
 //            quantises and writes 16- or 8-bit code units to LDS; the row's
 //            codes then leave in 16-byte stores.
@@ -30,8 +32,6 @@
 #include "wave_rows.h"
 
 namespace quarot {
-
-constexpr int kKronBlock = 512;
 
 // H_m as bit masks over columns, rows and columns padded to 32 with zeros:
 // row r has entry -1 where bit c of neg[r] is set, +1 where only bit c of
@@ -85,8 +85,8 @@ __device__ __forceinline__ int kron_row(int a) { return a ^ (((a >> 4) & 1) << 2
 // opens with s_nop 1; stages 1 and 2 read only what the previous stage's asm
 // blocks wrote, at least 28 instructions earlier.  The last block of stage 2
 // closes with s_nop 1 for whatever follows.
-template <int STAGE, int HALVES>
-__device__ __forceinline__ void dpp_fmac_stage(float (&v)[64], float c) {
+template <int STAGE, int HALVES, int N>
+__device__ __forceinline__ void dpp_fmac_stage(float (&v)[N], float c) {
 #define QR_FMAC_DPP(LEAD, CTRL, TRAIL)                                                       \
   asm volatile(LEAD                                                                          \
                "v_fmac_f32_dpp %0, %0, %4 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
@@ -95,9 +95,9 @@ __device__ __forceinline__ void dpp_fmac_stage(float (&v)[64], float c) {
                "v_fmac_f32_dpp %3, %3, %4 " CTRL " row_mask:0xf bank_mask:0xf" TRAIL      \
                : "+v"(v[r]), "+v"(v[r + 1]), "+v"(v[r + 2]), "+v"(v[r + 3])              \
                : "v"(c))
-  constexpr int kLast = HALVES == 1 ? 56 : 60;
+  constexpr int kLast = HALVES == 1 ? N - 8 : N - 4;
 #pragma unroll
-  for (int r = 0; r < 64; r += 4) {
+  for (int r = 0; r < N; r += 4) {
     if (HALVES == 1 && (r & 4)) continue;
     if (STAGE == 0) QR_FMAC_DPP("s_nop 1\n", "quad_perm:[1,0,3,2]", "");
     else if (STAGE == 1) QR_FMAC_DPP("", "quad_perm:[2,3,0,1]", "");
@@ -110,30 +110,40 @@ __device__ __forceinline__ void dpp_fmac_stage(float (&v)[64], float c) {
 template <int M>
 struct KronCfg {
   static constexpr int D = 1024 * M;
-  // b per phase-2 task: 4 for m = 28 (448 tasks), 2 for m = 12 (384 tasks
-  // rather than 192, so six of the eight waves share phase 2)
-  static constexpr int BW = (M == 12) ? 2 : 4;
+  // m = 12: 256-thread blocks (four waves, sixteen phase-1 tiles each), two
+  // blocks per CU, so two rows are in flight per CU with their own barriers
+  // and prefetches; m = 28 rows (112 KiB of fp32 in LDS) take the whole CU:
+  // one 512-thread block of eight waves with eight tiles each
+  static constexpr int NWAVE = (M == 12) ? 4 : 8;
+  static constexpr int THREADS = 64 * NWAVE;
+  static constexpr int TILES = 1024 / (16 * NWAVE);
+  static constexpr int BLOCKS_PER_CU = (M == 12) ? 2 : 1;
+  // the sign masks of sixteen tiles kept as their int8 words (32 registers
+  // instead of 64), expanded per row
+  static constexpr bool COMPACT_SIGNS = TILES > 8;
+  // b per phase-2 task: 4 (m = 12: 192 tasks, m = 28: 448)
+  static constexpr int BW = 4;
   static constexpr int UNITS = M / BW;      // runs of BW consecutive b per group
   static constexpr int TASKS = 64 * UNITS;  // phase-2 tasks per row
   static constexpr int HALVES = (M > 16) ? 2 : 1;
   static constexpr int LDS_BYTES = D * 4 + D / 2;  // fp32 row, then its codes
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
-  static_assert(TASKS <= kKronBlock, "one phase-2 task per thread");
+  static_assert(TASKS <= THREADS, "one phase-2 task per thread");
 };
 
 // RMS: the row is normalised by 1 / sqrt(mean(x^2) + rms_eps) first (the
 // rotation fused into RMSNorm, gain absorbed); the factor comes from the
 // rotated values (the rotation keeps the norm) and scales the quantiser.
 template <int M, bool CLAMP, bool RMS>
-__global__ __launch_bounds__(kKronBlock) void had_quant_kron(
+__global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
     const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
     float* __restrict__ x_rot, float norm, float rms_eps) {
   using C = KronCfg<M>;
   extern __shared__ float4 kron_lds[];  // the row in fp32 (phase 1 -> phase 2), then its codes
   float* buf = reinterpret_cast<float*>(kron_lds);
-  __shared__ float red[kKronBlock / 64];
-  __shared__ float red_ss[kKronBlock / 64];
+  __shared__ float red[C::NWAVE];
+  __shared__ float red_ss[C::NWAVE];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -162,21 +172,22 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     h_lo[j] = in ? had_entry(nz_lo, neg_lo, j - shift) : _Float16(0.0f);
     h_hi[j] = in ? had_entry(nz_hi, neg_hi, j - shift) : _Float16(0.0f);
   }
-  // sign masks of this lane's phase-1 elements (the same for every row)
-  uint4 mask[8];
-  if (signs) {
-    uint32_t w[8][2];
+  // signs of this lane's phase-1 elements (the same for every row): group
+  // a = (1024 / NWAVE) wave + 16 t + n.  Either the fp16 sign-bit masks
+  // (8 tiles) or the int8 sign words, expanded per row (16 tiles).
+  constexpr int TILES = C::TILES, AW = 1024 / C::NWAVE;
+  uint4 mask[C::COMPACT_SIGNS ? 1 : TILES];
+  uint2 sw[C::COMPACT_SIGNS ? TILES : 1];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int a = 128 * wave + 16 * t + n;
-      __builtin_memcpy(&w[t][0], signs + a * M + off16, 4);
-      __builtin_memcpy(&w[t][1], signs + a * M + off16 + 4, 4);
+  for (int t = 0; t < TILES; ++t) {
+    uint32_t w0 = 0, w1 = 0;
+    if (signs) {
+      const int a = AW * wave + 16 * t + n;
+      __builtin_memcpy(&w0, signs + a * M + off16, 4);
+      __builtin_memcpy(&w1, signs + a * M + off16 + 4, 4);
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) mask[t] = sign_masks8(w[t][0] & keep_lo, w[t][1] & keep_hi);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) mask[t] = make_uint4(0, 0, 0, 0);
+    if constexpr (C::COMPACT_SIGNS) sw[t] = make_uint2(w0 & keep_lo, w1 & keep_hi);
+    else mask[t] = sign_masks8(w0 & keep_lo, w1 & keep_hi);
   }
   const float s_q1 = (lane & 1) ? -1.0f : 1.0f;
   const float s_q2 = (lane & 2) ? -1.0f : 1.0f;
@@ -190,11 +201,11 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
   const float sigma = (__builtin_popcount(combo & 7) & 1) ? -1.0f : 1.0f;
 
   // loads of one row's phase-1 chunks
-  auto load_row = [&](int64_t row, uint4 (&raw)[8]) {
+  auto load_row = [&](int64_t row, uint4 (&raw)[TILES]) {
     const __half* src = x + row * ld_x;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int a = 128 * wave + 16 * t + n;
+    for (int t = 0; t < TILES; ++t) {
+      const int a = AW * wave + 16 * t + n;
       // (the lanes past m are masked at use: masking here would make the
       // prefetch wait for its own data; 8-byte aligned, one dwordx4)
       __builtin_memcpy(&raw[t], src + a * M + off16, 16);
@@ -202,18 +213,27 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
   };
 
   int64_t row = blockIdx.x;
-  uint4 raw[8];
+  uint4 raw[TILES];
   if (row < rows) load_row(row, raw);
   for (; row < rows; row += gridDim.x) {
-    float v[64];
+    float v[8 * TILES];
     // ---- phase 1: H_m on the matrix cores --------------------------------
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < TILES; ++t) {
       uint4 r = raw[t];
-      r.x = (r.x & keep_lo) ^ mask[t].x;
-      r.y = (r.y & keep_lo) ^ mask[t].y;
-      r.z = (r.z & keep_hi) ^ mask[t].z;
-      r.w = (r.w & keep_hi) ^ mask[t].w;
+      uint4 mk;
+      if constexpr (C::COMPACT_SIGNS) {
+        // (opaque per row, so the expansion is not hoisted out of the row loop)
+        uint32_t s0 = sw[t].x, s1 = sw[t].y;
+        asm volatile("" : "+v"(s0), "+v"(s1));
+        mk = sign_masks8(s0, s1);
+      } else {
+        mk = mask[t];
+      }
+      r.x = (r.x & keep_lo) ^ mk.x;
+      r.y = (r.y & keep_lo) ^ mk.y;
+      r.z = (r.z & keep_hi) ^ mk.z;
+      r.w = (r.w & keep_hi) ^ mk.w;
       const half8_t bop = __builtin_bit_cast(half8_t, r);
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       const float4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
@@ -228,11 +248,12 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     // prefetch the next row
     const int64_t nrow = row + gridDim.x;
     if (nrow < rows) load_row(nrow, raw);
-    // a4-a6: register bits 3-5
+    // a4-a6: register bits 3-5 (a7, a tile bit too with sixteen tiles, is
+    // left to phase 2)
 #pragma unroll
     for (int h = 8; h < 64; h <<= 1)
 #pragma unroll
-      for (int r = 0; r < 64; ++r)
+      for (int r = 0; r < 8 * TILES; ++r)
         if ((r & h) == 0) {
           const float a = v[r], b = v[r + h];
           v[r] = a + b;
@@ -246,8 +267,8 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     dpp_fmac_stage<2, C::HALVES>(v, s_r8);
     // valid outputs to LDS: b = 16 h + 4 g + (0..3), group a at row kron_row(a)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int a = kron_row(128 * wave + 16 * t + n);
+    for (int t = 0; t < TILES; ++t) {
+      const int a = kron_row(AW * wave + 16 * t + n);
 #pragma unroll
       for (int h = 0; h < C::HALVES; ++h) {
         const int b0 = 16 * h + 4 * g;
@@ -302,12 +323,12 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     __syncthreads();  // phase-2 reads of buf are done; red is complete
     amax = red[0];
 #pragma unroll
-    for (int w = 1; w < kKronBlock / 64; ++w) amax = fmaxf(amax, red[w]);
+    for (int w = 1; w < C::NWAVE; ++w) amax = fmaxf(amax, red[w]);
     float rs = 1.0f;
     if (RMS) {
       float tot = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kKronBlock / 64; ++w) tot += red_ss[w];
+      for (int w = 0; w < C::NWAVE; ++w) tot += red_ss[w];
       rs = rsqrtf(tot * (norm * norm / float(C::D)) + rms_eps);  // mean(x^2) = sum(v^2) / d^2
     }
     const __half s16 = row_scale_fp16(amax * norm * rs, clip_ratio);
@@ -347,10 +368,10 @@ __global__ __launch_bounds__(kKronBlock) void had_quant_kron(
     // the row's codes: D / 2 bytes, 16-byte stores.  The codes have their
     // own LDS area, so the next row's phase 1 may start while they leave.
     uint8_t* qrow = q_out + row * ld_q;
-    constexpr int kChunks = C::D / 32, kIter = (kChunks + kKronBlock - 1) / kKronBlock;
+    constexpr int kChunks = C::D / 32, kIter = (kChunks + C::THREADS - 1) / C::THREADS;
 #pragma unroll
     for (int i = 0; i < kIter; ++i) {
-      const int c = tid + kKronBlock * i;
+      const int c = tid + C::THREADS * i;
       if (i + 1 < kIter || c < kChunks)
         *reinterpret_cast<uint4*>(qrow + 16 * c) = reinterpret_cast<const uint4*>(buf + C::D)[c];
     }
