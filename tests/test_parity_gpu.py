@@ -194,6 +194,29 @@ def test_gemm_large_tile_shapes(M, N, K):
     check_y_elementwise(host(y), y_ref)
 
 
+def test_gemm_large_tile_strided_outputs():
+    # the large-tile kernel's element-wise epilogue stores (ldc % 8 != 0,
+    # accumulator row stride % 4 != 0) with ragged edges; guard bands past
+    # each row stay untouched
+    rng = np.random.default_rng(41)
+    M, N, K = 4001, 4099, 800
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, M).astype(np.float16)
+    sb = rng.uniform(0.001, 0.1, N).astype(np.float16)
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    say(f"gemm large tiles, strided outputs M={M} N={N} K={K}")
+    ybuf = torch.full((M, N + 3), 7.0, dtype=torch.float16, device="cuda")
+    abuf = torch.full((M, N + 5), -123, dtype=torch.int32, device="cuda")
+    qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(sa), dev(oracle.pack_int4(qb)), dev(sb), K,
+                 out=ybuf[:, :N], acc_out=abuf[:, :N])
+    yh, ah = host(ybuf), host(abuf)
+    np.testing.assert_array_equal(ah[:, :N], acc_ref)
+    assert np.all(ah[:, N:] == -123)
+    assert np.all(yh[:, N:] == np.float16(7.0))
+    check_y_elementwise(yh[:, :N], y_ref)
+
+
 def test_gemm_large_tile_extreme_codes():
     # all -8 x all -8 at the 70B down-projection shape: acc = 64 K everywhere
     M, N, K = 4096, 4096, 28672
