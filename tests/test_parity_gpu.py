@@ -194,6 +194,25 @@ def test_gemm_large_tile_shapes(M, N, K):
     check_y_elementwise(host(y), y_ref)
 
 
+# K shorter than the ring: no full K tile (the partial tile only), one, two
+# or three full tiles, with the prologue's copies clamped to the last full tile.
+@pytest.mark.parametrize("K", [32, 96, 128, 256, 384, 416])
+def test_gemm_large_tile_short_k(K):
+    M, N = 4096, 4112
+    rng = np.random.default_rng(K)
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, M).astype(np.float16)
+    sb = rng.uniform(0.001, 0.1, N).astype(np.float16)
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    say(f"gemm large tiles, short K: M={M} N={N} K={K}")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(sa), dev(oracle.pack_int4(qb)), dev(sb), K,
+                     acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    check_y_elementwise(host(y), y_ref)
+
+
 def test_gemm_large_tile_strided_outputs():
     # the large-tile kernel's element-wise epilogue stores (ldc % 8 != 0,
     # accumulator row stride % 4 != 0) with ragged edges; guard bands past
