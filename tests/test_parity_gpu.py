@@ -400,11 +400,12 @@ def test_had_quant_no_signs_single_row_and_determinism():
 @pytest.mark.parametrize("m", [12, 28])
 @pytest.mark.parametrize("clip", [1.0, 0.9])
 def test_had_quant_kron_rows_strided_grid_stride(m, clip):
-    # d = 1024 m takes the Kronecker kernel; 300 rows exceed one block per
-    # compute unit, so blocks walk several rows and prefetch the next one
+    # d = 1024 m takes the Kronecker kernel; the rows exceed the blocks it
+    # launches (two per compute unit for m = 12, one for m = 28), so blocks
+    # walk several rows and prefetch the next one
     rng = np.random.default_rng(100 + m)
     d = 1024 * m
-    rows, ld = 300, 1024 * m + 96
+    rows, ld = (600 if m == 12 else 300), 1024 * m + 96
     buf = rng.standard_normal((rows, ld)).astype(np.float32)
     buf[:, rng.integers(0, d, 3)] *= 60.0
     buf = buf.astype(np.float16)
