@@ -541,11 +541,11 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_big_kernel(
   // K-pair g = 2 kt + kp.  Step g reads K-pair g + 2 (tile kt + 1, same kp)
   // into register set g % 2, widens K-pair g + 1 into the other widened set
   // and runs the MFMAs of K-pair g.  Iteration kt starts by waiting until
-  // tile kt + 1 has landed (its copy was issued two iterations earlier; only
-  // tile kt + 2's copy may still be in flight) and a barrier, after which
-  // every wave has consumed tile kt - 1, so its stage takes the copy of
-  // tile kt + 3.  Copies past the last full tile repeat it into stages that
-  // are never read as real data.
+  // tile kt + 1 has landed (its copy was issued NST - 2 iterations earlier;
+  // only the copies of tiles kt + 2 .. kt + NST - 2 may still be in flight)
+  // and a barrier, after which every wave has consumed tile kt - 1, so its
+  // stage takes the copy of tile kt + NST - 1.  Copies past the last full
+  // tile repeat it into stages that are never read as real data.
   if (kfull > 0) {
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t) QB_COPY(t, t);
