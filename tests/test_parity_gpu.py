@@ -236,6 +236,31 @@ def test_gemm_large_tile_strided_outputs():
     check_y_elementwise(yh[:, :N], y_ref)
 
 
+# Packed A and B rows inside wider buffers (lda, ldb > K/2, multiples of 16)
+# whose padding bytes hold random codes: a read past the K/2 bytes of a row
+# would add them to the sums.  Both the 64 x 64-tile and the large-tile kernel.
+@pytest.mark.parametrize("M,N,K", [(300, 520, 800), (4000, 4100, 1056)])
+def test_gemm_strided_inputs(M, N, K):
+    rng = np.random.default_rng(M + N + K + 17)
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.01, 2.0, M).astype(np.float16)
+    sb = rng.uniform(0.001, 0.1, N).astype(np.float16)
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    lda, ldb = K // 2 + 16, K // 2 + 48
+    abuf = rng.integers(0, 256, size=(M, lda), dtype=np.uint8)
+    bbuf = rng.integers(0, 256, size=(N, ldb), dtype=np.uint8)
+    abuf[:, : K // 2] = oracle.pack_int4(qa)
+    bbuf[:, : K // 2] = oracle.pack_int4(qb)
+    say(f"gemm strided inputs M={M} N={N} K={K} lda={lda} ldb={ldb}")
+    a_dev, b_dev = dev(abuf)[:, : K // 2], dev(bbuf)[:, : K // 2]
+    assert a_dev.stride(0) == lda and b_dev.stride(0) == ldb
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(a_dev, dev(sa), b_dev, dev(sb), K, acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    check_y_elementwise(host(y), y_ref)
+
+
 def test_gemm_large_tile_extreme_codes():
     # all -8 x all -8 at the 70B down-projection shape: acc = 64 K everywhere
     M, N, K = 4096, 4096, 28672
