@@ -160,7 +160,9 @@ int quarot_cross_head_had_quant(const void* z, int64_t rows, int64_t n_heads, in
  *   acc_out    optional int32 [M x ld_acc] receiving acc (ld_acc >= N);
  *              NULL in production.
  * Supported: M, N >= 0 (0 is a no-op), K > 0 with K % 32 == 0 and
- * K <= 65536 (so 256 * |acc| <= 256 * 64 K fits in int32).
+ * K <= 65536 (so 256 * |acc| <= 256 * 64 K fits in int32); M, N < 2^31,
+ * else UNSUPPORTED (as is a grid of 2^32 or more work items, which takes
+ * over 10^12 outputs).
  */
 int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
                      const uint8_t* b_q, int64_t ldb, const void* b_scale,
@@ -274,8 +276,9 @@ int quarot_kv_had_quant(const void* k, const void* v,
  *                on entry do not matter.  Calls that share a workspace must
  *                be ordered (one stream).
  * Errors: INVALID for bad sizes, mode, scale, missing buffers or a short
- * workspace; UNSUPPORTED for D != 128, Hq / Hkv > 8, max_len > 2^24, or
- * cross_head with Hq not a power of two <= 256; MISALIGNED as stated.
+ * workspace; UNSUPPORTED for D != 128, Hq / Hkv > 8, max_len > 2^24,
+ * B * Hkv >= 2^24, or cross_head with Hq not a power of two <= 256;
+ * MISALIGNED as stated.
  */
 int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
                                const int8_t* signs, int64_t signs_stride_h, int32_t mode,

@@ -252,7 +252,10 @@ int decode_shape_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_l
   QR_CHECK_ARG(max_len >= 1, QUAROT_ERR_INVALID, "max_len = %lld < 1", (long long)max_len);
   QR_CHECK_ARG(max_len <= (int64_t(1) << 24), QUAROT_ERR_UNSUPPORTED,
                "max_len = %lld > 2^24 (32-bit buffer offsets)", (long long)max_len);
-  QR_CHECK_ARG(B * Hkv < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED, "B * Hkv too large");
+  // one 256-thread workgroup per (b, kv head) in the first grid dimension,
+  // whose work-item count must stay below 2^32
+  QR_CHECK_ARG(B * Hkv < (int64_t(1) << 24), QUAROT_ERR_UNSUPPORTED, "B * Hkv = %lld >= 2^24",
+               (long long)(B * Hkv));
   return QUAROT_OK;
 }
 

@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int kRowsPerBlock = 4;  // one wave per row
+constexpr int64_t kMaxBlocks = int64_t(1) << 16;
 
 template <int NH>
 __device__ __forceinline__ constexpr float head_norm() {
@@ -43,64 +44,71 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void cross_head_quant_kernel(
     uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
     float* __restrict__ z_rot) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;  // uniform per wave; no barrier follows
-  const __half* src = z + row * ld_z + 2 * lane;
+  // one wave per row; rows are uniform per wave and no barrier follows, so
+  // the waves stride over the rows independently
+  const int64_t stride = int64_t(gridDim.x) * kRowsPerBlock;
+  for (int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6); row < rows;
+       row += stride) {
+    const __half* src = z + row * ld_z + 2 * lane;
 
-  uint32_t raw[NH];
+    uint32_t raw[NH];
 #pragma unroll
-  for (int h = 0; h < NH; ++h) raw[h] = *reinterpret_cast<const uint32_t*>(src + h * kHeadDim);
+    for (int h = 0; h < NH; ++h) raw[h] = *reinterpret_cast<const uint32_t*>(src + h * kHeadDim);
 
-  float v0[NH], v1[NH];
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    const float2 f = __half22float2(__builtin_bit_cast(__half2, raw[h]));
-    v0[h] = f.x;
-    v1[h] = f.y;
-  }
-  // unnormalised Sylvester transform over the head index
-#pragma unroll
-  for (int s = 1; s < NH; s <<= 1) {
+    float v0[NH], v1[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      if ((h & s) == 0) {
-        const float a0 = v0[h], b0 = v0[h + s];
-        const float a1 = v1[h], b1 = v1[h + s];
-        v0[h] = a0 + b0;
-        v0[h + s] = a0 - b0;
-        v1[h] = a1 + b1;
-        v1[h + s] = a1 - b1;
+      const float2 f = __half22float2(__builtin_bit_cast(__half2, raw[h]));
+      v0[h] = f.x;
+      v1[h] = f.y;
+    }
+    // unnormalised Sylvester transform over the head index
+#pragma unroll
+    for (int s = 1; s < NH; s <<= 1) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        if ((h & s) == 0) {
+          const float a0 = v0[h], b0 = v0[h + s];
+          const float a1 = v1[h], b1 = v1[h + s];
+          v0[h] = a0 + b0;
+          v0[h + s] = a0 - b0;
+          v1[h] = a1 + b1;
+          v1[h + s] = a1 - b1;
+        }
       }
     }
-  }
-  float amax = 0.0f;
+    float amax = 0.0f;
 #pragma unroll
-  for (int h = 0; h < NH; ++h) amax = fmaxf(amax, fmaxf(fabsf(v0[h]), fabsf(v1[h])));
-  amax = wave_max_dpp(amax);
+    for (int h = 0; h < NH; ++h) amax = fmaxf(amax, fmaxf(fabsf(v0[h]), fabsf(v1[h])));
+    amax = wave_max_dpp(amax);
 
-  constexpr float kNorm = head_norm<NH>();
-  const __half s16 = row_scale_fp16(amax * kNorm, clip_ratio);
-  const float kq = inv_scale(s16) * kNorm;
-  uint8_t* qrow = q_out + row * ld_q + lane;
+    constexpr float kNorm = head_norm<NH>();
+    const __half s16 = row_scale_fp16(amax * kNorm, clip_ratio);
+    const float kq = inv_scale(s16) * kNorm;
+    uint8_t* qrow = q_out + row * ld_q + lane;
 #pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    const uint32_t c0 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v0[h], kq));
-    const uint32_t c1 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v1[h], kq));
-    // byte 0 of each is q + 8; xor 8 gives the 4-bit two's complement
-    qrow[h * (kHeadDim / 2)] = static_cast<uint8_t>((((c1 << 4) | (c0 & 0xFu)) ^ 0x88u) & 0xFFu);
-  }
-  if (lane == 0) scale_out[row] = s16;
-  if (z_rot) {
-    float2* dst = reinterpret_cast<float2*>(z_rot + row * (NH * kHeadDim) + 2 * lane);
+    for (int h = 0; h < NH; ++h) {
+      const uint32_t c0 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v0[h], kq));
+      const uint32_t c1 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v1[h], kq));
+      // byte 0 of each is q + 8; xor 8 gives the 4-bit two's complement
+      qrow[h * (kHeadDim / 2)] = static_cast<uint8_t>((((c1 << 4) | (c0 & 0xFu)) ^ 0x88u) & 0xFFu);
+    }
+    if (lane == 0) scale_out[row] = s16;
+    if (z_rot) {
+      float2* dst = reinterpret_cast<float2*>(z_rot + row * (NH * kHeadDim) + 2 * lane);
 #pragma unroll
-    for (int h = 0; h < NH; ++h) dst[h * (kHeadDim / 2)] = make_float2(v0[h] * kNorm, v1[h] * kNorm);
+      for (int h = 0; h < NH; ++h) dst[h * (kHeadDim / 2)] = make_float2(v0[h] * kNorm, v1[h] * kNorm);
+    }
   }
 }
 
 template <int NH>
 int launch_nh(const __half* z, int64_t rows, int64_t ld_z, float clip_ratio, uint8_t* q_out,
               int64_t ld_q, __half* scale_out, float* z_rot, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  // at most 2^16 blocks (the waves loop over further rows), so the grid's
+  // work-item count stays far below 2^32
+  const int64_t blocks = std::min<int64_t>((rows + kRowsPerBlock - 1) / kRowsPerBlock, kMaxBlocks);
+  const dim3 grid(static_cast<unsigned>(blocks));
   const dim3 block(64 * kRowsPerBlock);
   if (clip_ratio < 1.0f)
     hipLaunchKernelGGL((cross_head_quant_kernel<NH, true>), grid, block, 0, stream, z, rows, ld_z,

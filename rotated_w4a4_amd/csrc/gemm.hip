@@ -380,7 +380,7 @@ int launch_cfg(const uint8_t* a_q, int64_t lda, const __half* a_scale, const uin
   const int tiles_m = int((M + C::BM - 1) / C::BM);
   const int tiles_n = int((N + C::BN - 1) / C::BN);
   const int64_t total = int64_t(tiles_m) * tiles_n;
-  if (total > 0x7fffffff) {
+  if (total * C::THREADS > 0xffffffffLL) {  // work items of one grid dimension
     set_error("too many tiles");
     return QUAROT_ERR_UNSUPPORTED;
   }
@@ -667,7 +667,7 @@ int launch_big(const uint8_t* a_q, int64_t lda, const __half* a_scale, const uin
   const int tiles_m = int((M + C::BM - 1) / C::BM);
   const int tiles_n = int((N + C::BN - 1) / C::BN);
   const int64_t total = int64_t(tiles_m) * tiles_n;
-  if (total > 0x7fffffff) {
+  if (total * C::THREADS > 0xffffffffLL) {  // work items of one grid dimension
     set_error("too many tiles");
     return QUAROT_ERR_UNSUPPORTED;
   }

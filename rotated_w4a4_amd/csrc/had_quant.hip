@@ -223,7 +223,9 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
   if (m == 1 && d <= 256) {
     const int64_t rpb = kQuadBlock / 4;
     int64_t blocks = (rows + rpb - 1) / rpb;
-    const int64_t cap = int64_t(1) << 24;  // grid limit; beyond it blocks loop
+    // at most 2^16 blocks (beyond, blocks loop), far below the 2^32
+    // work-item limit of a grid dimension
+    const int64_t cap = int64_t(1) << 16;
     if (blocks > cap) blocks = cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kQuadBlock)};
 #define QR_QUAD(DD, CL, RM)                                                                    \

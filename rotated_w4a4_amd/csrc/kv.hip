@@ -118,7 +118,9 @@ int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t
   const int64_t groups = B * H * S;
   const int64_t per_block = kBlock / 4;
   int64_t blocks = (groups + per_block - 1) / per_block;
-  const int64_t cap = int64_t(1) << 24;  // grid limit; beyond it blocks loop
+  // at most 2^16 blocks (beyond, blocks loop), far below the 2^32 work-item
+  // limit of a grid dimension
+  const int64_t cap = int64_t(1) << 16;
   if (blocks > cap) blocks = cap;
   const dim3 grid{unsigned(blocks), unsigned(n_tensors)}, block{unsigned(kBlock)};
 #define QR_KV(DD, CL, MD) \
