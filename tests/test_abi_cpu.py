@@ -121,6 +121,10 @@ def _gemm(lib, **kw):
     (dict(sa=FAKE + 1), MISALIGNED),
     (dict(c=FAKE + 1), MISALIGNED),
     (dict(acc=FAKE + 2, ld_acc=16), MISALIGNED),
+    (dict(M=1 << 31), UNSUPPORTED),
+    # 2^36 tiles of 256 x 256: more work items than a grid dimension holds;
+    # rejected on the host before any launch
+    (dict(M=(1 << 31) - 1, N=(1 << 31) - 1, ldc=(1 << 31) - 1), UNSUPPORTED),
 ])
 def test_gemm_rejects(lib, kw, status):
     assert _gemm(lib, **kw) == status
@@ -198,6 +202,7 @@ def _dec(lib, **kw):
     (dict(max_len=0), INVALID),
     (dict(max_len=513), INVALID),
     (dict(max_len=(1 << 24) + 1, S_cache=1 << 25), UNSUPPORTED),
+    (dict(B=1 << 21, Hq=64, Hkv=8), UNSUPPORTED),  # 2^24 workgroups of 256 threads
     (dict(ssh=-1), INVALID),
     (dict(q=None), INVALID),
     (dict(vs=None), INVALID),
