@@ -36,7 +36,10 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int GROUP_M = 4;
+// Tiles are taken in groups of GROUP_M along M. With the XCD-major order an
+// XCD's share of a 2048 x 4096 launch is then 8 x 4 tiles of 128 x 256
+// (1024 A rows and 1024 B rows through its L2), not 4 x 8 (512 and 2048).
+constexpr int GROUP_M = 8;
 
 // LDS holds one K tile per buffer, row-major with BKB-byte rows (no
 // padding).  The LDS has 64 four-byte banks and serves a 128-bit read for 16
