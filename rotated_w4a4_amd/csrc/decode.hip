@@ -532,8 +532,15 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
   constexpr int W = kCombineDims;
   const int b = blockIdx.x, d0 = W * blockIdx.y;
   const int total = p.hq * W;
+  // With at most 64 query heads, thread idx takes head idx % Hq and dim
+  // idx / Hq: the heads of one dim sit on the lanes of one wave, and the
+  // transform over the head index is a chain of lane shuffles (no LDS, no
+  // barriers).  Every thread then runs exactly one iteration (blockDim.x is
+  // total), and partner lanes idx ^ h (h < Hq) are threads of the block.
+  const bool on_lanes = CROSS && p.hq <= 64;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int hq = idx / W, dl = idx % W;
+    const int hq = on_lanes ? (idx & (p.hq - 1)) : idx / W;
+    const int dl = on_lanes ? (idx / p.hq) : idx % W;
     const int kv = hq / p.group, gi = hq - kv * p.group;
     const int64_t s0 = (int64_t(b) * p.hkv + kv) * p.splits;
     float big = -INFINITY, lsum = 0.0f, o = 0.0f;
@@ -566,7 +573,17 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
       big = nb;
     }
     const float res = lsum > 0.0f ? o / lsum : 0.0f;
-    if (CROSS) {
+    if (CROSS && on_lanes) {
+      float v = res;
+      for (int h = 1; h < p.hq; h <<= 1) {
+        const float w = __shfl_xor(v, h);
+        v = (hq & h) ? w - v : v + w;
+      }
+      v *= 1.0f / sqrtf(float(p.hq));
+      const int64_t at = (int64_t(b) * p.hq + hq) * kDecD + d0 + dl;
+      p.out[at] = __float2half_rn(v);
+      if (p.out_f32) p.out_f32[at] = v;
+    } else if (CROSS) {
       zs[idx] = res;
     } else {
       const int64_t at = (int64_t(b) * p.hq + hq) * kDecD + d0 + dl;
@@ -574,7 +591,7 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
       if (p.out_f32) p.out_f32[at] = res;
     }
   }
-  if (!CROSS) return;
+  if (!CROSS || on_lanes) return;
   __syncthreads();
   const int half_total = total / 2;
   for (int h = 1; h < p.hq; h <<= 1) {

@@ -93,6 +93,8 @@ CASES = [
     (4, 8, 8, 256, 200, [200, 50, 3, 17], 0, False, True),
     (2, 2, 6, 96, 96, [96, 95], 0, False, False),        # group of 3 (not a power of two)
     (1, 1, 1, 33, 33, None, 1, False, False),            # one head, 33 positions
+    (2, 16, 128, 160, 160, [160, 77], 0, True, False),   # cross-head over 128 heads (LDS path)
+    (2, 1, 2, 64, 64, None, 0, True, False),             # cross-head over 2 heads (lane path)
 ]
 
 
