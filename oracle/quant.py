@@ -20,9 +20,11 @@ other readings of the pages in the design notes):
 
 * The scale is stored in fp16 and the codes are computed from the stored
   (fp16-rounded) scale, so stored scales and codes always agree.
-* The rounding decision x / S -> integer is taken in fp32, the precision the
-  pages give for the online Hadamard output: x~ is rounded to fp32, divided by
-  the fp16 scale in fp32, and rounded half to even.
+* The rounding decision x / S -> integer is the definition evaluated exactly:
+  the float64 rotated value divided by the stored scale widened to float64,
+  rounded half to even (``np.rint``).  A kernel that rotates in fp32 can land
+  on the other side of a rounding boundary on a few elements; that is what
+  the code tolerance of the parity tests measures.
 * Nibble order: element 2k goes to the low nibble of byte k, element 2k+1 to
   the high nibble; each nibble is the 4-bit two's complement of the code.
 * An all-zero row keeps the 1e-5 floor: its scale is fp16(clip * 1e-5 / 7)
@@ -65,10 +67,10 @@ def row_scales(x_rot: np.ndarray, clip_ratio: float = 1.0) -> np.ndarray:
 
 
 def codes_from_scales(x_rot: np.ndarray, scales16: np.ndarray) -> np.ndarray:
-    """q = clamp(rint(fp32(x) / fp32(S)), -8, 7), one scale per row (int8)."""
-    x32 = np.asarray(x_rot).astype(np.float32)
-    s32 = np.asarray(scales16, dtype=np.float16).astype(np.float32)[:, None]
-    r = np.rint(x32 / s32)  # float32 division, ties to even
+    """q = clamp(rint(x / float64(S)), -8, 7), one scale per row (int8)."""
+    x64 = np.asarray(x_rot, dtype=np.float64)
+    s64 = np.asarray(scales16, dtype=np.float16).astype(np.float64)[:, None]
+    r = np.rint(x64 / s64)  # float64 division, ties to even
     return np.clip(r, QMIN, QMAX).astype(np.int8)
 
 
@@ -117,9 +119,9 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
 #   q = clamp(rint(x / S) + z, 0, 15)                     (uint4 code)
 #   x_hat = S * (q - z)
 # with the same precision conventions as the symmetric quantiser: S is the
-# stored fp16 scale; alpha and the zero-point division are taken in fp32
-# (the fp32 value of x~), x / S in fp32 with ties to even; z is kept within
-# +-ZMAX so it is exactly representable in the fp16 it is stored in.
+# stored fp16 scale (rounded once from the float64 range); alpha, the
+# zero-point division and x / S are float64 with ties to even; z is kept
+# within +-ZMAX so it is exactly representable in the fp16 it is stored in.
 # ---------------------------------------------------------------------------
 
 ZMAX = 1024
@@ -130,22 +132,22 @@ def asym_params(x_rot: np.ndarray, clip_ratio: float = 0.95):
     """Per-row (scale fp16, zero point int32) of the asymmetric quantiser."""
     if not (0.0 < clip_ratio <= 1.0):
         raise ValueError("clip_ratio must be in (0, 1]")
-    x32 = np.asarray(x_rot).astype(np.float32)
-    c = np.float32(clip_ratio)
-    amin = c * x32.min(axis=1)
-    amax = c * x32.max(axis=1)
-    rng = np.maximum(amax - amin, np.float32(ABSMAX_FLOOR))
-    s16 = (rng / np.float32(UQMAX)).astype(np.float16)
-    z = np.rint(-amin / s16.astype(np.float32))
+    x64 = np.asarray(x_rot, dtype=np.float64)
+    c = float(clip_ratio)
+    amin = c * x64.min(axis=1)
+    amax = c * x64.max(axis=1)
+    rng = np.maximum(amax - amin, ABSMAX_FLOOR)
+    s16 = (rng / UQMAX).astype(np.float16)
+    z = np.rint(-amin / s16.astype(np.float64))
     z = np.clip(z, -ZMAX, ZMAX).astype(np.int32)
     return s16, z
 
 
 def asym_codes(x_rot: np.ndarray, scales16: np.ndarray, zeros: np.ndarray) -> np.ndarray:
-    """q = clamp(rint(fp32(x) / fp32(S)) + z, 0, 15), one (S, z) per row (uint8)."""
-    x32 = np.asarray(x_rot).astype(np.float32)
-    s32 = np.asarray(scales16, dtype=np.float16).astype(np.float32)[:, None]
-    r = np.rint(x32 / s32) + np.asarray(zeros, dtype=np.float32)[:, None]
+    """q = clamp(rint(x / float64(S)) + z, 0, 15), one (S, z) per row (uint8)."""
+    x64 = np.asarray(x_rot, dtype=np.float64)
+    s64 = np.asarray(scales16, dtype=np.float16).astype(np.float64)[:, None]
+    r = np.rint(x64 / s64) + np.asarray(zeros, dtype=np.float64)[:, None]
     return np.clip(r, 0, UQMAX).astype(np.uint8)
 
 

@@ -46,6 +46,16 @@ def test_ties_round_to_even():
     np.testing.assert_array_equal(q, want)
 
 
+def test_decision_is_taken_on_the_exact_value():
+    # x / S a hair above or below k + 1/2: rint of the exact quotient (ties
+    # to even only at an exact tie).  A decision taken on fp32-rounded values
+    # would see 2.5 and 4.5 here and round both to even.
+    s = np.array([np.float16(1.0)])
+    x = np.array([[2.5 + 2.0 ** -40, 4.5 - 2.0 ** -40, -2.5 - 2.0 ** -40, 2.5]])
+    assert np.float32(x[0, 0]) == np.float32(2.5)  # the fp32 view is a tie
+    np.testing.assert_array_equal(codes_from_scales(x, s)[0], [3, 4, -3, 2])
+
+
 def test_absmax_maps_to_seven():
     rng = np.random.default_rng(5)
     x = rng.standard_normal((50, 333))
