@@ -158,22 +158,23 @@ def paley1(q: int) -> np.ndarray:
     return h.astype(np.int8)
 
 
-SUPPORTED_M = (1, 12, 28)
+# Orders with a Paley type-I matrix here: q = m - 1 a prime (or 27) with
+# q = 3 mod 4.  (16 has none: 15 is not a prime power.)
+SUPPORTED_M = (1, 4, 8, 12, 20, 24, 28, 32)
 
 
 @functools.lru_cache(maxsize=None)
 def _hadamard_m_cached(m: int) -> bytes:
     if m == 1:
         h = np.ones((1, 1), dtype=np.int8)
-    elif m == 12:
-        h = paley1(11)
-    elif m == 28:
-        h = paley1(27)
+    elif m in SUPPORTED_M:
+        h = paley1(m - 1)
     else:
         raise ValueError(f"no small Hadamard factor of order {m} (have {SUPPORTED_M})")
     return h.tobytes()
 
 
 def hadamard_m(m: int) -> np.ndarray:
-    """The small Kronecker factor H_m used for d = 2^n * m (int8 [m x m])."""
+    """The small Kronecker factor H_m used for d = 2^n * m (int8 [m x m]):
+    [1] for m = 1, else the Paley type-I matrix of order m."""
     return np.frombuffer(_hadamard_m_cached(m), dtype=np.int8).reshape(m, m).copy()

@@ -7,10 +7,13 @@
   Guide", step 1 of "Deep Dive"): the same R is applied to each output
   channel's row of W [n_out x d] (W~ = W R^T), so X~ W~^T = X W^T; then one
   symmetric scale per output channel (max/7, round to nearest) and pack.
-* RMSNorm producer ("QuaRot Guide", step 2 of "Deep Dive", "Online Activation
-  Rotation Fused into RMSNorm"): the normalised row x / sqrt(mean(x^2) + eps)
-  is rotated and quantised per token.  The RMSNorm gain is absorbed into the
-  next weights (paper-graph-ui summary, Stage 1a), so no gain is applied.
+* Gated FFN producer (paper-graph-ui summary, section 3.4 "FFN Activation
+  Rotation (Stage 1b)"): the down-projection's input is the SwiGLU product
+  c = SiLU(A) * B, SiLU(t) = t * sigmoid(t) = t / (1 + exp(-t)), and the
+  online Hadamard is applied to c; fusing it into its producer is the
+  kernel improvement the page's section 6 names.  The product is formed in
+  float64 and rotated without an intermediate fp16 rounding (the fused
+  kernel never stores it).
 * Out-projection input (same page, Stage 1c "Attention Value Projection
   Rotation"): the concatenated attention output Z gets the online cross-head
   transform Z (H_{n_h} (x) I_{d_h}) (no random signs: the head-wise factor
@@ -34,29 +37,29 @@ from .quant import pack_int4, pack_uint4, quantize_rows, quantize_rows_asym
 from .rotate import rotate_rows
 
 __all__ = ["had_quant", "prep_weights", "w4a4_linear", "kv_had_quant", "kv_had_quant_asym",
-           "rmsnorm", "rmsnorm_had_quant", "cross_head_quant"]
+           "silu", "swiglu", "swiglu_had_quant", "cross_head_quant"]
 
 
-def had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0):
-    """Rotate+quant rows of x.
+def had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0, hm=None):
+    """Rotate+quant rows of x (hm: the small factor H_m, default Paley).
 
     Returns dict(x_rot float64, codes int8, packed uint8 [rows x d/2], scales fp16).
     """
-    x_rot = rotate_rows(x, signs, m)
+    x_rot = rotate_rows(x, signs, m, hm)
     codes, scales = quantize_rows(x_rot, clip_ratio)
     return {"x_rot": x_rot, "codes": codes, "packed": pack_int4(codes), "scales": scales}
 
 
-def prep_weights(w: np.ndarray, signs: np.ndarray, m: int = 1):
+def prep_weights(w: np.ndarray, signs: np.ndarray, m: int = 1, hm=None):
     """Offline weight prep: W~ = W R^T, per-output-channel max/7 RTN, pack."""
-    return had_quant(w, signs, m, clip_ratio=1.0)
+    return had_quant(w, signs, m, clip_ratio=1.0, hm=hm)
 
 
 def w4a4_linear(x: np.ndarray, w: np.ndarray, signs: np.ndarray, m: int = 1,
-                clip_ratio: float = 1.0):
+                clip_ratio: float = 1.0, hm=None):
     """The whole quantised linear layer: returns acts, weights, acc and y."""
-    a = had_quant(x, signs, m, clip_ratio)
-    b = prep_weights(w, signs, m)
+    a = had_quant(x, signs, m, clip_ratio, hm)
+    b = prep_weights(w, signs, m, hm)
     acc, y = w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
     return {"act": a, "wgt": b, "acc": acc, "y": y}
 
@@ -97,17 +100,22 @@ def kv_had_quant_asym(t: np.ndarray, signs: np.ndarray, clip_ratio: float = 0.95
     }
 
 
-def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
-    """Row-wise x / sqrt(mean(x^2) + eps) in float64 (gain absorbed: none)."""
-    x = np.asarray(x, dtype=np.float64)
-    ms = np.mean(x * x, axis=1, keepdims=True)
-    return x / np.sqrt(ms + eps)
+def silu(t: np.ndarray) -> np.ndarray:
+    """SiLU(t) = t / (1 + exp(-t)) in float64 (-0 where exp(-t) overflows)."""
+    t = np.asarray(t, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(-t))
 
 
-def rmsnorm_had_quant(x: np.ndarray, signs: np.ndarray, m: int = 1, clip_ratio: float = 1.0,
-                      eps: float = 1e-5):
-    """RMSNorm, then rotate+quant: had_quant(rmsnorm(x, eps))."""
-    return had_quant(rmsnorm(x, eps), signs, m, clip_ratio)
+def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """The gated FFN product SiLU(gate) * up, elementwise, float64."""
+    return silu(gate) * np.asarray(up, dtype=np.float64)
+
+
+def swiglu_had_quant(gate: np.ndarray, up: np.ndarray, signs: np.ndarray, m: int = 1,
+                     clip_ratio: float = 1.0, hm=None):
+    """Rotate+quant of the gated product: had_quant(SiLU(gate) * up)."""
+    return had_quant(swiglu(gate, up), signs, m, clip_ratio, hm)
 
 
 def cross_head_quant(z: np.ndarray, n_heads: int, clip_ratio: float = 1.0):

@@ -38,22 +38,33 @@ def split_d(d: int, m: int) -> int:
     return p.bit_length() - 1
 
 
-def dense_rotation(d: int, signs: np.ndarray, m: int = 1) -> np.ndarray:
+def _factor(m: int, hm) -> np.ndarray:
+    """H_m as float64: the given matrix, or the Paley matrix of order m."""
+    if hm is None:
+        return hadamard_m(m).astype(np.float64)
+    h = np.asarray(hm)
+    if h.shape != (m, m):
+        raise ValueError(f"hm must be [{m} x {m}]")
+    return h.astype(np.float64)
+
+
+def dense_rotation(d: int, signs: np.ndarray, m: int = 1, hm=None) -> np.ndarray:
     """The full rotation R = (H_{2^n} (x) H_m) diag(s) / sqrt(d), float64 [d x d]."""
     n = split_d(d, m)
-    h = np.kron(sylvester(1 << n).astype(np.float64), hadamard_m(m).astype(np.float64))
+    h = np.kron(sylvester(1 << n).astype(np.float64), _factor(m, hm))
     return h * signs.astype(np.float64)[None, :] / math.sqrt(d)
 
 
-def rotate_rows(x: np.ndarray, signs: np.ndarray, m: int = 1,
+def rotate_rows(x: np.ndarray, signs: np.ndarray, m: int = 1, hm=None,
                 chunk_rows: int = 256) -> np.ndarray:
-    """x~ = R x for every row of x (any real dtype in, float64 out)."""
+    """x~ = R x for every row of x (any real dtype in, float64 out).  hm: the
+    small factor H_m (default: the Paley matrix of order m)."""
     x = np.asarray(x)
     rows, d = x.shape
     n = split_d(d, m)
     p = 1 << n
     h2 = sylvester(p).astype(np.float64)
-    hm = hadamard_m(m).astype(np.float64)
+    hm = _factor(m, hm)
     s = signs.astype(np.float64)
     inv = 1.0 / math.sqrt(d)
     out = np.empty((rows, d), dtype=np.float64)

@@ -55,7 +55,7 @@ def test_one_hot_spreads_evenly():
     assert np.isclose(np.linalg.norm(y), 1.0, rtol=1e-14)
 
 
-@pytest.mark.parametrize("m", [12, 28])
+@pytest.mark.parametrize("m", [4, 8, 12, 20, 24, 28, 32])
 def test_paley_is_hadamard_and_skew(m):
     h = hadamard_m(m).astype(np.int64)
     assert set(np.unique(h)) == {-1, 1}
@@ -67,7 +67,7 @@ def test_paley_is_hadamard_and_skew(m):
     assert np.all(h[1:, 0] == -1)
 
 
-@pytest.mark.parametrize("q", [11, 27])
+@pytest.mark.parametrize("q", [3, 7, 11, 19, 23, 27, 31])
 def test_jacobsthal_identities(q):
     h = paley1(q).astype(np.int64)
     jac = h[1:, 1:] - np.eye(q, dtype=np.int64)

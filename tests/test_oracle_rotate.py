@@ -58,6 +58,33 @@ def test_matches_butterfly_fwht(d):
     np.testing.assert_allclose(rotate_rows(x, s), want, rtol=0, atol=1e-12)
 
 
+def _transformed(h: np.ndarray, seed: int) -> np.ndarray:
+    """Another Hadamard matrix of the same order: rows and columns permuted,
+    rows and columns sign-flipped (all preserve H H^T = m I)."""
+    rng = np.random.default_rng(seed)
+    m = h.shape[0]
+    h = h[rng.permutation(m)][:, rng.permutation(m)]
+    return (h * (1 - 2 * rng.integers(0, 2, m))[:, None]
+            * (1 - 2 * rng.integers(0, 2, m))[None, :]).astype(np.int8)
+
+
+@pytest.mark.parametrize("d,m", [(16, 4), (64, 8), (40, 20), (96, 24), (56, 28), (128, 32),
+                                 (48, 12)])
+def test_given_factor_equals_dense_kron(d, m):
+    # the caller's H_m (any Hadamard matrix of order m) enters exactly as
+    # np.kron(H_{2^n}, H_m) does
+    from oracle import hadamard_m
+    x, s = _rng_case(d)
+    hm = _transformed(hadamard_m(m), d + m)
+    np.testing.assert_array_equal(hm.astype(int) @ hm.T.astype(int), m * np.eye(m, dtype=int))
+    dense = np.kron(sylvester(d // m).astype(np.float64), hm.astype(np.float64))
+    want = (x * s) @ dense.T / np.sqrt(d)
+    got = rotate_rows(x, s, m, hm)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    # and differs from the default factor
+    assert np.abs(got - rotate_rows(x, s, m)).max() > 1e-3
+
+
 def test_kron_index_order():
     # (H_2 (x) H_12): entry ((a, b), (a', b')) = H_2[a, a'] H_12[b, b'];
     # a one-hot input at (a'=1, b'=3) must come out as H_2[:, 1] (x) H_12[:, 3].

@@ -40,6 +40,7 @@ __all__ = [
     "ACT_CONFIGS",
     "KV_CONFIG",
     "make_act_inputs",
+    "make_swiglu_inputs",
     "make_kv_inputs",
     "DecodeConfig",
     "DECODE_CONFIGS",
@@ -237,6 +238,38 @@ def make_act_inputs(cfg: ActConfig, seed: int = 0, tokens: Optional[int] = None,
         "n": cfg.n,
         "m": cfg.m,
     }
+    if with_w:
+        w = rng.standard_normal((no, d), dtype=np.float32) * np.float32(cfg.w_std)
+        out["w"] = w.astype(np.float16)
+    return out
+
+
+def make_swiglu_inputs(cfg: ActConfig, seed: int = 0, tokens: Optional[int] = None,
+                       n_out: Optional[int] = None, with_w: bool = True) -> dict:
+    """Draw (signs, gate fp16, up fp16, W fp16) for the fused gated-product
+    path of a SwiGLU workload: the two projections whose product SiLU(gate) *
+    up is the workload's X.
+
+    The draws are those of ``make_act_inputs`` (signs -> outlier indices ->
+    outlier factors -> A -> B -> W): gate = fp16(A) and up = fp16(B) with the
+    outlier channels of B multiplied by their factors, which scales the
+    product's channels alike.  Signs and W equal make_act_inputs'.
+    """
+    if not cfg.swiglu:
+        raise ValueError(f"{cfg.name} is not a gated-product workload")
+    rng = np.random.default_rng(seed)
+    d = cfg.d
+    t = cfg.tokens if tokens is None else tokens
+    no = cfg.n_out if n_out is None else n_out
+    signs = random_signs(rng, d)
+    idx = np.sort(rng.choice(d, size=cfg.outlier_count, replace=False))
+    factors = rng.uniform(cfg.outlier_lo, cfg.outlier_hi, size=cfg.outlier_count).astype(np.float32)
+    gate = rng.standard_normal((t, d), dtype=np.float32).astype(np.float16)
+    up = rng.standard_normal((t, d), dtype=np.float32)
+    up[:, idx] *= factors[None, :]
+    out = {"signs": signs, "gate": gate, "up": up.astype(np.float16), "outlier_idx": idx,
+           "outlier_factors": factors, "d": d, "n": cfg.n, "m": cfg.m}
+    del up
     if with_w:
         w = rng.standard_normal((no, d), dtype=np.float32) * np.float32(cfg.w_std)
         out["w"] = w.astype(np.float16)
