@@ -5,8 +5,10 @@ One step = one pass of the online path over one batch of synthetic input:
 rotate+quant of the activations X (fused randomized Hadamard + per-token INT4,
 ``quarot_had_quant``) followed by the W4A4 GEMM with dequant
 (``quarot_w4a4_gemm``) against weights prepared offline (untimed) by the same
-rotate+quant kernel.  Default workload: X fp16 [2048 x 4096] with 0.1%
-outlier channels, random-sign H_4096, W int4 [4096 x 4096].
+rotate+quant kernel.  Default workload: the LLaMA-2-70B prefill
+down-projection, X fp16 [4096 x 28672] (a SwiGLU-like product with 0.1%
+outlier channels), random-sign H_1024 (x) H_28 (Paley), W int4
+[8192 x 28672], Y fp16 [4096 x 8192].
 
 Inputs are resident in HBM before timing starts.  To keep the 256 MB
 Infinity Cache from serving repeated reads, the step cycles over enough
@@ -19,10 +21,11 @@ Prints ONE JSON line:
   roofline         the dominant kernel (the GEMM) against INT8 MFMA peak
   roofline_rotate_quant  rotate+quant against HBM peak
   cpu_baseline     the CPU oracle timed on this host on the same workload
-Extra workloads for profiling: --workload NAME, --kv (the K/V cache write),
---decode (one decode step: append the new token's K/V, then attention of every
-query head over the int4 cache, with the head-wise query rotation and the
-cross-head transform).
+Extra workloads for profiling: --workload NAME, --swiglu (the gated FFN
+product fused into rotate+quant, against the unfused producer + rotate+quant),
+--kv (the K/V cache write), --decode (one decode step: append the new token's
+K/V, then attention of every query head over the int4 cache, with the
+head-wise query rotation and the cross-head transform).
 """
 
 from __future__ import annotations
@@ -59,7 +62,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llama7b_proj", choices=sorted(workloads.ACT_CONFIGS))
+    p.add_argument("--workload", default="llama70b_down", choices=sorted(workloads.ACT_CONFIGS))
     p.add_argument("--kv", action="store_true", help="benchmark the K/V cache write instead")
     p.add_argument("--kv-asym", action="store_true",
                    help="with --kv or --decode: the asymmetric cache (zero point, clip 0.95)")
@@ -69,8 +72,11 @@ def parse_args():
                    choices=sorted(workloads.DECODE_CONFIGS))
     p.add_argument("--no-cross-head", action="store_true",
                    help="with --decode: leave out the cross-head transform")
-    p.add_argument("--rmsnorm", action="store_true",
-                   help="with an activation workload: the RMSNorm-fused rotate+quant")
+    p.add_argument("--swiglu", action="store_true",
+                   help="with a SwiGLU workload: rotate+quant fused with the gated product "
+                        "SiLU(gate) * up, against the unfused producer + rotate+quant")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="token rows of the CPU oracle sample (0 = the workload's default)")
     p.add_argument("--cross-head", action="store_true",
                    help="benchmark the cross-head transform + quantisation of the attention output")
     p.add_argument("--cross-head-workload", default="attn_out_70b",
@@ -97,24 +103,42 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
-def time_kernel(torch, stream, launch, count: int, lead: int = 10) -> float:
-    """Average duration (ms) of `count` back-to-back launches on `stream`.
+def time_kernel(torch, stream, launch, count: int, lead: int = 10) -> dict:
+    """Per-launch duration (ms) of `count` back-to-back launches on `stream`.
 
-    A spin kernel holds the stream while the host enqueues everything, so no
-    host launch latency lands between the events; `lead` untimed launches run
-    right before the first event so the clocks have left the spin's idle
-    state."""
+    Two passes behind a spin kernel (so the host has enqueued everything
+    before the first launch starts; `lead` untimed launches bring the clocks
+    out of the spin's idle state):
+      mean          two events around all launches of the first pass
+      median, min   one event between consecutive launches of the second pass
+    """
+    def spin_and_lead():
+        torch.cuda._sleep(SPIN_CYCLES)
+        for i in range(lead):
+            launch(i)
+
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(SPIN_CYCLES)
-    for i in range(lead):
-        launch(i)
+    spin_and_lead()
     e0.record(stream)
     for i in range(count):
         launch(lead + i)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / count
+    mean = e0.elapsed_time(e1) / count
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(count + 1)]
+    spin_and_lead()
+    evs[0].record(stream)
+    for i in range(count):
+        launch(lead + i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(count)]
+    return {"mean": mean, "median": float(np.median(per)), "min": float(min(per))}
+
+
+def us_stats(t: dict) -> dict:
+    return {k: round(v * 1e3, 3) for k, v in t.items()}
 
 
 # The source file each timed kernel is compiled from.
@@ -159,31 +183,52 @@ def measured_traffic(workload: str, kernel: str):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
-def cpu_baseline_act(cfg, inp) -> dict:
-    """The oracle, as it stands, on the full step of this workload."""
+def host_cpus() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# Token rows of the CPU oracle sample per workload: about 10-30 s of host work.
+CPU_ROWS = {"tiny": 16, "llama7b_proj": 2048, "down_12288": 1024, "llama70b_down": 512}
+
+
+def cpu_baseline_act(cfg, inp, rows: int) -> dict:
+    """The oracle, as it stands, on the first `rows` tokens of the step:
+    rotate+quant of those rows, and their integer GEMM + dequant against all
+    of W (whose offline preparation by the oracle is not timed)."""
     import oracle
 
+    rows = min(rows, inp["x"].shape[0])
+    x = inp["x"][:rows]
     t0 = time.perf_counter()
-    a = oracle.had_quant(inp["x"], inp["signs"], cfg.m)
+    a = oracle.had_quant(x, inp["signs"], cfg.m)
     t1 = time.perf_counter()
     b = oracle.prep_weights(inp["w"], inp["signs"], cfg.m)  # offline, not counted
     t2 = time.perf_counter()
     acc, y = oracle.w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
     t3 = time.perf_counter()
-    T, d, N = inp["x"].shape[0], cfg.d, inp["w"].shape[0]
-    rq_bytes = 2 * T * d + T * d // 2 + 2 * T
+    d, N = cfg.d, inp["w"].shape[0]
+    rq_bytes = 2 * rows * d + rows * d // 2 + 2 * rows
     return {
         "value": rq_bytes / (t1 - t0) / 1e9,
         "unit": "GB/s",
-        "gemm_tops": 2.0 * T * N * d / (t3 - t2) / 1e12,
+        "gemm_tops": 2.0 * rows * N * d / (t3 - t2) / 1e12,
         "seconds_rotate_quant": t1 - t0,
         "seconds_gemm_dequant": t3 - t2,
         "cores": blas_threads(),
+        "host_cpus": host_cpus(),
         "kind": "oracle",
-        "sample": f"full {cfg.name} step: rotate+quant of X [{T} x {d}] (float64 dense "
-                  f"factored rotation) and the exact integer GEMM [{T} x {N} x {d}] + dequant "
-                  f"(float64 BLAS); weight prep excluded",
+        "sample": f"{rows} of the {inp['x'].shape[0]} tokens of {cfg.name}: rotate+quant of "
+                  f"X [{rows} x {d}] (float64 dense factored rotation, float64 rint) and the "
+                  f"exact integer GEMM [{rows} x {N} x {d}] + dequant (float64 BLAS); the "
+                  f"oracle's weight prep is not timed. cores = BLAS threads",
     }
+
+
+def make_sets(n: int, make) -> list:
+    return [make(i) for i in range(n)]
 
 
 def bench_act(args, torch, qr) -> dict:
@@ -193,38 +238,36 @@ def bench_act(args, torch, qr) -> dict:
     T, d, N = inp["x"].shape[0], cfg.d, inp["w"].shape[0]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     signs = dev(inp["signs"])
+    had_m = qr.hadamard_factor(cfg.m) if cfg.m > 1 else None
     x0 = dev(inp["x"])
     w0 = dev(inp["w"])
     # offline weight prep (same kernel, untimed)
-    qw0, sw0 = qr.had_quant(w0, signs, cfg.m)
+    qw0, sw0 = qr.had_quant(w0, signs, cfg.m, had_m=had_m)
     del w0
     per_set = T * d * 2 + T * d // 2 + 2 * T + N * d // 2 + 2 * N + T * N * 2
     nsets = args.sets or max(1, -(-CACHE_DEFEAT_BYTES // per_set))
     log(f"{nsets} buffer sets of {per_set / 2**20:.1f} MiB")
-    sets = []
-    for _ in range(nsets):
-        sets.append({
-            "x": x0.clone(),
-            "qx": torch.empty((T, d // 2), dtype=torch.uint8, device="cuda"),
-            "sx": torch.empty((T,), dtype=torch.float16, device="cuda"),
-            "qw": qw0.clone(),
-            "sw": sw0.clone(),
-            "y": torch.empty((T, N), dtype=torch.float16, device="cuda"),
-        })
+    sets = make_sets(nsets, lambda i: {
+        "x": x0 if i == 0 else x0.clone(),
+        "qx": torch.empty((T, d // 2), dtype=torch.uint8, device="cuda"),
+        "sx": torch.empty((T,), dtype=torch.float16, device="cuda"),
+        "qw": qw0 if i == 0 else qw0.clone(),
+        "sw": sw0 if i == 0 else sw0.clone(),
+        "y": torch.empty((T, N), dtype=torch.float16, device="cuda"),
+    })
     stream = torch.cuda.current_stream()
-    rms = args.rmsnorm
 
-    def rotate_quant(s):
-        if rms:
-            qr.rmsnorm_had_quant(s["x"], 1e-5, signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"],
-                                 stream=stream)
-        else:
-            qr.had_quant(s["x"], signs, cfg.m, 1.0, q_out=s["qx"], scale_out=s["sx"], stream=stream)
+    def rotate_quant(st):
+        qr.had_quant(st["x"], signs, cfg.m, 1.0, q_out=st["qx"], scale_out=st["sx"],
+                     had_m=had_m, stream=stream)
+
+    def gemm(st):
+        qr.w4a4_gemm(st["qx"], st["sx"], st["qw"], st["sw"], d, out=st["y"], stream=stream)
 
     def step(i):
-        s = sets[i % nsets]
-        rotate_quant(s)
-        qr.w4a4_gemm(s["qx"], s["sx"], s["qw"], s["sw"], d, out=s["y"], stream=stream)
+        st = sets[i % nsets]
+        rotate_quant(st)
+        gemm(st)
 
     for i in range(args.warmup):
         step(i)
@@ -237,25 +280,16 @@ def bench_act(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # (2) per-kernel durations from HIP events on the launch stream: K
-    # back-to-back launches of one kernel (cycling over the buffer sets)
-    # between two events, behind a spin kernel so the host has queued them
-    # all before the first starts.
-    def launch_rq(i):
-        rotate_quant(sets[i % nsets])
-
-    def launch_gemm(i):
-        s = sets[i % nsets]
-        qr.w4a4_gemm(s["qx"], s["sx"], s["qw"], s["sw"], d, out=s["y"], stream=stream)
-
-    rq_ms = time_kernel(torch, stream, launch_rq, args.steps)
-    gemm_ms = time_kernel(torch, stream, launch_gemm, args.steps)
+    # (2) per-kernel durations from HIP events on the launch stream
+    rq = time_kernel(torch, stream, lambda i: rotate_quant(sets[i % nsets]), args.steps)
+    gm = time_kernel(torch, stream, lambda i: gemm(sets[i % nsets]), args.steps)
     rq_bytes = 2 * T * d + T * d // 2 + 2 * T
     gemm_ops = 2.0 * T * N * d
-    rq_gbs = rq_bytes / (rq_ms * 1e-3) / 1e9
-    tops = gemm_ops / (gemm_ms * 1e-3) / 1e12
-    log(f"rotate+quant {rq_ms * 1e3:.2f} us ({rq_gbs:.0f} GB/s); gemm {gemm_ms * 1e3:.2f} us "
-        f"({tops:.0f} TOPS); wall/step {wall / args.steps * 1e3:.4f} ms")
+    rq_gbs = rq_bytes / (rq["mean"] * 1e-3) / 1e9
+    tops = gemm_ops / (gm["mean"] * 1e-3) / 1e12
+    log(f"rotate+quant {rq['mean'] * 1e3:.2f} us ({rq_gbs:.0f} GB/s); gemm "
+        f"{gm['mean'] * 1e3:.2f} us ({tops:.0f} TOPS); wall/step {wall / args.steps * 1e3:.4f} ms")
+    rot = f"H_{d // cfg.m}" + (f" (x) H_{cfg.m} (Paley)" if cfg.m > 1 else "")
     out = {
         "metric": "rotate+quant GB/s (% HBM peak); W4A4 GEMM TOPS (% INT8 MFMA peak)",
         "value": round(rq_gbs, 2),
@@ -271,13 +305,13 @@ def bench_act(args, torch, qr) -> dict:
         "dtype": "fp32 rotate / int8 MFMA (int4 codes, int32 acc)",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: X fp16 [{T} x {d}] with {cfg.outlier_count} outlier "
-                        f"channels, " + ("RMSNorm (eps 1e-5, gain absorbed) fused, " if rms else "")
-                        + f"rotation H_{d // cfg.m}" + (f" (x) H_{cfg.m}" if cfg.m > 1 else "")
-                        + f" with random signs, W int4 [{N} x {d}], Y fp16 [{T} x {N}]",
+            "workload": f"{cfg.name}: X fp16 [{T} x {d}]"
+                        + (" (SiLU(A) * B)" if cfg.swiglu else "")
+                        + f" with {cfg.outlier_count} outlier channels x U(10,100), rotation "
+                        f"{rot} with random signs, W int4 [{N} x {d}], Y fp16 [{T} x {N}]",
             "tokens": T, "d": d, "n_out": N, "buffer_sets": nsets,
         },
-        "kernels_us": {"had_quant": round(rq_ms * 1e3, 3), "w4a4_gemm": round(gemm_ms * 1e3, 3)},
+        "kernels_us": {"had_quant": us_stats(rq), "w4a4_gemm": us_stats(gm)},
         "roofline": {
             "kernel": "w4a4_gemm",
             "bound": "mfma",
@@ -286,22 +320,117 @@ def bench_act(args, torch, qr) -> dict:
             "unit": "TFLOP/s",
             "frac": round(tops / INT8_PEAK_TOPS, 4),
             "traffic": measured_traffic(cfg.name, "w4a4_gemm"),
-            "note": "integer ops (TOPS) against the dense INT8 MFMA peak; 2*M*N*K per launch",
+            "note": "integer ops (TOPS) against the dense INT8 MFMA peak; 2*M*N*K per launch; "
+                    "traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE",
         },
         "roofline_rotate_quant": {
-            "kernel": "rmsnorm_had_quant" if rms else "had_quant",
+            "kernel": "had_quant",
             "bound": "hbm",
             "achieved": round(rq_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg.name + ("_rmsnorm" if rms else ""), "had_quant"),
+            "traffic": measured_traffic(cfg.name, "had_quant"),
             "algorithmic_bytes": rq_bytes,
         },
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (baseline)")
-        out["cpu_baseline"] = cpu_baseline_act(cfg, inp)
+        out["cpu_baseline"] = cpu_baseline_act(cfg, inp, args.cpu_rows or CPU_ROWS[cfg.name])
+    return out
+
+
+def bench_swiglu(args, torch, qr) -> dict:
+    """The gated product fused into rotate+quant, against the same work
+    unfused: torch's SiLU and multiply writing the fp16 product, then
+    rotate+quant of it."""
+    cfg = workloads.ACT_CONFIGS[args.workload]
+    if not cfg.swiglu:
+        raise SystemExit(f"--swiglu needs a SwiGLU workload, not {cfg.name}")
+    log(f"swiglu workload {cfg.name}: generating inputs")
+    inp = workloads.make_swiglu_inputs(cfg, with_w=False)
+    T, d = inp["gate"].shape
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    signs = dev(inp["signs"])
+    had_m = qr.hadamard_factor(cfg.m) if cfg.m > 1 else None
+    g0, u0 = dev(inp["gate"]), dev(inp["up"])
+    fused_bytes = 4 * T * d + T * d // 2 + 2 * T
+    per_set = fused_bytes + 2 * T * d  # + the unfused product buffer
+    nsets = args.sets or max(2, -(-CACHE_DEFEAT_BYTES // per_set))
+    sets = make_sets(nsets, lambda i: {
+        "g": g0 if i == 0 else g0.clone(), "u": u0 if i == 0 else u0.clone(),
+        "x": torch.empty((T, d), dtype=torch.float16, device="cuda"),
+        "q": torch.empty((T, d // 2), dtype=torch.uint8, device="cuda"),
+        "s": torch.empty((T,), dtype=torch.float16, device="cuda")})
+    stream = torch.cuda.current_stream()
+    F = torch.nn.functional
+
+    def fused(i):
+        st = sets[i % nsets]
+        qr.swiglu_had_quant(st["g"], st["u"], signs, cfg.m, 1.0, q_out=st["q"],
+                            scale_out=st["s"], had_m=had_m, stream=stream)
+
+    def producer(i):
+        st = sets[i % nsets]
+        torch.mul(F.silu(st["g"]), st["u"], out=st["x"])
+
+    def unfused(i):
+        producer(i)
+        st = sets[i % nsets]
+        qr.had_quant(st["x"], signs, cfg.m, 1.0, q_out=st["q"], scale_out=st["s"],
+                     had_m=had_m, stream=stream)
+
+    for i in range(args.warmup):
+        fused(i)
+        unfused(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tf = time_kernel(torch, stream, fused, args.steps)
+    tu = time_kernel(torch, stream, unfused, args.steps)
+    tp = time_kernel(torch, stream, producer, args.steps)
+    gbs = fused_bytes / (tf["mean"] * 1e-3) / 1e9
+    log(f"fused {tf['mean'] * 1e3:.2f} us ({gbs:.0f} GB/s); unfused {tu['mean'] * 1e3:.2f} us "
+        f"(producer {tp['mean'] * 1e3:.2f} us)")
+    out = {
+        "metric": "gated product + rotate+quant GB/s (% HBM peak)",
+        "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 product and rotation (fp16 hi/lo MFMA operands) / int4 codes",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} gated product: gate, up fp16 [{T} x {d}], "
+                               f"{cfg.outlier_count} outlier channels x U(10,100) in up, "
+                               f"SiLU(gate) * up rotated by H_{d // cfg.m} (x) H_{cfg.m} with "
+                               f"random signs, per-token int4",
+                   "buffer_sets": nsets},
+        "kernels_us": {"swiglu_had_quant": us_stats(tf),
+                       "unfused_producer_plus_had_quant": us_stats(tu),
+                       "unfused_producer_only": us_stats(tp)},
+        "speedup_vs_unfused": round(tu["mean"] / tf["mean"], 3),
+        "roofline": {"kernel": "swiglu_had_quant", "bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name + "_swiglu", "had_quant"),
+                     "algorithmic_bytes": fused_bytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        rows = min(args.cpu_rows or CPU_ROWS[cfg.name], T)
+        log("timing the CPU oracle on a sample")
+        t0 = time.perf_counter()
+        oracle.swiglu_had_quant(inp["gate"][:rows], inp["up"][:rows], inp["signs"], cfg.m)
+        sec = time.perf_counter() - t0
+        nb = rows * (4 * d + d // 2 + 2)
+        out["cpu_baseline"] = {"value": nb / sec / 1e9, "unit": "GB/s", "seconds": sec,
+                               "cores": blas_threads(), "host_cpus": host_cpus(),
+                               "kind": "oracle",
+                               "sample": f"{rows} of the {T} tokens (float64 SiLU product, "
+                                         f"dense factored rotation, rint)"}
     return out
 
 
@@ -346,7 +475,8 @@ def bench_kv(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = time_kernel(torch, stream, step, args.steps)
+    tk = time_kernel(torch, stream, step, args.steps)
+    ms = tk["mean"]
     nbytes = per_set
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"kv {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
@@ -362,6 +492,7 @@ def bench_kv(args, torch, qr) -> dict:
                                + (", asymmetric uint4 + fp16 scale and zero point, clip 0.95"
                                   if asym else ", symmetric int4 + fp16 scale"),
                    "buffer_sets": nsets},
+        "kernels_us": {"kv_had_quant": us_stats(tk)},
         "roofline": {"kernel": "kv_had_quant", "bound": "hbm", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(cfg.name + ("_asym" if asym else ""),
@@ -380,7 +511,7 @@ def cpu_baseline_cross_head(cfg, z16, rows=None) -> dict:
     dt = time.perf_counter() - t0
     nbytes = rows * (2 * cfg.d + cfg.d // 2 + 2)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "seconds": dt, "cores": blas_threads(),
-            "kind": "oracle",
+            "host_cpus": host_cpus(), "kind": "oracle",
             "sample": f"{rows} of the {cfg.tokens} tokens of {cfg.name} (float64 einsum over the "
                       f"head index, then the quantiser)"}
 
@@ -413,7 +544,8 @@ def bench_cross_head(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = time_kernel(torch, stream, step, args.steps)
+    tk = time_kernel(torch, stream, step, args.steps)
+    ms = tk["mean"]
     gbs = per_set / (ms * 1e-3) / 1e9
     log(f"cross-head {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
     out = {
@@ -427,7 +559,7 @@ def bench_cross_head(args, torch, qr) -> dict:
                                f"{cfg.head_dim}], {cfg.loud_heads} heads x U(10,100); "
                                f"H_{cfg.heads} over the head index, per-token int4",
                    "buffer_sets": nsets},
-        "kernels_us": {"cross_head": round(ms * 1e3, 3)},
+        "kernels_us": {"cross_head": us_stats(tk)},
         "roofline": {"kernel": "cross_head_quant", "bound": "hbm", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(cfg.name, "cross_head"),
@@ -460,7 +592,7 @@ def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows: int = 4) -
     sec = time.perf_counter() - t0
     nbytes = decode_call_bytes(rows, cfg.heads, dcfg.q_heads, S, cfg.head_dim, mode)
     return {"value": nbytes / sec / 1e9, "unit": "GB/s", "seconds": sec, "cores": blas_threads(),
-            "kind": "oracle",
+            "host_cpus": host_cpus(), "kind": "oracle",
             "sample": f"{rows} of {cfg.batch} batch rows of the decode attention (query rotation, "
                       f"dequantisation, float64 softmax attention{', cross-head' if cross else ''}) "
                       f"over {S} cached positions; the oracle's cache build is not timed"}
@@ -540,9 +672,10 @@ def bench_decode(args, torch, qr) -> dict:
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = time_kernel(torch, stream, step, args.steps)
-    ms_att = time_kernel(torch, stream, attend, args.steps)
-    ms_app = time_kernel(torch, stream, append, args.steps)
+    t_step = time_kernel(torch, stream, step, args.steps)
+    t_att = time_kernel(torch, stream, attend, args.steps)
+    t_app = time_kernel(torch, stream, append, args.steps)
+    ms_step, ms_att, ms_app = t_step["mean"], t_att["mean"], t_app["mean"]
     step_gbs = (att_bytes + app_bytes) / (ms_step * 1e-3) / 1e9
     att_gbs = att_bytes / (ms_att * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.2f} us ({step_gbs:.0f} GB/s); attention call "
@@ -563,8 +696,8 @@ def bench_decode(args, torch, qr) -> dict:
                                + (f", cross-head H_{Hq}" if cross else ""),
                    "tokens_per_s": round(B / (ms_step * 1e-3), 1),
                    "buffer_sets": nsets},
-        "kernels_us": {"kv_decode_attention": round(ms_att * 1e3, 3),
-                       "kv_had_quant_append": round(ms_app * 1e3, 3)},
+        "kernels_us": {"kv_decode_attention": us_stats(t_att),
+                       "kv_had_quant_append": us_stats(t_app), "decode_step": us_stats(t_step)},
         "roofline": {"kernel": "kv_decode_attention (split + combine kernels)", "bound": "hbm",
                      "achieved": round(att_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(att_gbs / HBM_PEAK_GBS, 4),
@@ -686,6 +819,8 @@ def main() -> int:
             out = bench_decode(args, torch, qr)
         elif args.kv:
             out = bench_kv(args, torch, qr)
+        elif args.swiglu:
+            out = bench_swiglu(args, torch, qr)
         else:
             out = bench_act(args, torch, qr)
     print(json.dumps(out), flush=True)

@@ -10,8 +10,10 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
- *     allocated and owned by the caller.  The library allocates nothing,
- *     frees nothing and keeps no reference after returning.
+ *     allocated and owned by the caller, except the small Hadamard factor
+ *     had_m, which is read from HOST memory during the call.  The library
+ *     allocates nothing, frees nothing and keeps no reference after
+ *     returning.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     null stream) and the call returns without synchronising.  A kernel
  *     fault surfaces at the caller's next synchronisation.
@@ -47,12 +49,12 @@ enum {
  * Fused randomized Hadamard rotation + per-token symmetric INT4 quantisation.
  *
  * Follows [S] section 3.4 Stage 1a (randomized Hadamard R = H diag(s), and
- * H_d = H_{2^n} (x) H_m when d is not a power of two), Stage 1b (online
- * Hadamard before the down-projection), Stage 2b (per-token symmetric scale
- * clip * max|x| / 7) and "Kernel Implementation and Hardware Efficiency"
- * (quantise per token, pack two INT4 per byte); [G] section "2. Why
- * Randomized Walsh-Hadamard Transforms" and step 2 of "Deep Dive" (round to
- * nearest, clip to [-8, 7]).
+ * H_d = H_{2^n} (x) H_m with a known Hadamard matrix H_m when d is not a
+ * power of two), Stage 1b (online Hadamard before the down-projection),
+ * Stage 2b (per-token symmetric scale clip * max|x| / 7) and "Kernel
+ * Implementation and Hardware Efficiency" (quantise per token, pack two INT4
+ * per byte); [G] section "2. Why Randomized Walsh-Hadamard Transforms" and
+ * step 2 of "Deep Dive" (round to nearest, clip to [-8, 7]).
  *
  * For every row r of x (fp16 [rows x d], row stride ld_x elements):
  *   x~      = (H_{2^n} (x) H_m) diag(signs) x_r / sqrt(d)      (fp32 arithmetic)
@@ -60,14 +62,21 @@ enum {
  *   q_j     = clamp(rint(x~_j / S_r), -8, 7)                     (ties to even)
  * and writes q packed into q_out (uint8 [rows x d/2], row stride ld_q bytes)
  * and S_r into scale_out (fp16 [rows]).  The Kronecker index of element j
- * is j = a*m + b: H_m mixes the contiguous group b, H_{2^n} mixes a.
+ * is j = a*m + b: H_m mixes the contiguous group b (row b of had_m weights
+ * column c: y[a*m + b] = sum_c had_m[b*m + c] x[a*m + c]), H_{2^n} (the
+ * Sylvester matrix, entry (i, j) = (-1)^popcount(i & j)) mixes a.
  *
  * Arguments:
  *   x          fp16 [rows x d], 16-byte aligned, ld_x >= d, ld_x % 8 == 0.
  *   signs      int8 [d] of +1/-1, or NULL for all +1.
- *   m          1, 12 or 28: the size of the small Hadamard factor, taken
- *              from the library's built-in Paley type-I matrices
- *              (quarot_hadamard_factor() returns them); d = 2^n * m.
+ *   m          1, or a multiple of 4 up to 32: the order of the small
+ *              Hadamard factor; d = 2^n * m.
+ *   had_m      HOST memory: int8 [m x m] row-major, entries +1/-1, with
+ *              had_m had_m^T = m I (checked).  NULL iff m == 1.  It is read
+ *              during the call and handed to the kernels by value; the
+ *              library keeps no reference.  quarot_hadamard_factor() returns
+ *              the Paley matrices of order 12 and 28 the configs use; offline
+ *              weight preparation must use the same matrix as the activations.
  *   clip_ratio in (0, 1].  1.0 gives S = max|x~| / 7.
  *   q_out      uint8 [rows x ld_q], 16-byte aligned, ld_q >= d/2, ld_q % 16 == 0.
  *   scale_out  fp16 [rows], 2-byte aligned.
@@ -75,31 +84,44 @@ enum {
  *              NULL in production (it adds 4*d bytes of traffic per row).
  * Supported: rows >= 0 (0 is a no-op), d = 2^n * m with d % 32 == 0 and
  * d <= 32768.  Non-finite inputs are outside the contract.
+ * Errors: INVALID for bad sizes, strides, clip, a missing required pointer,
+ * had_m given with m == 1 or missing with m > 1, or had_m not a Hadamard
+ * matrix; UNSUPPORTED for other m or d; MISALIGNED as stated.
  */
 int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
-                     const int8_t* signs, int32_t m, float clip_ratio,
+                     const int8_t* signs, int32_t m, const int8_t* had_m, float clip_ratio,
                      uint8_t* q_out, int64_t ld_q, void* scale_out,
                      float* x_rot_out, void* stream);
 
 /*
- * RMSNorm fused into rotate+quant: each row is first normalised,
- * y = x / sqrt(mean(x^2) + eps), then rotated and quantised exactly as
- * quarot_had_quant does with y in place of x.
+ * The gated FFN product fused into rotate+quant: the row that is rotated and
+ * quantised is c = SiLU(gate) * up, formed in the same pass, so the product
+ * never travels through HBM.
  *
- * Follows [G] step 2 of "Deep Dive" (the online rotation fused into the
- * RMSNorm kernel: normalise, rotate in registers, quantise per token); the
- * RMSNorm gain is absorbed into the next weights ([S] §3.4 Stage 1a), so no
- * gain is applied.  The rotation keeps the norm, so the kernels take
- * mean(x^2) from the rotated values and fold 1 / sqrt(mean + eps) into the
- * scale and codes; x_rot_out (optional) receives R y.
+ * Follows [S] section 3.4 "FFN Activation Rotation (Stage 1b)" (the online
+ * Hadamard is applied to the SwiGLU output (SiLU(A) * B) H right before the
+ * down-projection) and section 6 "Limitations and Trade-offs" (fusing the
+ * quantisation into the neighbouring kernels is the open kernel
+ * improvement); the rotation and quantiser are those of quarot_had_quant.
  *
- * Arguments as quarot_had_quant, plus eps (finite, > 0).
- * Errors: as quarot_had_quant; INVALID for a bad eps.
+ * For every row r:
+ *   c_j   = SiLU(gate_rj) * up_rj,   SiLU(t) = t / (1 + exp(-t))   (fp32)
+ *   then x~, S_r and the codes exactly as quarot_had_quant with c in place
+ *   of x.  The product is not rounded to fp16 before the rotation: the
+ *   kernels keep about 22 significant bits of it (fp32 rotation input).
+ *
+ * Arguments:
+ *   gate, up   fp16 [rows x d] each, 16-byte aligned, row strides ld_gate,
+ *              ld_up >= d and multiples of 8 (a fused gate_up projection
+ *              output [rows x 2d] is gate = p, up = p + d, both strides 2d).
+ *   everything else as quarot_had_quant; x_rot_out receives the rotated
+ *   product.  Products beyond the fp16 range (|c| > 65504) are outside the
+ *   contract.
  */
-int quarot_rmsnorm_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x, float eps,
-                             const int8_t* signs, int32_t m, float clip_ratio,
-                             uint8_t* q_out, int64_t ld_q, void* scale_out,
-                             float* x_rot_out, void* stream);
+int quarot_swiglu_had_quant(const void* gate, const void* up, int64_t rows, int64_t d,
+                            int64_t ld_gate, int64_t ld_up, const int8_t* signs, int32_t m,
+                            const int8_t* had_m, float clip_ratio, uint8_t* q_out, int64_t ld_q,
+                            void* scale_out, float* x_rot_out, void* stream);
 
 /*
  * Cross-head transform + per-token symmetric INT4 quantisation of the
@@ -213,6 +235,10 @@ int quarot_w4a4_gemm(const uint8_t* a_q, int64_t lda, const void* a_scale,
  *                given, ignored in mode 0.
  *   S_cache, pos0  cache length and first position written;
  *                0 <= pos0 and pos0 + S <= S_cache.
+ *   k_rot_out, v_rot_out  optional fp32 [B x H x S x D] (dense, indexed by
+ *                the input position s, 16-byte aligned) receiving the rotated
+ *                groups x~ for inspection; NULL in production.  Ignored for a
+ *                tensor that is not given.
  * Errors: INVALID for bad sizes, mode, clip or missing buffers;
  * UNSUPPORTED for other D or B*H*S >= 2^31; MISALIGNED as stated.
  */
@@ -223,7 +249,8 @@ int quarot_kv_had_quant(const void* k, const void* v,
                         int32_t mode, float clip_ratio,
                         uint8_t* k_q, void* k_scale, void* k_zero,
                         uint8_t* v_q, void* v_scale, void* v_zero,
-                        int64_t S_cache, int64_t pos0, void* stream);
+                        int64_t S_cache, int64_t pos0, float* k_rot_out, float* v_rot_out,
+                        void* stream);
 
 /*
  * One decode step of attention over the INT4 cache written by
@@ -299,12 +326,13 @@ int64_t quarot_kv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int
                                          int64_t max_len);
 
 /*
- * Host-only: copy the built-in small Hadamard factor H_m (entries +1/-1,
- * row-major int8 [m x m], HOST memory of m*m bytes) that quarot_had_quant
- * uses for d = 2^n * m.  m = 1 gives [1]; 12 and 28 give the Paley type-I
- * matrices for q = 11 and q = 27 ([S] Stage 1a: "a known Hadamard matrix of
- * size m"; [V]: a Paley block of size 12 for width 12288).  Offline weight
- * preparation must use the same matrix.  Makes no HIP call.
+ * Host-only: copy one of the library's Paley type-I Hadamard matrices
+ * (entries +1/-1, row-major int8 [m x m], HOST memory of m*m bytes), for a
+ * caller to pass as had_m.  m = 1 gives [1]; 12 and 28 give the Paley
+ * matrices for q = 11 and q = 27 ([S] Stage 1a takes any known Hadamard
+ * matrix of order m; [V] builds width 12288 with a Paley block of 12).  Offline weight
+ * preparation must rotate with the same matrix as the activations.  Makes
+ * no HIP call.
  */
 int quarot_hadamard_factor(int32_t m, int8_t* out_host);
 

@@ -18,17 +18,17 @@ _vp = ctypes.c_void_p
 _f32 = ctypes.c_float
 
 _SIGNATURES = {
-    "quarot_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _f32,
+    "quarot_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _f32,
                                         _vp, _i64, _vp, _vp, _vp]),
-    "quarot_rmsnorm_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _f32, _vp, _i32, _f32,
-                                                _vp, _i64, _vp, _vp, _vp]),
+    "quarot_swiglu_had_quant": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp,
+                                               _f32, _vp, _i64, _vp, _vp, _vp]),
     "quarot_cross_head_had_quant": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _i64,
                                                    _vp, _vp, _vp]),
     "quarot_w4a4_gemm": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                                         _vp, _i64, _vp, _i64, _vp]),
     "quarot_kv_had_quant": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                            _vp, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
-                                           _i64, _i64, _vp]),
+                                           _i64, _i64, _vp, _vp, _vp]),
     "quarot_kv_decode_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32,
                                                   _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                                   _f32, _i32, _vp, _vp, _vp, _i64, _vp]),
@@ -102,11 +102,34 @@ def _need(t, dtype, name: str, ndim: Optional[int] = None):
 
 
 def hadamard_factor(m: int) -> np.ndarray:
-    """The built-in H_m the kernels use (int8 [m, m], +-1)."""
+    """One of the library's Paley Hadamard matrices (int8 [m, m], +-1; m = 1, 12, 28)."""
     out = np.zeros((m, m), dtype=np.int8)
     _check("quarot_hadamard_factor",
            lib().quarot_hadamard_factor(m, out.ctypes.data_as(ctypes.c_void_p)))
     return out
+
+
+def _had_m_host(m: int, had_m):
+    """The host int8 [m, m] array passed as had_m (None for m = 1).  Without
+    an explicit matrix the library's own Paley matrix of order m is used."""
+    if m == 1:
+        if had_m is not None:
+            raise ValueError("had_m must be None when m = 1")
+        return None
+    if had_m is None:
+        return hadamard_factor(m)
+    if hasattr(had_m, "is_cuda"):
+        if had_m.is_cuda:
+            raise ValueError("had_m is read on the host: pass a CPU tensor or numpy array")
+        had_m = had_m.numpy()
+    h = np.ascontiguousarray(np.asarray(had_m), dtype=np.int8)
+    if h.shape != (m, m):
+        raise ValueError(f"had_m must be [{m}, {m}]")
+    return h
+
+
+def _host_ptr(a) -> Optional[int]:
+    return None if a is None else a.ctypes.data
 
 
 def _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out):
@@ -129,31 +152,42 @@ def _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out):
         _need(x_rot_out, torch.float32, "x_rot_out", 2)
         if not x_rot_out.is_contiguous() or tuple(x_rot_out.shape) != (rows, d):
             raise ValueError("x_rot_out must be contiguous float32 [rows, d]")
-    if q_out.stride(1) != 1 or q_out.shape[0] != rows or scale_out.shape[0] != rows:
-        raise ValueError("bad output shapes")
+    if q_out.stride(1) != 1 or q_out.shape[0] != rows or q_out.shape[1] < d // 2:
+        raise ValueError("q_out must be [rows, >= d/2] uint8 with contiguous rows")
+    if scale_out.shape[0] != rows or not scale_out.is_contiguous():
+        raise ValueError("scale_out must be a contiguous fp16 [rows]")
     return rows, d, q_out, scale_out
 
 
 def had_quant(x, signs=None, m: int = 1, clip_ratio: float = 1.0, q_out=None, scale_out=None,
-              x_rot_out=None, stream=None):
-    """Rotate+quant rows of fp16 x [rows, d]; returns (codes, scales)."""
+              x_rot_out=None, had_m=None, stream=None):
+    """Rotate+quant rows of fp16 x [rows, d] with H_{d/m} (x) H_m; returns
+    (codes, scales).  had_m: int8 [m, m] host matrix (default: the library's
+    Paley matrix of order m)."""
     rows, d, q_out, scale_out = _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out)
-    st = lib().quarot_had_quant(_ptr(x), rows, d, x.stride(0), _ptr(signs), m,
+    h = _had_m_host(m, had_m)
+    st = lib().quarot_had_quant(_ptr(x), rows, d, x.stride(0), _ptr(signs), m, _host_ptr(h),
                                 float(clip_ratio), _ptr(q_out), q_out.stride(0),
                                 _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
     _check("quarot_had_quant", st)
     return q_out, scale_out
 
 
-def rmsnorm_had_quant(x, eps: float = 1e-5, signs=None, m: int = 1, clip_ratio: float = 1.0,
-                      q_out=None, scale_out=None, x_rot_out=None, stream=None):
-    """RMSNorm (gain absorbed) then rotate+quant of rows of fp16 x [rows, d];
-    returns (codes, scales)."""
-    rows, d, q_out, scale_out = _had_quant_outputs(x, signs, q_out, scale_out, x_rot_out)
-    st = lib().quarot_rmsnorm_had_quant(_ptr(x), rows, d, x.stride(0), float(eps), _ptr(signs),
-                                        m, float(clip_ratio), _ptr(q_out), q_out.stride(0),
-                                        _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
-    _check("quarot_rmsnorm_had_quant", st)
+def swiglu_had_quant(gate, up, signs=None, m: int = 1, clip_ratio: float = 1.0, q_out=None,
+                     scale_out=None, x_rot_out=None, had_m=None, stream=None):
+    """Rotate+quant of the gated product SiLU(gate) * up, rows of fp16
+    [rows, d] each, formed in the same pass; returns (codes, scales)."""
+    torch = _torch()
+    rows, d, q_out, scale_out = _had_quant_outputs(gate, signs, q_out, scale_out, x_rot_out)
+    _need(up, torch.float16, "up", 2)
+    if tuple(up.shape) != (rows, d) or up.stride(1) != 1:
+        raise ValueError("up must be [rows, d] with contiguous rows, like gate")
+    h = _had_m_host(m, had_m)
+    st = lib().quarot_swiglu_had_quant(_ptr(gate), _ptr(up), rows, d, gate.stride(0),
+                                       up.stride(0), _ptr(signs), m, _host_ptr(h),
+                                       float(clip_ratio), _ptr(q_out), q_out.stride(0),
+                                       _ptr(scale_out), _ptr(x_rot_out), _stream(stream))
+    _check("quarot_swiglu_had_quant", st)
     return q_out, scale_out
 
 
@@ -202,14 +236,25 @@ def w4a4_gemm(a_q, a_scale, b_q, b_scale, k: int, out=None, acc_out=None, stream
     return out
 
 
+def _check_signs(signs, length: int, name: str = "signs") -> None:
+    """signs: a contiguous int8 device vector of at least `length` entries."""
+    torch = _torch()
+    if signs is None:
+        return
+    _need(signs, torch.int8, name)
+    if not signs.is_contiguous() or signs.numel() < length:
+        raise ValueError(f"{name} must be a contiguous int8 tensor of at least {length} entries")
+
+
 def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0: int = 0,
                  signs_stride_h: int = 0, clip_ratio: float = 1.0, mode: int = 0,
-                 k_zero=None, v_zero=None, stream=None):
+                 k_zero=None, v_zero=None, k_rot_out=None, v_rot_out=None, stream=None):
     """Quantise K (and V) [B, H, S, D] into caches [B, H, S_cache, D/2] at pos0.
 
     mode 0: symmetric int4 codes + fp16 scales.  mode 1: asymmetric uint4
     codes + fp16 scales + fp16 zero points (k_zero / v_zero, shaped like the
-    scales); the pages use clip_ratio 0.95 for it."""
+    scales); the pages use clip_ratio 0.95 for it.  k_rot_out / v_rot_out:
+    optional float32 [B, H, S, D] receiving the rotated groups."""
     torch = _torch()
     ref = k if k is not None else v
     _need(ref, torch.float16, "k/v", 4)
@@ -243,8 +288,17 @@ def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0
             S_cache = cq.shape[2]
         elif cq.shape[2] != S_cache:
             raise ValueError("k and v caches must have the same length")
-    if signs is not None:
-        _need(signs, torch.int8, "signs")
+    if signs_stride_h < 0:
+        raise ValueError("signs_stride_h must be >= 0")
+    _check_signs(signs, int(signs_stride_h) * (H - 1) + D)
+    for name, t, r in (("k_rot_out", k, k_rot_out), ("v_rot_out", v, v_rot_out)):
+        if r is None:
+            continue
+        if t is None:
+            raise ValueError(f"{name} given without its tensor")
+        _need(r, torch.float32, name, 4)
+        if not r.is_contiguous() or tuple(r.shape) != (B, H, S, D):
+            raise ValueError(f"{name} must be contiguous float32 [B, H, S, D]")
     sb, sh, ss, _ = ref.stride()
     st = lib().quarot_kv_had_quant(_ptr(k), _ptr(v), B, H, S, D, sb, sh, ss, _ptr(signs),
                                    int(signs_stride_h), int(mode), float(clip_ratio),
@@ -254,7 +308,8 @@ def kv_had_quant(k, v, signs, k_cache, k_scale, v_cache=None, v_scale=None, pos0
                                    _ptr(v_cache) if v is not None else None,
                                    _ptr(v_scale) if v is not None else None,
                                    _ptr(v_zero) if (v is not None and mode == 1) else None,
-                                   S_cache, int(pos0), _stream(stream))
+                                   S_cache, int(pos0), _ptr(k_rot_out), _ptr(v_rot_out),
+                                   _stream(stream))
     _check("quarot_kv_had_quant", st)
     if mode == 1:
         return k_cache, k_scale, k_zero, v_cache, v_scale, v_zero
@@ -298,8 +353,9 @@ def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: i
             _need(z, torch.float16, name, 3)
             if not z.is_contiguous() or tuple(z.shape) != (B, Hkv, S_cache):
                 raise ValueError(f"{name} must be contiguous [B, Hkv, S_cache]")
-    if signs is not None:
-        _need(signs, torch.int8, "signs")
+    if signs_stride_h < 0:
+        raise ValueError("signs_stride_h must be >= 0")
+    _check_signs(signs, int(signs_stride_h) * (Hkv - 1) + D)
     if lengths is not None:
         _need(lengths, torch.int32, "lengths", 1)
         if lengths.shape[0] != B or not lengths.is_contiguous():
@@ -309,8 +365,12 @@ def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: i
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
     _need(out, torch.float16, "out", 3)
+    if not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be contiguous fp16 [B, Hq, D]")
     if out_f32 is not None:
         _need(out_f32, torch.float32, "out_f32", 3)
+        if not out_f32.is_contiguous() or tuple(out_f32.shape) != (B, Hq, D):
+            raise ValueError("out_f32 must be contiguous float32 [B, Hq, D]")
     need = kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -78,24 +78,69 @@ int quarot_hadamard_factor(int32_t m, int8_t* out_host) {
 
 namespace {
 
-int had_quant_checked(const void* x, int64_t rows, int64_t d, int64_t ld_x, const int8_t* signs,
-                      int32_t m, float clip_ratio, uint8_t* q_out, int64_t ld_q, void* scale_out,
-                      float* x_rot_out, float rms_eps, void* stream) {
+// The caller's small Hadamard factor (host memory), validated and turned
+// into the kernels' bit masks: NULL iff m == 1; m a multiple of 4 up to 32;
+// entries +1/-1 with H H^T = m I in exact integer arithmetic.
+int had_masks_checked(int32_t m, const int8_t* had_m, HadMasks* out) {
+  *out = HadMasks{};
+  if (m == 1) {
+    QR_CHECK_ARG(had_m == nullptr, QUAROT_ERR_INVALID, "had_m must be NULL when m = 1");
+    out->nz[0] = 1u;
+    return QUAROT_OK;
+  }
+  QR_CHECK_ARG(m >= 4 && m <= 32 && m % 4 == 0, QUAROT_ERR_UNSUPPORTED,
+               "m = %d: the small Hadamard factor must have order 1 or a multiple of 4 up to 32",
+               m);
+  QR_CHECK_ARG(had_m != nullptr, QUAROT_ERR_INVALID, "had_m is required for m = %d", m);
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < m; ++j) {
+      const int e = had_m[i * m + j];
+      QR_CHECK_ARG(e == 1 || e == -1, QUAROT_ERR_INVALID,
+                   "had_m[%d][%d] = %d: entries must be +1 or -1", i, j, e);
+    }
+  for (int i = 0; i < m; ++i)
+    for (int j = i; j < m; ++j) {
+      int dot = 0;
+      for (int k = 0; k < m; ++k) dot += had_m[i * m + k] * had_m[j * m + k];
+      QR_CHECK_ARG(dot == (i == j ? m : 0), QUAROT_ERR_INVALID,
+                   "had_m is not a Hadamard matrix: rows %d and %d have dot product %d", i, j,
+                   dot);
+    }
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < m; ++j) {
+      out->nz[i] |= 1u << j;
+      if (had_m[i * m + j] < 0) out->neg[i] |= 1u << j;
+    }
+  return QUAROT_OK;
+}
+
+// Shared checks and dispatch of the rotate+quant entry points.  up != NULL:
+// the rows are SiLU(x) * up.
+int had_quant_checked(const void* x, int64_t ld_x, const void* up, int64_t ld_up, int64_t rows,
+                      int64_t d, const int8_t* signs, int32_t m, const int8_t* had_m,
+                      float clip_ratio, uint8_t* q_out, int64_t ld_q, void* scale_out,
+                      float* x_rot_out, void* stream) {
   QR_CHECK_ARG(rows >= 0, QUAROT_ERR_INVALID, "rows = %lld < 0", (long long)rows);
   QR_CHECK_ARG(d > 0, QUAROT_ERR_INVALID, "d = %lld <= 0", (long long)d);
   QR_CHECK_ARG(clip_ok(clip_ratio), QUAROT_ERR_INVALID, "clip_ratio must be in (0, 1]");
-  QR_CHECK_ARG(m == 1 || m == 12 || m == 28, QUAROT_ERR_UNSUPPORTED,
-               "m = %d: built-in Hadamard factors are 1, 12, 28", m);
+  HadMasks hm;
+  const int st = had_masks_checked(m, had_m, &hm);
+  if (st != QUAROT_OK) return st;
   QR_CHECK_ARG(d % m == 0 && is_pow2(d / m), QUAROT_ERR_UNSUPPORTED,
                "d = %lld is not 2^n * %d", (long long)d, m);
   QR_CHECK_ARG(d % 32 == 0 && d <= 32768, QUAROT_ERR_UNSUPPORTED,
                "d = %lld: need d %% 32 == 0 and d <= 32768", (long long)d);
-  QR_CHECK_ARG(ld_x >= d, QUAROT_ERR_INVALID, "ld_x = %lld < d", (long long)ld_x);
+  QR_CHECK_ARG(ld_x >= d, QUAROT_ERR_INVALID, "row stride %lld < d", (long long)ld_x);
+  QR_CHECK_ARG(up == nullptr || ld_up >= d, QUAROT_ERR_INVALID, "ld_up = %lld < d",
+               (long long)ld_up);
   QR_CHECK_ARG(ld_q >= d / 2, QUAROT_ERR_INVALID, "ld_q = %lld < d/2", (long long)ld_q);
   if (rows == 0) return QUAROT_OK;
-  QR_CHECK_ARG(x && q_out && scale_out, QUAROT_ERR_INVALID, "x, q_out and scale_out are required");
+  QR_CHECK_ARG(x && q_out && scale_out, QUAROT_ERR_INVALID,
+               "the input, q_out and scale_out are required");
   QR_CHECK_ARG(aligned(x, 16) && ld_x % 8 == 0, QUAROT_ERR_MISALIGNED,
-               "x must be 16-byte aligned with ld_x %% 8 == 0");
+               "the input must be 16-byte aligned with a row stride %% 8 == 0");
+  QR_CHECK_ARG(up == nullptr || (aligned(up, 16) && ld_up % 8 == 0), QUAROT_ERR_MISALIGNED,
+               "up must be 16-byte aligned with ld_up %% 8 == 0");
   QR_CHECK_ARG(aligned(q_out, 16) && ld_q % 16 == 0, QUAROT_ERR_MISALIGNED,
                "q_out must be 16-byte aligned with ld_q %% 16 == 0");
   QR_CHECK_ARG(aligned(scale_out, 2), QUAROT_ERR_MISALIGNED, "scale_out must be 2-byte aligned");
@@ -103,30 +148,32 @@ int had_quant_checked(const void* x, int64_t rows, int64_t d, int64_t ld_x, cons
                "x_rot_out must be 16-byte aligned");
   QR_CHECK_ARG(rows <= (int64_t(1) << 31) - 1, QUAROT_ERR_UNSUPPORTED, "rows too large");
   const int n = log2_exact(d / m);
-  return launch_had_quant(static_cast<const __half*>(x), rows, int(d), n, m, ld_x, signs,
-                          clip_ratio, q_out, ld_q, static_cast<__half*>(scale_out), x_rot_out,
-                          rms_eps, static_cast<hipStream_t>(stream));
+  const RowSource src{static_cast<const __half*>(x), ld_x, static_cast<const __half*>(up),
+                      ld_up};
+  return launch_had_quant(src, rows, int(d), n, m, hm, signs, clip_ratio, q_out, ld_q,
+                          static_cast<__half*>(scale_out), x_rot_out,
+                          static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
 
 int quarot_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x,
-                     const int8_t* signs, int32_t m, float clip_ratio,
+                     const int8_t* signs, int32_t m, const int8_t* had_m, float clip_ratio,
                      uint8_t* q_out, int64_t ld_q, void* scale_out,
                      float* x_rot_out, void* stream) {
   clear_error();
-  return had_quant_checked(x, rows, d, ld_x, signs, m, clip_ratio, q_out, ld_q, scale_out,
-                           x_rot_out, -1.0f, stream);
+  return had_quant_checked(x, ld_x, nullptr, 0, rows, d, signs, m, had_m, clip_ratio, q_out,
+                           ld_q, scale_out, x_rot_out, stream);
 }
 
-int quarot_rmsnorm_had_quant(const void* x, int64_t rows, int64_t d, int64_t ld_x, float eps,
-                             const int8_t* signs, int32_t m, float clip_ratio,
-                             uint8_t* q_out, int64_t ld_q, void* scale_out,
-                             float* x_rot_out, void* stream) {
+int quarot_swiglu_had_quant(const void* gate, const void* up, int64_t rows, int64_t d,
+                            int64_t ld_gate, int64_t ld_up, const int8_t* signs, int32_t m,
+                            const int8_t* had_m, float clip_ratio, uint8_t* q_out, int64_t ld_q,
+                            void* scale_out, float* x_rot_out, void* stream) {
   clear_error();
-  QR_CHECK_ARG(eps > 0.0f && eps < INFINITY, QUAROT_ERR_INVALID, "eps must be finite and > 0");
-  return had_quant_checked(x, rows, d, ld_x, signs, m, clip_ratio, q_out, ld_q, scale_out,
-                           x_rot_out, eps, stream);
+  QR_CHECK_ARG(rows == 0 || up != nullptr, QUAROT_ERR_INVALID, "up is required");
+  return had_quant_checked(gate, ld_gate, up, ld_up, rows, d, signs, m, had_m, clip_ratio, q_out,
+                           ld_q, scale_out, x_rot_out, stream);
 }
 
 int quarot_cross_head_had_quant(const void* z, int64_t rows, int64_t n_heads, int64_t head_dim,
@@ -195,7 +242,8 @@ int quarot_kv_had_quant(const void* k, const void* v,
                         int32_t mode, float clip_ratio,
                         uint8_t* k_q, void* k_scale, void* k_zero,
                         uint8_t* v_q, void* v_scale, void* v_zero,
-                        int64_t S_cache, int64_t pos0, void* stream) {
+                        int64_t S_cache, int64_t pos0, float* k_rot_out, float* v_rot_out,
+                        void* stream) {
   clear_error();
   QR_CHECK_ARG(B >= 0 && H >= 0 && S >= 0, QUAROT_ERR_INVALID, "B, H, S must be >= 0");
   QR_CHECK_ARG(D == 32 || D == 64 || D == 128 || D == 256, QUAROT_ERR_UNSUPPORTED,
@@ -216,6 +264,7 @@ int quarot_kv_had_quant(const void* k, const void* v,
   uint8_t* qs[2] = {k_q, v_q};
   void* ss[2] = {k_scale, v_scale};
   void* zs[2] = {k_zero, v_zero};
+  float* rs[2] = {k_rot_out, v_rot_out};
   for (int i = 0; i < 2; ++i) {
     if (!srcs[i]) continue;
     QR_CHECK_ARG(qs[i] && ss[i], QUAROT_ERR_INVALID, "%s_q and %s_scale are required",
@@ -225,9 +274,11 @@ int quarot_kv_had_quant(const void* k, const void* v,
     QR_CHECK_ARG(aligned(srcs[i], 16) && aligned(qs[i], 16) && aligned(ss[i], 2) &&
                      (mode == 0 || aligned(zs[i], 2)),
                  QUAROT_ERR_MISALIGNED, "inputs and code buffers must be 16-byte aligned");
+    QR_CHECK_ARG(rs[i] == nullptr || aligned(rs[i], 16), QUAROT_ERR_MISALIGNED,
+                 "%s_rot_out must be 16-byte aligned", i ? "v" : "k");
     t[nt++] = KvTensorArgs{static_cast<const __half*>(srcs[i]), qs[i],
                            static_cast<__half*>(ss[i]),
-                           mode == 1 ? static_cast<__half*>(zs[i]) : nullptr};
+                           mode == 1 ? static_cast<__half*>(zs[i]) : nullptr, rs[i]};
   }
   QR_CHECK_ARG(B * H * S < (int64_t(1) << 31), QUAROT_ERR_UNSUPPORTED, "too many groups");
   return launch_kv_had_quant(t, nt, B, H, S, int(D), stride_b, stride_h, stride_s, signs,

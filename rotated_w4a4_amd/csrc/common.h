@@ -1,7 +1,8 @@
 // Internal helpers shared by the HIP sources of libquarot (not installed).
 //
 // Contents: status/last-error plumbing, the compile-time Paley type-I
-// Hadamard factors H_12 and H_28, and small device utilities.
+// Hadamard matrices of order 12 and 28 (handed out by quarot_hadamard_factor),
+// the H_m bit masks and the kernel launchers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -154,13 +155,32 @@ static_assert(had_factor_ok<12>(), "H_12 is not Hadamard");
 static_assert(had_factor_ok<28>(), "H_28 is not Hadamard");
 
 // ---------------------------------------------------------------------------
+// The small Hadamard factor H_m as bit masks over columns, rows and columns
+// padded to 32 with zeros: row r has entry -1 where bit c of neg[r] is set,
+// +1 where only bit c of nz[r] is set, 0 where neither is.  Built on the
+// host from the caller's matrix and handed to the kernels by value.
+// ---------------------------------------------------------------------------
+struct HadMasks {
+  uint32_t neg[32];
+  uint32_t nz[32];
+};
+
+// The rows a rotate+quant launch reads: x (fp16, row stride ld_x), or, with
+// up != nullptr, the gated product SiLU(x) * up formed on the fly (x is then
+// the gate projection, up the up projection, row stride ld_up).
+struct RowSource {
+  const __half* x;
+  int64_t ld_x;
+  const __half* up;
+  int64_t ld_up;
+};
+
+// ---------------------------------------------------------------------------
 // Kernel launchers (one per .hip file); arguments already validated.
 // ---------------------------------------------------------------------------
-// rms_eps < 0: plain rotate+quant; rms_eps >= 0: each row is first divided
-// by sqrt(mean(x^2) + rms_eps).
-int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t ld_x,
-                     const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
-                     __half* scale_out, float* x_rot_out, float rms_eps, hipStream_t stream);
+int launch_had_quant(const RowSource& src, int64_t rows, int d, int n, int m,
+                     const HadMasks& hm, const int8_t* signs, float clip_ratio, uint8_t* q_out,
+                     int64_t ld_q, __half* scale_out, float* x_rot_out, hipStream_t stream);
 
 int launch_w4a4_gemm(const uint8_t* a_q, int64_t lda, const __half* a_scale,
                      const uint8_t* b_q, int64_t ldb, const __half* b_scale,
@@ -172,6 +192,7 @@ struct KvTensorArgs {
   uint8_t* q;
   __half* scale;
   __half* zero;  // asymmetric mode only
+  float* rot;    // optional fp32 [B, H, S, D] copy of the rotated groups
 };
 
 int launch_kv_had_quant(const KvTensorArgs* t, int n_tensors, int64_t B, int64_t H,

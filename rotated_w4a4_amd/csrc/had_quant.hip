@@ -1,24 +1,27 @@
-// quarot_had_quant kernels: fused randomized Hadamard rotation + per-token
-// symmetric INT4 quantisation with nibble packing.
+// quarot_had_quant / quarot_swiglu_had_quant kernels: fused randomized
+// Hadamard rotation + per-token symmetric INT4 quantisation with nibble
+// packing.
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary): section 3.4 Stage 1a (R = H diag(s); H_d = H_{2^n} (x) H_m for
-// d = 2^n m), Stage 1b (online FWHT in FP32 before the down-projection),
-// Stage 2b (per-token symmetric scale) and "Kernel Implementation and
-// Hardware Efficiency" (quantise, pack two INT4 per byte).  "QuaRot Guide",
-// section 3 of "The Architecture": the FWHT is d log d additions and
-// subtractions.
+// d = 2^n m), Stage 1b (online FWHT in FP32 before the down-projection, on
+// the SwiGLU product), Stage 2b (per-token symmetric scale) and "Kernel
+// Implementation and Hardware Efficiency" (quantise, pack two INT4 per
+// byte).  "QuaRot Guide", section 3 of "The Architecture": the FWHT is
+// d log d additions and subtractions.
 //
 // Kernels:
-//   * had_quant_quad<D>   d = 32..256: a quad of lanes per row (quad_rows.h).
-//   * had_quant_4096_split  d = 4096: two waves per row, one LDS exchange
-//                         (split_rows.h).
+//   * had_quant_quad<D>   d = 32..256, m = 1: a quad of lanes per row
+//                         (quad_rows.h).
+//   * had_quant_4096_split  d = 4096, m = 1: two waves per row, one LDS
+//                         exchange (split_rows.h).
 //   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
-//                         on the matrix cores, one LDS exchange (kron_rows.h).
-//   * had_quant_lds<M>    any supported d (<= 32768): one workgroup per row,
-//                         the row staged in LDS as fp32; H_m applied per
+//                         on the matrix cores, one LDS exchange
+//                         (kron_rows.h); also the gated product.
+//   * had_quant_lds       any supported d (<= 32768) and m: one workgroup per
+//                         row, the row staged in LDS as fp32; H_m applied per
 //                         contiguous group, then radix-32 FWHT passes over
-//                         the power-of-two index.
+//                         the power-of-two index; also the gated product.
 #include "quad_rows.h"
 #include "wave_rows.h"
 #include "kron_rows.h"
@@ -30,11 +33,11 @@ namespace {
 
 constexpr int kQuadBlock = 256;  // 64 rows per block iteration
 
-template <int D, bool CLAMP, bool RMS>
+template <int D, bool CLAMP>
 __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
-    float* __restrict__ x_rot, float rms_eps) {
+    float* __restrict__ x_rot) {
   constexpr int NC = D / 32;
   const int lane_q = threadIdx.x & 3;
   uint4 mask[NC];
@@ -48,9 +51,8 @@ __global__ __launch_bounds__(kQuadBlock) void had_quant_quad(
     const int64_t rr = active ? r : 0;
     uint4 raw[NC];
     quad_load<D>(x + rr * ld_x, lane_q, raw);
-    quad_row<D, CLAMP, RMS>(raw, q_out + rr * ld_q, scale_out + rr,
-                            x_rot ? x_rot + rr * D : nullptr, mask, lane_q, clip_ratio, active,
-                            rms_eps);
+    quad_row<D, CLAMP>(raw, q_out + rr * ld_q, scale_out + rr, x_rot ? x_rot + rr * D : nullptr,
+                       mask, lane_q, clip_ratio, active);
   }
 }
 
@@ -63,40 +65,41 @@ constexpr int kRadixBits = 5;  // 32 values per FWHT task
 // LDS index with one pad word per 32 to spread strided accesses over banks.
 __device__ __forceinline__ int pidx(int e) { return e + (e >> 5); }
 
-template <int M>
-__device__ __forceinline__ void apply_hm(float* buf, int d) {
-  constexpr HadFactor<M> H = HadTable<M>::value;
-  const int groups = d / M;
+// H_m on every contiguous group of m (m <= 32), entries from the masks:
+// y[b] = sum_c (+-1) x[c], the sign from bit c of neg[b].
+__device__ __forceinline__ void apply_hm(float* buf, int d, int m, const HadMasks& hm) {
+  const int groups = d / m;
   for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-    float in[M], out[M];
+    float in[32];
 #pragma unroll
-    for (int b = 0; b < M; ++b) in[b] = buf[pidx(g * M + b)];
+    for (int c = 0; c < 32; ++c) in[c] = c < m ? buf[pidx(g * m + c)] : 0.0f;
 #pragma unroll
-    for (int b = 0; b < M; ++b) {
-      float acc = 0.0f;
+    for (int b = 0; b < 32; ++b) {
+      if (b < m) {
+        const uint32_t neg = hm.neg[b];
+        float acc = 0.0f;
 #pragma unroll
-      for (int c = 0; c < M; ++c) acc = (H.v[b][c] > 0) ? acc + in[c] : acc - in[c];
-      out[b] = acc;
+        for (int c = 0; c < 32; ++c) acc += ((neg >> c) & 1u) ? -in[c] : in[c];
+        buf[pidx(g * m + b)] = acc;  // in[] holds the group's inputs
+      }
     }
-#pragma unroll
-    for (int b = 0; b < M; ++b) buf[pidx(g * M + b)] = out[b];
   }
 }
 
-// One radix-2^R pass of the FWHT over the power-of-two index a (stride M)
+// One radix-2^R pass of the FWHT over the power-of-two index a (stride m)
 // covering index bits [s, s + R).
-template <int R, int M>
-__device__ __forceinline__ void fwht_pass(float* buf, int n, int s) {
-  const int tasks = (M << n) >> R;
+template <int R>
+__device__ __forceinline__ void fwht_pass(float* buf, int n, int m, int s) {
+  const int tasks = (m << n) >> R;
   for (int t = threadIdx.x; t < tasks; t += blockDim.x) {
-    const int b = t % M;
-    const int rest = t / M;
+    const int b = t % m;
+    const int rest = t / m;
     const int lo = rest & ((1 << s) - 1);
     const int hi = rest >> s;
     const int a0 = lo | (hi << (s + R));
     float v[1 << R];
 #pragma unroll
-    for (int j = 0; j < (1 << R); ++j) v[j] = buf[pidx((a0 + (j << s)) * M + b)];
+    for (int j = 0; j < (1 << R); ++j) v[j] = buf[pidx((a0 + (j << s)) * m + b)];
 #pragma unroll
     for (int h = 1; h < (1 << R); h <<= 1) {
 #pragma unroll
@@ -109,26 +112,33 @@ __device__ __forceinline__ void fwht_pass(float* buf, int n, int s) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < (1 << R); ++j) buf[pidx((a0 + (j << s)) * M + b)] = v[j];
+    for (int j = 0; j < (1 << R); ++j) buf[pidx((a0 + (j << s)) * m + b)] = v[j];
   }
 }
 
-template <int M, bool RMS>
+// SWIGLU: x is the gate projection and up the up projection; the row is
+// SiLU(x) * up in fp32.  m = 1 with a null mask set skips the H_m step.
+template <bool SWIGLU>
 __global__ __launch_bounds__(kLdsBlock) void had_quant_lds(
-    const __half* __restrict__ x, int64_t rows, int d, int n, int64_t ld_x,
-    const int8_t* __restrict__ signs, float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q,
-    __half* __restrict__ scale_out, float* __restrict__ x_rot, float norm, float rms_eps) {
+    const __half* __restrict__ x, int64_t ld_x, const __half* __restrict__ up, int64_t ld_up,
+    int64_t rows, int d, int n, int m, HadMasks hm, const int8_t* __restrict__ signs,
+    float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
+    float* __restrict__ x_rot, float norm) {
   extern __shared__ float buf[];
   __shared__ float red[kLdsBlock / 64];
-  __shared__ float red_ss[kLdsBlock / 64];
   const int chunks = d / 8;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const __half* src = x + row * ld_x;
-    // 1. load, flip signs, widen to fp32
+    // 1. load (and form the gated product), flip signs, widen to fp32
     for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * c);
       float f[8];
-      unpack_half8(raw, f);
+      unpack_half8(*reinterpret_cast<const uint4*>(src + 8 * c), f);
+      if (SWIGLU) {
+        float u[8];
+        unpack_half8(*reinterpret_cast<const uint4*>(up + row * ld_up + 8 * c), u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = silu_f32(f[i]) * u[i];
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float sgn = (signs && signs[8 * c + i] < 0) ? -1.0f : 1.0f;
@@ -137,8 +147,8 @@ __global__ __launch_bounds__(kLdsBlock) void had_quant_lds(
     }
     __syncthreads();
     // 2. H_m on each contiguous group of m
-    if (M > 1) {
-      apply_hm<M>(buf, d);
+    if (m > 1) {
+      apply_hm(buf, d, m, hm);
       __syncthreads();
     }
     // 3. FWHT over the 2^n index, radix-32 passes (last pass may be smaller)
@@ -146,49 +156,34 @@ __global__ __launch_bounds__(kLdsBlock) void had_quant_lds(
     while (s < n) {
       const int r = (n - s >= kRadixBits) ? kRadixBits : (n - s);
       switch (r) {
-        case 5: fwht_pass<5, M>(buf, n, s); break;
-        case 4: fwht_pass<4, M>(buf, n, s); break;
-        case 3: fwht_pass<3, M>(buf, n, s); break;
-        case 2: fwht_pass<2, M>(buf, n, s); break;
-        default: fwht_pass<1, M>(buf, n, s); break;
+        case 5: fwht_pass<5>(buf, n, m, s); break;
+        case 4: fwht_pass<4>(buf, n, m, s); break;
+        case 3: fwht_pass<3>(buf, n, m, s); break;
+        case 2: fwht_pass<2>(buf, n, m, s); break;
+        default: fwht_pass<1>(buf, n, m, s); break;
       }
       s += r;
       __syncthreads();
     }
     // 4. row absmax
-    float amax = 0.0f, ss = 0.0f;
+    float amax = 0.0f;
     for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float y = buf[pidx(8 * c + i)] * norm;
-        amax = fmaxf(amax, fabsf(y));
-        if (RMS) ss = fmaf(y, y, ss);
-      }
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(buf[pidx(8 * c + i)] * norm));
     }
     amax = wave_max(amax);
-    if (RMS) ss = wave_sum_dpp(ss);
-    if ((threadIdx.x & 63) == 0) {
-      red[threadIdx.x >> 6] = amax;
-      if (RMS) red_ss[threadIdx.x >> 6] = ss;
-    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
     __syncthreads();
     amax = red[0];
     for (int w = 1; w < int(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
-    // RMS: normalise by 1 / sqrt(mean(x^2) + eps); the rotation keeps the norm
-    float rs = 1.0f;
-    if (RMS) {
-      float tot = 0.0f;
-      for (int w = 0; w < int(blockDim.x >> 6); ++w) tot += red_ss[w];
-      rs = rsqrtf(tot / float(d) + rms_eps);
-    }
-    const __half s16 = row_scale_fp16(amax * rs, clip_ratio);
+    const __half s16 = row_scale_fp16(amax, clip_ratio);
     const float k = inv_scale(s16);
     // 5. quantise, pack, store
     uint8_t* qrow = q_out + row * ld_q;
     for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
       float f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = buf[pidx(8 * c + i)] * (norm * rs);
+      for (int i = 0; i < 8; ++i) f[i] = buf[pidx(8 * c + i)] * norm;
       *reinterpret_cast<uint32_t*>(qrow + 4 * c) = pack8(f, k);
       if (x_rot) {
         float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(d) + 8 * c);
@@ -212,15 +207,56 @@ int sm_count_cached() {
   return count;
 }
 
+// Raise the dynamic LDS limit of the Kronecker kernel instantiation once.
+template <int M, bool CLAMP, bool SWIGLU>
+bool kron_attr_ok() {
+  static const bool ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<M, CLAMP, SWIGLU>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          KronCfg<M, SWIGLU>::LDS_BYTES) == hipSuccess;
+  return ok;
+}
+
+template <int M, bool CLAMP, bool SWIGLU>
+int launch_kron(const RowSource& src, int64_t rows, const HadMasks& hm, const int8_t* signs,
+                float clip_ratio, uint8_t* q_out, int64_t ld_q, __half* scale_out,
+                float* x_rot_out, int cus, hipStream_t stream) {
+  using C = KronCfg<M, SWIGLU>;
+  if (!kron_attr_ok<M, CLAMP, SWIGLU>()) {
+    set_error("could not raise the dynamic LDS limit for d = %d", C::D);
+    return QUAROT_ERR_HIP;
+  }
+  // two waves per SIMD (up to 256 VGPRs): one or two blocks per CU
+  const int64_t cap = int64_t(cus) * C::BLOCKS_PER_CU;
+  const int64_t blocks = rows < cap ? rows : cap;
+  const float norm = 1.0f / sqrtf(float(C::D));
+  hipLaunchKernelGGL((had_quant_kron<M, CLAMP, SWIGLU>), dim3(unsigned(blocks)),
+                     dim3(unsigned(C::THREADS)), C::LDS_BYTES, stream, src.x, src.ld_x, src.up,
+                     src.ld_up, rows, signs, hm, clip_ratio, q_out, ld_q, scale_out, x_rot_out,
+                     norm);
+  return check_launch("had_quant_kron");
+}
+
+template <int M, bool SWIGLU>
+int launch_kron_clip(const RowSource& src, int64_t rows, const HadMasks& hm,
+                     const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
+                     __half* scale_out, float* x_rot_out, int cus, hipStream_t stream) {
+  if (clip_ratio != 1.0f)
+    return launch_kron<M, true, SWIGLU>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
+                                        x_rot_out, cus, stream);
+  return launch_kron<M, false, SWIGLU>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
+                                       x_rot_out, cus, stream);
+}
+
 }  // namespace
 
-int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t ld_x,
-                     const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
-                     __half* scale_out, float* x_rot_out, float rms_eps, hipStream_t stream) {
+int launch_had_quant(const RowSource& src, int64_t rows, int d, int n, int m,
+                     const HadMasks& hm, const int8_t* signs, float clip_ratio, uint8_t* q_out,
+                     int64_t ld_q, __half* scale_out, float* x_rot_out, hipStream_t stream) {
   const int cus = sm_count_cached();
-  const bool rms = rms_eps >= 0.0f;  // normalise each row by its RMS first
   const bool clamp = clip_ratio != 1.0f;
-  if (m == 1 && d <= 256) {
+  const bool gated = src.up != nullptr;
+  if (!gated && m == 1 && d <= 256) {
     const int64_t rpb = kQuadBlock / 4;
     int64_t blocks = (rows + rpb - 1) / rpb;
     // at most 2^16 blocks (beyond, blocks loop), far below the 2^32
@@ -228,17 +264,12 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
     const int64_t cap = int64_t(1) << 16;
     if (blocks > cap) blocks = cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kQuadBlock)};
-#define QR_QUAD(DD, CL, RM)                                                                    \
-  hipLaunchKernelGGL((had_quant_quad<DD, CL, RM>), grid, block, 0, stream, x, rows, ld_x, signs, \
-                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, rms_eps)
-#define QR_QUAD_D(DD)                   \
-  if (rms) {                            \
-    if (clamp) QR_QUAD(DD, true, true); \
-    else QR_QUAD(DD, false, true);      \
-  } else {                              \
-    if (clamp) QR_QUAD(DD, true, false); \
-    else QR_QUAD(DD, false, false);     \
-  }
+#define QR_QUAD(DD, CL)                                                                      \
+  hipLaunchKernelGGL((had_quant_quad<DD, CL>), grid, block, 0, stream, src.x, rows, src.ld_x, \
+                     signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out)
+#define QR_QUAD_D(DD)          \
+  if (clamp) QR_QUAD(DD, true); \
+  else QR_QUAD(DD, false)
     switch (d) {
       case 32: QR_QUAD_D(32); break;
       case 64: QR_QUAD_D(64); break;
@@ -249,87 +280,39 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
 #undef QR_QUAD
     return check_launch("had_quant_quad");
   }
-  if (m == 1 && d == 4096) {
+  if (!gated && m == 1 && d == 4096) {
     const int64_t cap = int64_t(cus) * 8;  // 16 KiB LDS, two waves per block
     const int64_t blocks = rows < cap ? rows : cap;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kSplitBlock)};
-#define QR_SPLIT(CL, RM)                                                                       \
-  hipLaunchKernelGGL((had_quant_4096_split<CL, RM>), grid, block, 0, stream, x, rows, ld_x, signs, \
-                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, rms_eps)
-    if (rms) {
-      if (clamp) QR_SPLIT(true, true); else QR_SPLIT(false, true);
-    } else {
-      if (clamp) QR_SPLIT(true, false); else QR_SPLIT(false, false);
-    }
-#undef QR_SPLIT
+    if (clamp)
+      hipLaunchKernelGGL((had_quant_4096_split<true>), grid, block, 0, stream, src.x, rows,
+                         src.ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out);
+    else
+      hipLaunchKernelGGL((had_quant_4096_split<false>), grid, block, 0, stream, src.x, rows,
+                         src.ld_x, signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out);
     return check_launch("had_quant_4096_split");
   }
-  if ((m == 12 || m == 28) && d == 1024 * m) {
-    static const bool kron_attr_ok = [] {
-      bool ok = true;
-#define QR_ATTR(MM, CL, RM)                                                                  \
-  ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<MM, CL, RM>),       \
-                            hipFuncAttributeMaxDynamicSharedMemorySize,                      \
-                            KronCfg<MM>::LDS_BYTES) == hipSuccess
-      QR_ATTR(12, false, false);
-      QR_ATTR(12, true, false);
-      QR_ATTR(12, false, true);
-      QR_ATTR(12, true, true);
-      QR_ATTR(28, false, false);
-      QR_ATTR(28, true, false);
-      QR_ATTR(28, false, true);
-      QR_ATTR(28, true, true);
-#undef QR_ATTR
-      return ok;
-    }();
-    if (!kron_attr_ok) {
-      set_error("could not raise the dynamic LDS limit for d = %d", d);
-      return QUAROT_ERR_HIP;
-    }
-    const size_t lds = m == 12 ? KronCfg<12>::LDS_BYTES : KronCfg<28>::LDS_BYTES;
-    // two waves per SIMD (up to 256 VGPRs): two 256-thread blocks per CU for
-    // m = 12, one 512-thread block for m = 28
-    const int64_t cap =
-        int64_t(cus) * (m == 12 ? KronCfg<12>::BLOCKS_PER_CU : KronCfg<28>::BLOCKS_PER_CU);
-    const int64_t blocks = rows < cap ? rows : cap;
-    const unsigned threads = m == 12 ? KronCfg<12>::THREADS : KronCfg<28>::THREADS;
-    const dim3 grid{unsigned(blocks)}, block{threads};
-    const float norm = 1.0f / sqrtf(float(d));
-#define QR_KRON(MM, CL, RM)                                                                     \
-  hipLaunchKernelGGL((had_quant_kron<MM, CL, RM>), grid, block, lds, stream, x, rows, ld_x, signs, \
-                     clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm, rms_eps)
-#define QR_KRON_M(MM)                    \
-  if (rms) {                             \
-    if (clamp) QR_KRON(MM, true, true);  \
-    else QR_KRON(MM, false, true);       \
-  } else {                               \
-    if (clamp) QR_KRON(MM, true, false); \
-    else QR_KRON(MM, false, false);      \
+  if (m == 12 && d == 1024 * 12) {
+    return gated ? launch_kron_clip<12, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                              scale_out, x_rot_out, cus, stream)
+                 : launch_kron_clip<12, false>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                               scale_out, x_rot_out, cus, stream);
   }
-    if (m == 12) {
-      QR_KRON_M(12);
-    } else {
-      QR_KRON_M(28);
-    }
-#undef QR_KRON_M
-#undef QR_KRON
-    return check_launch("had_quant_kron");
+  if (m == 28 && d == 1024 * 28) {
+    return gated ? launch_kron_clip<28, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                              scale_out, x_rot_out, cus, stream)
+                 : launch_kron_clip<28, false>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                               scale_out, x_rot_out, cus, stream);
   }
   const size_t lds = size_t(d + d / 32) * sizeof(float);
   // the generic kernel stages up to 32768 + 1024 floats (132 KiB) in LDS
   static const bool lds_attr_ok = [] {
     const int bytes = (32768 + 1024) * int(sizeof(float));
-    bool ok = true;
-#define QR_ATTR(MM, RM)                                                                       \
-  ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<MM, RM>),             \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess
-    QR_ATTR(1, false);
-    QR_ATTR(12, false);
-    QR_ATTR(28, false);
-    QR_ATTR(1, true);
-    QR_ATTR(12, true);
-    QR_ATTR(28, true);
-#undef QR_ATTR
+    bool ok = hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<false>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  bytes) == hipSuccess;
+    ok &= hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_lds<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
     return ok;
   }();
   if (!lds_attr_ok && lds > 65536) {
@@ -337,24 +320,17 @@ int launch_had_quant(const __half* x, int64_t rows, int d, int n, int m, int64_t
     return QUAROT_ERR_HIP;
   }
   const int64_t per_cu = (lds <= 40 * 1024) ? 4 : (lds <= 76 * 1024 ? 2 : 1);
-  int64_t blocks = rows < int64_t(cus) * per_cu ? rows : int64_t(cus) * per_cu;
+  const int64_t blocks = rows < int64_t(cus) * per_cu ? rows : int64_t(cus) * per_cu;
   const dim3 grid{unsigned(blocks)}, block{unsigned(kLdsBlock)};
   const float norm = 1.0f / sqrtf(float(d));
-#define QR_LDS(MM, RM)                                                                         \
-  hipLaunchKernelGGL((had_quant_lds<MM, RM>), grid, block, lds, stream, x, rows, d, n, ld_x,   \
-                     signs, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm, rms_eps)
-  switch (m) {
-    case 1:
-      if (rms) QR_LDS(1, true); else QR_LDS(1, false);
-      break;
-    case 12:
-      if (rms) QR_LDS(12, true); else QR_LDS(12, false);
-      break;
-    default:
-      if (rms) QR_LDS(28, true); else QR_LDS(28, false);
-      break;
-  }
-#undef QR_LDS
+  if (gated)
+    hipLaunchKernelGGL((had_quant_lds<true>), grid, block, lds, stream, src.x, src.ld_x, src.up,
+                       src.ld_up, rows, d, n, m, hm, signs, clip_ratio, q_out, ld_q, scale_out,
+                       x_rot_out, norm);
+  else
+    hipLaunchKernelGGL((had_quant_lds<false>), grid, block, lds, stream, src.x, src.ld_x, src.up,
+                       src.ld_up, rows, d, n, m, hm, signs, clip_ratio, q_out, ld_q, scale_out,
+                       x_rot_out, norm);
   return check_launch("had_quant_lds");
 }
 

@@ -1,6 +1,15 @@
 // Rotate+quant of rows of d = 1024 * m, m = 12 or 28 (H_1024 (x) H_m):
 // one workgroup owns one row (m = 28: 512 threads, one per CU; m = 12: 256
-// threads, two per CU, so two rows are in flight per CU).
+// threads, two per CU, so two rows are in flight per CU).  H_m is the
+// caller's matrix, handed in as bit masks.
+//
+// With SWIGLU the row is the gated FFN product c = SiLU(gate) * up, formed
+// in fp32 from the two fp16 inputs as they arrive (the same page, section
+// 3.4 Stage 1b: the online Hadamard acts on that product).  The matrix cores
+// take fp16 operands, so c is split into hi = fp16(c) and
+// lo = fp16((c - hi) * 2^11); H_m hi and H_m lo are two MFMAs with their own
+// fp32 accumulators, joined as H_m hi + 2^-11 H_m lo, keeping about 22 bits
+// of c.
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
@@ -33,40 +42,50 @@
 
 namespace quarot {
 
-// H_m as bit masks over columns, rows and columns padded to 32 with zeros:
-// row r has entry -1 where bit c of neg[r] is set, +1 where only bit c of
-// nz[r] is set, 0 where neither is.
-struct HadMasks {
-  uint32_t neg[32];
-  uint32_t nz[32];
-};
-
-template <int M>
-constexpr HadMasks make_had_masks() {
-  constexpr HadFactor<M> h = make_had_factor<M>();
-  HadMasks r{};
-  for (int i = 0; i < M; ++i)
-    for (int j = 0; j < M; ++j) {
-      r.nz[i] |= 1u << j;
-      if (h.v[i][j] < 0) r.neg[i] |= 1u << j;
-    }
-  return r;
-}
-
-__constant__ HadMasks kHadMasks12 = make_had_masks<12>();
-__constant__ HadMasks kHadMasks28 = make_had_masks<28>();
-
-template <int M>
-__device__ __forceinline__ const HadMasks& kron_masks() {
-  static_assert(M == 12 || M == 28, "Paley factors of order 12 and 28");
-  if constexpr (M == 12) return kHadMasks12;
-  else return kHadMasks28;
-}
-
 // Entry c of a mask row (already shifted to the lane's first column).
 __device__ __forceinline__ _Float16 had_entry(uint32_t nz, uint32_t neg, int c) {
   if (!((nz >> c) & 1u)) return _Float16(0.0f);
   return ((neg >> c) & 1u) ? _Float16(-1.0f) : _Float16(1.0f);
+}
+
+// Row r of the masks for a lane-dependent r < 32: the kernel argument is
+// read with uniform loads and selected per lane.
+__device__ __forceinline__ uint32_t mask_row(const uint32_t (&rowsv)[32], int r) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) out = (r == i) ? rowsv[i] : out;
+  return out;
+}
+
+// SiLU(t) = t / (1 + exp(-t)) in fp32: v_exp_f32 (2^x) and v_rcp_f32, each
+// within about one ulp.  For t -> -inf the exponential overflows to inf and
+// the result is -0; for t -> +inf it is t.
+__device__ __forceinline__ float silu_f32(float t) {
+  const float e = __builtin_amdgcn_exp2f(t * -1.4426950408889634f);
+  return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Eight gated products c = SiLU(g) * u from one 16-byte chunk of each input,
+// split for the matrix cores: hi = fp16(c), lo = fp16((c - hi) * 2^11).
+// c is made opaque once formed: otherwise the backend folds fp16(s * u) into
+// a single-rounding mixed-precision multiply for the residual while the
+// operand takes fp16 of the rounded product, and where the two disagree by an
+// fp16 ulp the low part no longer completes hi.
+__device__ __forceinline__ void swiglu_split8(const uint4& g, const uint4& u, uint4& hi,
+                                              uint4& lo) {
+  float gf[8], uf[8];
+  unpack_half8(g, gf);
+  unpack_half8(u, uf);
+  half8_t h, l;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float c = silu_f32(gf[j]) * uf[j];
+    asm volatile("" : "+v"(c));
+    h[j] = static_cast<_Float16>(c);
+    l[j] = static_cast<_Float16>((c - static_cast<float>(h[j])) * 2048.0f);
+  }
+  hi = __builtin_bit_cast(uint4, h);
+  lo = __builtin_bit_cast(uint4, l);
 }
 
 // LDS row of group a: a2 is flipped when a4 is set.  Phase 1 writes 16
@@ -107,20 +126,26 @@ __device__ __forceinline__ void dpp_fmac_stage(float (&v)[N], float c) {
 #undef QR_FMAC_DPP
 }
 
-template <int M>
+template <int M, bool SWIGLU = false>
 struct KronCfg {
   static constexpr int D = 1024 * M;
   // m = 12: 256-thread blocks (four waves, sixteen phase-1 tiles each), two
   // blocks per CU, so two rows are in flight per CU with their own barriers
   // and prefetches; m = 28 rows (112 KiB of fp32 in LDS) take the whole CU:
-  // one 512-thread block of eight waves with eight tiles each
-  static constexpr int NWAVE = (M == 12) ? 4 : 8;
+  // one 512-thread block of eight waves with eight tiles each.  The gated
+  // product prefetches two inputs, which sixteen tiles per lane would not
+  // hold: it always runs eight waves of eight tiles.
+  static constexpr bool TWO_BLOCKS = (M == 12) && !SWIGLU;
+  static constexpr int NWAVE = TWO_BLOCKS ? 4 : 8;
   static constexpr int THREADS = 64 * NWAVE;
   static constexpr int TILES = 1024 / (16 * NWAVE);
-  static constexpr int BLOCKS_PER_CU = (M == 12) ? 2 : 1;
-  // the sign masks of sixteen tiles kept as their int8 words (32 registers
-  // instead of 64), expanded per row
-  static constexpr bool COMPACT_SIGNS = TILES > 8;
+  static constexpr int BLOCKS_PER_CU = TWO_BLOCKS ? 2 : 1;
+  // how the lane keeps its phase-1 signs across rows: 0 the fp16 sign-bit
+  // masks (four registers per tile), 1 the int8 sign words (two per tile,
+  // expanded per row: sixteen tiles), 2 one bit per element (a byte per
+  // tile, four tiles per register: the gated product, whose second input
+  // stream needs the registers)
+  static constexpr int SIGN_STORE = SWIGLU ? 2 : (TILES > 8 ? 1 : 0);
   // b per phase-2 task: 4 (m = 12: 192 tasks, m = 28: 448)
   static constexpr int BW = 4;
   static constexpr int UNITS = M / BW;      // runs of BW consecutive b per group
@@ -131,19 +156,18 @@ struct KronCfg {
   static_assert(TASKS <= THREADS, "one phase-2 task per thread");
 };
 
-// RMS: the row is normalised by 1 / sqrt(mean(x^2) + rms_eps) first (the
-// rotation fused into RMSNorm, gain absorbed); the factor comes from the
-// rotated values (the rotation keeps the norm) and scales the quantiser.
-template <int M, bool CLAMP, bool RMS>
-__global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
-    const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
-    float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
-    float* __restrict__ x_rot, float norm, float rms_eps) {
-  using C = KronCfg<M>;
+// SWIGLU: x is the gate projection and up the up projection; the row is
+// SiLU(x) * up.  Otherwise up is unused and the row is x.
+template <int M, bool CLAMP, bool SWIGLU>
+__global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kron(
+    const __half* __restrict__ x, int64_t ld_x, const __half* __restrict__ up, int64_t ld_up,
+    int64_t rows, const int8_t* __restrict__ signs, HadMasks hm, float clip_ratio,
+    uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
+    float* __restrict__ x_rot, float norm) {
+  using C = KronCfg<M, SWIGLU>;
   extern __shared__ float4 kron_lds[];  // the row in fp32 (phase 1 -> phase 2), then its codes
   float* buf = reinterpret_cast<float*>(kron_lds);
   __shared__ float red[C::NWAVE];
-  __shared__ float red_ss[C::NWAVE];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -160,11 +184,11 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
   const uint32_t keep_lo = cnt == 8 ? 0xFFFFFFFFu : 0u;
   const uint32_t keep_hi = cnt > 0 ? 0xFFFFFFFFu : 0u;
   // A operands: H_m rows n (and 16 + n) against the lane's K slots, zero
-  // padded: slot j pairs with column 8 g + j, or 8 g + j - 4 for a half chunk
+  // padded: slot j pairs with column 8 g + j, or 8 g + j - 4 for a half chunk.
   const int shift = cnt == 4 ? 4 : 0;
-  const HadMasks& hm = kron_masks<M>();
-  const uint32_t nz_lo = hm.nz[n] >> (8 * g), neg_lo = hm.neg[n] >> (8 * g);
-  const uint32_t nz_hi = hm.nz[n + 16] >> (8 * g), neg_hi = hm.neg[n + 16] >> (8 * g);
+  const uint32_t nz_lo = mask_row(hm.nz, n) >> (8 * g), neg_lo = mask_row(hm.neg, n) >> (8 * g);
+  const uint32_t nz_hi = mask_row(hm.nz, n + 16) >> (8 * g);
+  const uint32_t neg_hi = mask_row(hm.neg, n + 16) >> (8 * g);
   half8_t h_lo, h_hi;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -174,10 +198,11 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
   }
   // signs of this lane's phase-1 elements (the same for every row): group
   // a = (1024 / NWAVE) wave + 16 t + n.  Either the fp16 sign-bit masks
-  // (8 tiles) or the int8 sign words, expanded per row (16 tiles).
+  // or the int8 sign words, expanded per row.
   constexpr int TILES = C::TILES, AW = 1024 / C::NWAVE;
-  uint4 mask[C::COMPACT_SIGNS ? 1 : TILES];
-  uint2 sw[C::COMPACT_SIGNS ? TILES : 1];
+  uint4 mask[C::SIGN_STORE == 0 ? TILES : 1];
+  uint2 sw[C::SIGN_STORE == 1 ? TILES : 1];
+  uint32_t sbits[C::SIGN_STORE == 2 ? (TILES + 3) / 4 : 1] = {};
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
     uint32_t w0 = 0, w1 = 0;
@@ -186,8 +211,19 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
       __builtin_memcpy(&w0, signs + a * M + off16, 4);
       __builtin_memcpy(&w1, signs + a * M + off16 + 4, 4);
     }
-    if constexpr (C::COMPACT_SIGNS) sw[t] = make_uint2(w0 & keep_lo, w1 & keep_hi);
-    else mask[t] = sign_masks8(w0 & keep_lo, w1 & keep_hi);
+    w0 &= keep_lo;
+    w1 &= keep_hi;
+    if constexpr (C::SIGN_STORE == 0) {
+      mask[t] = sign_masks8(w0, w1);
+    } else if constexpr (C::SIGN_STORE == 1) {
+      sw[t] = make_uint2(w0, w1);
+    } else {
+      // bit j of the tile's byte: element j negative (bit 7 of its int8)
+      const uint32_t b = ((w0 >> 7) & 1u) | ((w0 >> 14) & 2u) | ((w0 >> 21) & 4u) |
+                         ((w0 >> 28) & 8u) | (((w1 >> 7) & 1u) << 4) | (((w1 >> 14) & 2u) << 4) |
+                         (((w1 >> 21) & 4u) << 4) | (((w1 >> 28) & 8u) << 4);
+      sbits[t >> 2] |= b << (8 * (t & 3));
+    }
   }
   const float s_q1 = (lane & 1) ? -1.0f : 1.0f;
   const float s_q2 = (lane & 2) ? -1.0f : 1.0f;
@@ -200,45 +236,98 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
   // sign left on this task's values by the phase-1 DPP stages
   const float sigma = (__builtin_popcount(combo & 7) & 1) ? -1.0f : 1.0f;
 
-  // loads of one row's phase-1 chunks
-  auto load_row = [&](int64_t row, uint4 (&raw)[TILES]) {
-    const __half* src = x + row * ld_x;
+  // loads of one row's phase-1 chunks (the up projection's too when gated):
+  // buffer loads over the row, so a lane keeps one 32-bit offset (tile t
+  // adds 32 m bytes) instead of a 64-bit address per tile and stream.
+  // (The lanes past m are masked at use: masking here would make the
+  // prefetch wait for its own data.)
+  constexpr int TU = SWIGLU ? TILES : 1;
+  const int lane_off = 2 * ((AW * wave + n) * M + off16);
+  auto load_row = [&](int64_t row, uint4 (&raw)[TILES], uint4 (&raw_u)[TU]) {
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(x + row * ld_x), 0, 2 * C::D,
+                                          0x00020000);
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int a = AW * wave + 16 * t + n;
-      // (the lanes past m are masked at use: masking here would make the
-      // prefetch wait for its own data; 8-byte aligned, one dwordx4)
-      __builtin_memcpy(&raw[t], src + a * M + off16, 16);
+    for (int t = 0; t < TILES; ++t)
+      raw[t] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane_off + 32 * M * t, 0, 0));
+    if constexpr (SWIGLU) {
+      const __amdgpu_buffer_rsrc_t ru =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(up + row * ld_up), 0, 2 * C::D,
+                                            0x00020000);
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+        raw_u[t] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ru, lane_off + 32 * M * t, 0, 0));
     }
   };
 
   int64_t row = blockIdx.x;
-  uint4 raw[TILES];
-  if (row < rows) load_row(row, raw);
+  uint4 raw[TILES], raw_u[TU];
+  if (row < rows) load_row(row, raw, raw_u);
   for (; row < rows; row += gridDim.x) {
     float v[8 * TILES];
     // ---- phase 1: H_m on the matrix cores --------------------------------
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      uint4 r = raw[t];
       uint4 mk;
-      if constexpr (C::COMPACT_SIGNS) {
+      if constexpr (C::SIGN_STORE == 0) {
+        mk = mask[t];
+      } else if constexpr (C::SIGN_STORE == 1) {
         // (opaque per row, so the expansion is not hoisted out of the row loop)
         uint32_t s0 = sw[t].x, s1 = sw[t].y;
         asm volatile("" : "+v"(s0), "+v"(s1));
         mk = sign_masks8(s0, s1);
       } else {
-        mk = mask[t];
+        uint32_t b = sbits[t >> 2];
+        asm volatile("" : "+v"(b));
+        b >>= 8 * (t & 3);
+        // element 2i to bit 15, element 2i + 1 to bit 31 of word i
+        mk.x = ((b & 1u) << 15) | ((b & 2u) << 30);
+        mk.y = ((b & 4u) << 13) | ((b & 8u) << 28);
+        mk.z = ((b & 16u) << 11) | ((b & 32u) << 26);
+        mk.w = ((b & 64u) << 9) | ((b & 128u) << 24);
       }
-      r.x = (r.x & keep_lo) ^ mk.x;
-      r.y = (r.y & keep_lo) ^ mk.y;
-      r.z = (r.z & keep_hi) ^ mk.z;
-      r.w = (r.w & keep_hi) ^ mk.w;
-      const half8_t bop = __builtin_bit_cast(half8_t, r);
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const float4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
-      float4_t d1 = zero;
-      if (C::HALVES == 2) d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bop, zero, 0, 0, 0);
+      float4_t d0, d1 = zero;
+      if constexpr (SWIGLU) {
+        uint4 hi, lo;
+        swiglu_split8(raw[t], raw_u[t], hi, lo);
+        hi.x = (hi.x & keep_lo) ^ mk.x;
+        hi.y = (hi.y & keep_lo) ^ mk.y;
+        hi.z = (hi.z & keep_hi) ^ mk.z;
+        hi.w = (hi.w & keep_hi) ^ mk.w;
+        lo.x = (lo.x & keep_lo) ^ mk.x;
+        lo.y = (lo.y & keep_lo) ^ mk.y;
+        lo.z = (lo.z & keep_hi) ^ mk.z;
+        lo.w = (lo.w & keep_hi) ^ mk.w;
+        const half8_t bh = __builtin_bit_cast(half8_t, hi);
+        const half8_t bl = __builtin_bit_cast(half8_t, lo);
+        // the low parts get their own accumulator: added on top of the high
+        // parts' sum inside one MFMA they kept only part of their bits
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bh, zero, 0, 0, 0);
+        const float4_t l0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bl, zero, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d0[q] = fmaf(l0[q], 1.0f / 2048.0f, d0[q]);
+        if (C::HALVES == 2) {
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bh, zero, 0, 0, 0);
+          const float4_t l1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bl, zero, 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d1[q] = fmaf(l1[q], 1.0f / 2048.0f, d1[q]);
+        }
+        // one tile's products at a time: interleaving the tiles' conversions
+        // would hold several tiles' temporaries at once and spill
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        uint4 r = raw[t];
+        r.x = (r.x & keep_lo) ^ mk.x;
+        r.y = (r.y & keep_lo) ^ mk.y;
+        r.z = (r.z & keep_hi) ^ mk.z;
+        r.w = (r.w & keep_hi) ^ mk.w;
+        const half8_t bop = __builtin_bit_cast(half8_t, r);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
+        if (C::HALVES == 2) d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bop, zero, 0, 0, 0);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[8 * t + q] = d0[q];
@@ -247,7 +336,7 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
     }
     // prefetch the next row
     const int64_t nrow = row + gridDim.x;
-    if (nrow < rows) load_row(nrow, raw);
+    if (nrow < rows) load_row(nrow, raw, raw_u);
     // a4-a6: register bits 3-5 (a7, a tile bit too with sixteen tiles, is
     // left to phase 2)
 #pragma unroll
@@ -280,21 +369,28 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
     }
     __syncthreads();
     // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
-    // register r = BW q + i holds b = BW unit + i of group a(q)
+    // register r = BW q + i holds b = BW unit + i of group a(q).  Group
+    // a(q) = abase + 4 (q & 1) + 128 (q >> 1); its LDS row kron_row(a(q))
+    // flips bit 2 when bit 4 of abase is set.  The per-thread base is made
+    // opaque per row, so the sixteen addresses are base + constant in the loop
+    // rather than sixteen registers kept across it.
     constexpr int BW = C::BW;
-    float amax = 0.0f, ss = 0.0f;
+    float amax = 0.0f;
+    int tbase = abase * M + BW * unit;
+    asm volatile("" : "+v"(tbase));
+    const int flip4 = ((abase >> 4) & 1) ? 4 * M : 0;
     if (task_on) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int a = kron_row(abase + ((q & 1) << 2) + ((q >> 1) << 7));
+        const int a_off = ((q & 1) ? 4 * M - flip4 : flip4) + 128 * M * (q >> 1);
         if (BW == 4) {
-          const float4 f = *reinterpret_cast<const float4*>(buf + a * M + 4 * unit);
+          const float4 f = *reinterpret_cast<const float4*>(buf + tbase + a_off);
           v[4 * q] = f.x;
           v[4 * q + 1] = f.y;
           v[4 * q + 2] = f.z;
           v[4 * q + 3] = f.w;
         } else {
-          const float2 f = *reinterpret_cast<const float2*>(buf + a * M + 2 * unit);
+          const float2 f = *reinterpret_cast<const float2*>(buf + tbase + a_off);
           v[2 * q] = f.x;
           v[2 * q + 1] = f.y;
         }
@@ -309,35 +405,24 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
             v[r + h] = a - b;
           }
 #pragma unroll
-      for (int r = 0; r < 16 * BW; ++r) {
-        amax = fmaxf(amax, fabsf(v[r]));
-        if (RMS) ss = fmaf(v[r], v[r], ss);
-      }
+      for (int r = 0; r < 16 * BW; ++r) amax = fmaxf(amax, fabsf(v[r]));
     }
     amax = wave_max_dpp(amax);
-    if (RMS) ss = wave_sum_dpp(ss);
-    if (lane == 0) {
-      red[wave] = amax;
-      if (RMS) red_ss[wave] = ss;
-    }
+    if (lane == 0) red[wave] = amax;
     __syncthreads();  // phase-2 reads of buf are done; red is complete
     amax = red[0];
 #pragma unroll
     for (int w = 1; w < C::NWAVE; ++w) amax = fmaxf(amax, red[w]);
-    float rs = 1.0f;
-    if (RMS) {
-      float tot = 0.0f;
-#pragma unroll
-      for (int w = 0; w < C::NWAVE; ++w) tot += red_ss[w];
-      rs = rsqrtf(tot * (norm * norm / float(C::D)) + rms_eps);  // mean(x^2) = sum(v^2) / d^2
-    }
-    const __half s16 = row_scale_fp16(amax * norm * rs, clip_ratio);
-    const float kq = inv_scale(s16) * norm * rs * sigma;
-    const float xnorm = norm * rs * sigma;
+    const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
+    const float kq = inv_scale(s16) * norm * sigma;
+    const float xnorm = norm * sigma;
     if (task_on) {
+      // element offset of register q's run in the row (natural order)
+      int ebase = abase * M + BW * unit;
+      asm volatile("" : "+v"(ebase));
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int a = abase + ((q & 1) << 2) + ((q >> 1) << 7);
+        const int e = ebase + M * (4 * (q & 1) + 128 * (q >> 1));
         if (BW == 4) {
           uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
           const float t0 = magic_code<CLAMP>(v[4 * q], kq), t1 = magic_code<CLAMP>(v[4 * q + 1], kq);
@@ -346,9 +431,9 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
                                                     __builtin_bit_cast(uint32_t, t0), 0x0c0c0400u);
           const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t3),
                                                     __builtin_bit_cast(uint32_t, t1), 0x0c0c0400u);
-          codes[(a * M + 4 * unit) >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
+          codes[e >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
           if (x_rot) {
-            float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + a * M + 4 * unit);
+            float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + e);
             *dst = make_float4(v[4 * q] * xnorm, v[4 * q + 1] * xnorm, v[4 * q + 2] * xnorm,
                                v[4 * q + 3] * xnorm);
           }
@@ -356,9 +441,9 @@ __global__ __launch_bounds__(KronCfg<M>::THREADS, 2) void had_quant_kron(
           uint8_t* codes = reinterpret_cast<uint8_t*>(buf + C::D);  // 2 codes per unit
           const uint32_t t0 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * q], kq));
           const uint32_t t1 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * q + 1], kq));
-          codes[(a * M + 2 * unit) >> 1] = uint8_t(((t1 << 4) | (t0 & 0xFu)) ^ 0x88u);
+          codes[e >> 1] = uint8_t(((t1 << 4) | (t0 & 0xFu)) ^ 0x88u);
           if (x_rot) {
-            float2* dst = reinterpret_cast<float2*>(x_rot + row * int64_t(C::D) + a * M + 2 * unit);
+            float2* dst = reinterpret_cast<float2*>(x_rot + row * int64_t(C::D) + e);
             *dst = make_float2(v[2 * q] * xnorm, v[2 * q + 1] * xnorm);
           }
         }

@@ -86,12 +86,14 @@ __global__ __launch_bounds__(kBlock) void kv_had_quant_kernel(KvLaunch p) {
       load_sign_masks<NC>(p.signs ? p.signs + head_key * p.signs_stride_h : nullptr, lane_q, mask);
       mask_head = head_key;
     }
+    // optional rotated copy, dense [B, H, S, D]: group g's row
+    float* rot = t.rot ? t.rot + int64_t(active ? g : 0) * D : nullptr;
     if (MODE == 0)
-      quad_row<D, CLAMP>(raw, t.q + slot * (D / 2), t.scale + slot, nullptr, mask, lane_q,
+      quad_row<D, CLAMP>(raw, t.q + slot * (D / 2), t.scale + slot, rot, mask, lane_q,
                          p.clip_ratio, active);
     else
-      quad_row_asym<D>(raw, t.q + slot * (D / 2), t.scale + slot, t.zero + slot, mask, lane_q,
-                       p.clip_ratio, active);
+      quad_row_asym<D>(raw, t.q + slot * (D / 2), t.scale + slot, t.zero + slot, rot, mask,
+                       lane_q, p.clip_ratio, active);
   }
 }
 

@@ -143,46 +143,27 @@ __device__ __forceinline__ float quad_sigma(int q) {
 // Rotate+quant (symmetric) of one row held by a quad, its raw chunks already
 // loaded.  qrow: code row (D/2 bytes); scale: where the fp16 scale goes;
 // xrot: optional fp32 row.
-template <int LB>
-__device__ __forceinline__ float quad_sum(float v) {
-  constexpr int ctrl = (LB == 0) ? 0xB1 : 0x4E;
-  return v + __builtin_bit_cast(
-                 float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
-}
 
-// With RMS the row is first normalised by 1 / sqrt(mean(x^2) + rms_eps)
-// ("QuaRot Guide", step 2 of "Deep Dive": the rotation fused into RMSNorm,
-// its gain absorbed into the next weights).  The rotation keeps the norm, so
-// the factor comes from the rotated values and scales the quantiser.
-template <int D, bool CLAMP, bool RMS = false>
+template <int D, bool CLAMP>
 __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __restrict__ qrow,
                                          __half* __restrict__ scale, float* __restrict__ xrot,
                                          const uint4 (&mask)[D / 32], int q, float clip_ratio,
-                                         bool active, float rms_eps = 0.0f) {
+                                         bool active) {
   constexpr int NC = D / 32;
   constexpr int E = 8 * NC;
   constexpr float kNorm = quad_norm<D>();
   float v[E];
   quad_transform<D>(raw, mask, q, active, v);
   // the transform is unnormalised: max|x~| = max|v| / sqrt(D)
-  float amax = 0.0f, ss = 0.0f;
+  float amax = 0.0f;
 #pragma unroll
-  for (int r = 0; r < E; ++r) {
-    amax = fmaxf(amax, fabsf(v[r]));
-    if (RMS) ss = fmaf(v[r], v[r], ss);
-  }
+  for (int r = 0; r < E; ++r) amax = fmaxf(amax, fabsf(v[r]));
   amax = quad_max<0>(amax);
   amax = quad_max<1>(amax);
-  float rs = 1.0f;
-  if (RMS) {
-    ss = quad_sum<0>(ss);
-    ss = quad_sum<1>(ss);
-    rs = rsqrtf(ss * (kNorm * kNorm / float(D)) + rms_eps);
-  }
-  const __half s16 = row_scale_fp16(amax * kNorm * rs, clip_ratio);
+  const __half s16 = row_scale_fp16(amax * kNorm, clip_ratio);
   if (!active) return;
   const float sigma = quad_sigma(q);
-  const float kq = inv_scale(s16) * kNorm * rs * sigma;
+  const float kq = inv_scale(s16) * kNorm * sigma;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     float t8[8];
@@ -197,7 +178,7 @@ __device__ __forceinline__ void quad_row(const uint4 (&raw)[D / 32], uint8_t* __
   }
   if (q == 0) *scale = s16;
   if (xrot) {
-    const float xn = kNorm * rs * sigma;
+    const float xn = kNorm * sigma;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       float4* dst = reinterpret_cast<float4*>(xrot + 8 * (q + 4 * j));
@@ -223,12 +204,13 @@ __device__ __forceinline__ float quad_min(float v) {
 // min and max of the group, S = fp16(max(range, 1e-5) / 15), the zero point
 // z = rint(-alpha_min / S) kept within +-1024 (stored as fp16, exact), and
 // the uint4 code q = clamp(rint(x / S) + z, 0, 15); element 2k in the low
-// nibble of byte k.
+// nibble of byte k.  xrot: optional fp32 row receiving x~.
 template <int D>
 __device__ __forceinline__ void quad_row_asym(const uint4 (&raw)[D / 32],
                                               uint8_t* __restrict__ qrow,
                                               __half* __restrict__ scale,
                                               __half* __restrict__ zero,
+                                              float* __restrict__ xrot,
                                               const uint4 (&mask)[D / 32], int q,
                                               float clip_ratio, bool active) {
   constexpr int NC = D / 32;
@@ -278,6 +260,17 @@ __device__ __forceinline__ void quad_row_asym(const uint4 (&raw)[D / 32],
   if (q == 0) {
     *scale = s16;
     *zero = __float2half_rn(z);
+  }
+  if (xrot) {
+    const float xn = kNorm * sigma;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      float4* dst = reinterpret_cast<float4*>(xrot + 8 * (q + 4 * j));
+      dst[0] = make_float4(v[8 * j + 0] * xn, v[8 * j + 1] * xn, v[8 * j + 2] * xn,
+                           v[8 * j + 3] * xn);
+      dst[1] = make_float4(v[8 * j + 4] * xn, v[8 * j + 5] * xn, v[8 * j + 6] * xn,
+                           v[8 * j + 7] * xn);
+    }
   }
 }
 

@@ -65,17 +65,13 @@ __device__ __forceinline__ void split_dpp_stage(float (&v)[32], float c) {
 #undef QR_FMAC_DPP4
 }
 
-// RMS: the row is normalised by 1 / sqrt(mean(x^2) + rms_eps) first (the
-// rotation fused into RMSNorm, gain absorbed); the factor comes from the
-// rotated values (the rotation keeps the norm) and scales the quantiser.
-template <bool CLAMP, bool RMS>
+template <bool CLAMP>
 __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
     const __half* __restrict__ x, int64_t rows, int64_t ld_x, const int8_t* __restrict__ signs,
     float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
-    float* __restrict__ x_rot, float rms_eps) {
+    float* __restrict__ x_rot) {
   __shared__ float4 lds[1024];
   __shared__ float red[kSplitBlock / 64];
-  __shared__ float red_ss[kSplitBlock / 64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -174,25 +170,16 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
           v[r] = a + b;
           v[r + h] = a - b;
         }
-    float amax = 0.0f, ss = 0.0f;
+    float amax = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      amax = fmaxf(amax, fabsf(v[r]));
-      if (RMS) ss = fmaf(v[r], v[r], ss);
-    }
+    for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(v[r]));
     amax = wave_max_dpp(amax);
-    if (RMS) ss = wave_sum_dpp(ss);
-    if (lane == 0) {
-      red[wave] = amax;
-      if (RMS) red_ss[wave] = ss;
-    }
+    if (lane == 0) red[wave] = amax;
     __syncthreads();  // phase-2 reads done, red complete
-    // the transform is unnormalised: 1/sqrt(4096) = 1/64 is exact, and
-    // mean(x^2) = sum(v^2) / 2^24
-    const float rs = RMS ? rsqrtf((red_ss[0] + red_ss[1]) * (1.0f / 16777216.0f) + rms_eps) : 1.0f;
-    amax = fmaxf(red[0], red[1]) * (1.0f / 64.0f) * rs;
+    // the transform is unnormalised: 1/sqrt(4096) = 1/64 is exact
+    amax = fmaxf(red[0], red[1]) * (1.0f / 64.0f);
     const __half s16 = row_scale_fp16(amax, clip_ratio);
-    const float kq = inv_scale(s16) * (1.0f / 64.0f) * rs * sigma;
+    const float kq = inv_scale(s16) * (1.0f / 64.0f) * sigma;
     uint8_t* qrow = q_out + row * ld_q;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -204,7 +191,7 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
     }
     if (threadIdx.x == 0) scale_out[row] = s16;
     if (x_rot) {
-      const float cn = (1.0f / 64.0f) * rs * sigma;
+      const float cn = (1.0f / 64.0f) * sigma;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int u = k >> 1;

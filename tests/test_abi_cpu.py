@@ -1,8 +1,9 @@
 """Host-side checks of libquarot (no GPU needed).
 
 * the library loads and exports every function declared in include/quarot.h;
-* its built-in Paley factors equal the oracle's (two independent
-  constructions of the same published definition);
+* its Paley factors equal the oracle's (two independent constructions of
+  the same published definition);
+* the caller's H_m (host memory) is validated: +-1 entries, H H^T = m I;
 * invalid arguments are rejected with the documented status before any HIP
   call (no call here reaches the device: each one fails validation).
 """
@@ -34,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
     names = set(re.findall(r"\b(quarot_[a-z0-9_]+)\s*\(", text))
     assert {"quarot_had_quant", "quarot_w4a4_gemm", "quarot_kv_had_quant",
             "quarot_kv_decode_attention", "quarot_kv_decode_workspace_bytes",
-            "quarot_rmsnorm_had_quant", "quarot_cross_head_had_quant"} <= names
+            "quarot_swiglu_had_quant", "quarot_cross_head_had_quant"} <= names
+    assert "quarot_rmsnorm_had_quant" not in names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -58,12 +60,29 @@ def test_status_strings(lib):
 FAKE = 0x10000  # 64 KiB-aligned host address never dereferenced by a failing call
 
 
+P12 = oracle.hadamard_m(12)
+
+
 def _hq(lib, **kw):
-    a = dict(x=FAKE, rows=4, d=256, ld_x=256, signs=None, m=1, clip=1.0, q=FAKE, ld_q=128,
-             scale=FAKE, xrot=None, stream=None)
+    a = dict(x=FAKE, rows=4, d=256, ld_x=256, signs=None, m=1, had_m=None, clip=1.0, q=FAKE,
+             ld_q=128, scale=FAKE, xrot=None, stream=None)
     a.update(kw)
-    return lib.quarot_had_quant(a["x"], a["rows"], a["d"], a["ld_x"], a["signs"], a["m"],
+    h = a["had_m"]
+    hp = h.ctypes.data_as(ctypes.c_void_p) if isinstance(h, np.ndarray) else h
+    return lib.quarot_had_quant(a["x"], a["rows"], a["d"], a["ld_x"], a["signs"], a["m"], hp,
                                 a["clip"], a["q"], a["ld_q"], a["scale"], a["xrot"], a["stream"])
+
+
+def _bad_entry():
+    h = P12.copy()
+    h[3, 5] = 0
+    return h
+
+
+def _not_orthogonal():
+    h = P12.copy()
+    h[3, 5] = -h[3, 5]  # +-1 entries, but rows 3 and 5 no longer orthogonal
+    return h
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -72,9 +91,18 @@ def _hq(lib, **kw):
     (dict(clip=0.0), INVALID),
     (dict(clip=1.5), INVALID),
     (dict(clip=float("nan")), INVALID),
-    (dict(m=20), UNSUPPORTED),
+    (dict(m=20), INVALID),  # had_m missing
+    (dict(m=5, had_m=np.ones((5, 5), np.int8)), UNSUPPORTED),
+    (dict(m=36, had_m=np.ones((36, 36), np.int8)), UNSUPPORTED),
+    (dict(m=2, had_m=np.ones((2, 2), np.int8)), UNSUPPORTED),
+    (dict(m=1, had_m=np.ones((1, 1), np.int8)), INVALID),  # NULL iff m == 1
+    (dict(m=12, d=12288, ld_x=12288, ld_q=6144), INVALID),  # had_m missing
+    (dict(m=12, d=12288, ld_x=12288, ld_q=6144, had_m=_bad_entry()), INVALID),
+    (dict(m=12, d=12288, ld_x=12288, ld_q=6144, had_m=_not_orthogonal()), INVALID),
+    (dict(m=12, d=12288, ld_x=12288, ld_q=6144, had_m=np.ones((12, 12), np.int8)), INVALID),
+    (dict(m=12, d=4096, ld_x=4096, ld_q=2048, had_m=P12), UNSUPPORTED),  # not 2^n * 12
     (dict(d=384, ld_x=384, ld_q=192), UNSUPPORTED),  # 384 = 3 * 128, not 2^n * 1
-    (dict(d=48, m=12, ld_x=48, ld_q=32), UNSUPPORTED),  # d % 32 != 0
+    (dict(d=48, m=12, had_m=P12, ld_x=48, ld_q=32), UNSUPPORTED),  # d % 32 != 0
     (dict(d=65536, ld_x=65536, ld_q=32768), UNSUPPORTED),
     (dict(ld_x=128), INVALID),
     (dict(ld_q=64), INVALID),
@@ -93,8 +121,44 @@ def test_had_quant_rejects(lib, kw, status):
     assert lib.quarot_last_error()
 
 
+def test_had_m_check_reports_the_rows(lib):
+    assert _hq(lib, m=12, d=12288, ld_x=12288, ld_q=6144, had_m=_not_orthogonal()) == INVALID
+    assert b"not a Hadamard matrix" in lib.quarot_last_error()
+
+
 def test_had_quant_zero_rows_is_noop(lib):
     assert _hq(lib, rows=0, x=None, q=None, scale=None) == OK
+
+
+def _sw(lib, **kw):
+    a = dict(g=FAKE, u=FAKE, rows=4, d=12288, ld_g=12288, ld_u=12288, signs=None, m=12,
+             had_m=P12, clip=1.0, q=FAKE, ld_q=6144, s=FAKE, xr=None)
+    a.update(kw)
+    h = a["had_m"]
+    hp = h.ctypes.data_as(ctypes.c_void_p) if isinstance(h, np.ndarray) else h
+    return lib.quarot_swiglu_had_quant(a["g"], a["u"], a["rows"], a["d"], a["ld_g"], a["ld_u"],
+                                       a["signs"], a["m"], hp, a["clip"], a["q"], a["ld_q"],
+                                       a["s"], a["xr"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), INVALID),
+    (dict(g=None), INVALID),
+    (dict(ld_u=12000), INVALID),
+    (dict(ld_u=12296 + 4), MISALIGNED),
+    (dict(u=FAKE + 8), MISALIGNED),
+    (dict(had_m=None), INVALID),
+    (dict(had_m=_not_orthogonal()), INVALID),
+    (dict(d=1000), UNSUPPORTED),
+    (dict(clip=2.0), INVALID),
+])
+def test_swiglu_had_quant_rejects(lib, kw, status):
+    assert _sw(lib, **kw) == status
+    assert lib.quarot_last_error()
+
+
+def test_swiglu_had_quant_zero_rows_is_noop(lib):
+    assert _sw(lib, rows=0, g=None, u=None, q=None, s=None) == OK
 
 
 def _gemm(lib, **kw):
@@ -137,12 +201,12 @@ def test_gemm_empty_is_noop(lib):
 def _kv(lib, **kw):
     a = dict(k=FAKE, v=FAKE, B=2, H=2, S=4, D=128, sb=1024, sh=512, ss=128, signs=None,
              ssh=0, mode=0, clip=1.0, kq=FAKE, ks=FAKE, kz=None, vq=FAKE, vs=FAKE, vz=None,
-             S_cache=8, pos0=0)
+             S_cache=8, pos0=0, kr=None, vr=None)
     a.update(kw)
     return lib.quarot_kv_had_quant(a["k"], a["v"], a["B"], a["H"], a["S"], a["D"], a["sb"],
                                    a["sh"], a["ss"], a["signs"], a["ssh"], a["mode"], a["clip"],
                                    a["kq"], a["ks"], a["kz"], a["vq"], a["vs"], a["vz"],
-                                   a["S_cache"], a["pos0"], None)
+                                   a["S_cache"], a["pos0"], a["kr"], a["vr"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -163,6 +227,8 @@ def _kv(lib, **kw):
     (dict(k=FAKE + 2), MISALIGNED),
     (dict(vq=FAKE + 4), MISALIGNED),
     (dict(ssh=-1), INVALID),
+    (dict(kr=FAKE + 4), MISALIGNED),
+    (dict(vr=FAKE + 8), MISALIGNED),
 ])
 def test_kv_rejects(lib, kw, status):
     assert _kv(lib, **kw) == status
@@ -232,33 +298,6 @@ def test_decode_workspace_size(lib):
     assert lib.quarot_kv_decode_workspace_bytes(1, 8, 1, 128, 0) == INVALID
     sizes = [lib.quarot_kv_decode_workspace_bytes(2, 8, 2, 128, n) for n in range(1, 3000, 37)]
     assert all(s > 0 for s in sizes)
-
-
-def _rms(lib, **kw):
-    a = dict(x=FAKE, rows=4, d=256, ld_x=256, eps=1e-5, signs=None, m=1, clip=1.0, q=FAKE,
-             ld_q=128, s=FAKE, xr=None)
-    a.update(kw)
-    return lib.quarot_rmsnorm_had_quant(a["x"], a["rows"], a["d"], a["ld_x"], a["eps"], a["signs"],
-                                        a["m"], a["clip"], a["q"], a["ld_q"], a["s"], a["xr"], None)
-
-
-@pytest.mark.parametrize("kw,status", [
-    (dict(eps=0.0), INVALID),
-    (dict(eps=-1e-5), INVALID),
-    (dict(eps=float("nan")), INVALID),
-    (dict(eps=float("inf")), INVALID),
-    (dict(d=100), UNSUPPORTED),
-    (dict(m=5), UNSUPPORTED),
-    (dict(clip=1.5), INVALID),
-    (dict(x=None), INVALID),
-    (dict(x=FAKE + 2), MISALIGNED),
-])
-def test_rmsnorm_had_quant_rejects(lib, kw, status):
-    assert _rms(lib, **kw) == status
-
-
-def test_rmsnorm_had_quant_zero_rows_is_noop(lib):
-    assert _rms(lib, rows=0, x=None, q=None, s=None) == OK
 
 
 def _ch(lib, **kw):

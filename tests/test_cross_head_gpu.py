@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import check_codes, check_rot, check_scales
+from parity import check_quant, check_rot
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -39,11 +39,10 @@ def host(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def check(z16, nh, clip, q, s, zr, frac):
+def check(z16, nh, clip, q, s, zr):
     ref = oracle.cross_head_quant(z16, nh, clip)
     err = check_rot(zr, ref["x_rot"])
-    check_scales(s, ref["scales"])
-    f = check_codes(oracle.unpack_int4(q), ref["codes"], frac=frac)
+    _, f = check_quant(oracle.unpack_int4(q), s, ref["x_rot"], ref["scales"])
     return err, f
 
 
@@ -60,7 +59,7 @@ def test_cross_head_head_counts(nh, clip):
     say(f"n_heads={nh} clip={clip} rows={rows}")
     zr = torch.empty((rows, nh * DH), dtype=torch.float32, device="cuda")
     q, s = qr.cross_head_had_quant(dev(z16), nh, clip, z_rot_out=zr)
-    err, f = check(z16, nh, clip, host(q), host(s), host(zr), 1e-2)
+    err, f = check(z16, nh, clip, host(q), host(s), host(zr))
     say(f"  rotated values max row-relative error {err:.2e}, code diff frac {f:.2e}")
     assert float(host(s)[7]) == float(np.float16(clip * 1e-5 / 7))
     assert not host(q)[7].any()
@@ -82,7 +81,7 @@ def test_cross_head_strided_rows():
     qr.cross_head_had_quant(z_dev, nh, 1.0, q_out=q_view, scale_out=s, z_rot_out=zr)
     qf = host(q_full)
     assert np.all(qf[:, d // 2:] == 0xA5)
-    check(np.ascontiguousarray(big[:, :d]), nh, 1.0, qf[:, : d // 2], host(s), host(zr), 1e-2)
+    check(np.ascontiguousarray(big[:, :d]), nh, 1.0, qf[:, : d // 2], host(s), host(zr))
 
 
 @pytest.mark.parametrize("nh", [4, 32])
@@ -103,7 +102,7 @@ def test_cross_head_unaligned_rows(nh):
     qr.cross_head_had_quant(z_dev, nh, 0.9, q_out=q_view, scale_out=s, z_rot_out=zr)
     qf = host(q_full)
     assert np.all(qf[:, d // 2:] == 0x5A)
-    check(np.ascontiguousarray(big[:, :d]), nh, 0.9, qf[:, : d // 2], host(s), host(zr), 1e-2)
+    check(np.ascontiguousarray(big[:, :d]), nh, 0.9, qf[:, : d // 2], host(s), host(zr))
 
 
 def test_cross_head_no_rows():
@@ -120,7 +119,7 @@ def test_cross_head_workload_rows(name, tokens):
     say(f"{name}: {tokens} x {cfg.d}")
     zr = torch.empty((tokens, cfg.d), dtype=torch.float32, device="cuda")
     q, s = qr.cross_head_had_quant(dev(z16), cfg.heads, z_rot_out=zr)
-    err, f = check(z16, cfg.heads, 1.0, host(q), host(s), host(zr), 1e-3)
+    err, f = check(z16, cfg.heads, 1.0, host(q), host(s), host(zr))
     say(f"  rotated values max row-relative error {err:.2e}, code diff frac {f:.2e}")
 
 
@@ -136,6 +135,5 @@ def test_cross_head_full_launch_sampled(name):
     rows = np.sort(np.random.default_rng(11).choice(cfg.tokens, 64, replace=False))
     rows[-1] = cfg.tokens - 1
     ref = oracle.cross_head_quant(z16[rows], cfg.heads)
-    check_scales(sh[rows], ref["scales"])
-    f = check_codes(oracle.unpack_int4(qh[rows]), ref["codes"], frac=1e-3)
+    _, f = check_quant(oracle.unpack_int4(qh[rows]), sh[rows], ref["x_rot"], ref["scales"])
     say(f"  sampled code diff frac {f:.2e}")

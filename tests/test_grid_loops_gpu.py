@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import check_codes, check_scales
+from parity import check_quant
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -59,8 +59,7 @@ def test_had_quant_rows_past_grid_cap():
     qh, sh = host(q), host(s)
     sel = sample(rows, per_pass, 1)
     ref = oracle.had_quant(x16[sel], signs, 1)
-    check_scales(sh[sel], ref["scales"])
-    check_codes(oracle.unpack_int4(qh[sel]), ref["codes"], frac=1e-2)
+    check_quant(oracle.unpack_int4(qh[sel]), sh[sel], ref["x_rot"], ref["scales"])
 
 
 def test_kv_groups_past_grid_cap():
@@ -76,8 +75,8 @@ def test_kv_groups_past_grid_cap():
     groups = v16.reshape(-1, D)
     sel = sample(groups.shape[0], per_pass, 2)
     ref = oracle.had_quant(groups[sel], signs, 1)
-    check_scales(host(vs).reshape(-1)[sel], ref["scales"])
-    check_codes(oracle.unpack_int4(host(vq).reshape(-1, D // 2)[sel]), ref["codes"], frac=1e-2)
+    check_quant(oracle.unpack_int4(host(vq).reshape(-1, D // 2)[sel]), host(vs).reshape(-1)[sel],
+                ref["x_rot"], ref["scales"])
 
 
 def test_cross_head_rows_past_grid_cap():
@@ -90,5 +89,4 @@ def test_cross_head_rows_past_grid_cap():
     qh, sh = host(q), host(s)
     sel = sample(rows, per_pass, 3)
     ref = oracle.cross_head_quant(z16[sel], nh)
-    check_scales(sh[sel], ref["scales"])
-    check_codes(oracle.unpack_int4(qh[sel]), ref["codes"], frac=1e-2)
+    check_quant(oracle.unpack_int4(qh[sel]), sh[sel], ref["x_rot"], ref["scales"])

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import (check_asym, check_codes, check_rot, check_scales, check_y_elementwise,
+from parity import (check_asym, check_codes, check_quant, check_rot, check_y_elementwise,
                     check_y_frobenius)
 
 torch = pytest.importorskip("torch")
@@ -76,8 +76,7 @@ def test_rotation_equals_dense_hadamard(d, m):
     ref = x16.astype(np.float64) @ dense.T
     check_rot(xr, ref, 1e-6)
     ref_q = oracle.had_quant(x16, signs, m)
-    check_scales(s, ref_q["scales"])
-    check_codes(oracle.unpack_int4(q), ref_q["codes"], frac=1e-2)
+    check_quant(oracle.unpack_int4(q), s, ref_q["x_rot"], ref_q["scales"])
 
 
 # ---------------------------------------------------------------------------
@@ -98,8 +97,7 @@ def test_had_quant_workload(name):
         np.r_[0, x16.shape[0] - 1, np.random.default_rng(7).choice(x16.shape[0], n, replace=False)])
     ref = oracle.had_quant(x16[rows], inp["signs"], cfg.m)
     e = check_rot(xr[rows], ref["x_rot"])
-    ns = check_scales(s[rows], ref["scales"])
-    f = check_codes(oracle.unpack_int4(q[rows]), ref["codes"])
+    ns, f = check_quant(oracle.unpack_int4(q[rows]), s[rows], ref["x_rot"], ref["scales"])
     np.testing.assert_array_equal(oracle.pack_int4(oracle.unpack_int4(q[rows])), q[rows])
     say(f"  rows checked {len(rows)}: rot err {e:.2e}, scale ulps {ns}, code diff frac {f:.2e}")
 
@@ -114,8 +112,7 @@ def test_had_quant_weights_workload():
     rows = np.random.default_rng(11).choice(w16.shape[0], 128, replace=False)
     ref = oracle.prep_weights(w16[rows], inp["signs"], cfg.m)
     check_rot(xr[rows], ref["x_rot"])
-    check_scales(s[rows], ref["scales"])
-    check_codes(oracle.unpack_int4(q[rows]), ref["codes"])
+    check_quant(oracle.unpack_int4(q[rows]), s[rows], ref["x_rot"], ref["scales"])
 
 
 # ---------------------------------------------------------------------------
@@ -275,7 +272,8 @@ def test_gemm_large_tile_extreme_codes():
 # ---------------------------------------------------------------------------
 # Full-size pipelines, sampled: rotate X and W on the GPU, GEMM on the GPU
 # ---------------------------------------------------------------------------
-FULL = {"llama7b_proj": (48, 64), "down_12288": (24, 48), "llama70b_down": (12, 24)}
+FULL = {"tiny": (16, 256), "llama7b_proj": (48, 64), "down_12288": (24, 48),
+        "llama70b_down": (12, 24)}
 
 
 @pytest.mark.parametrize("name", list(FULL))
@@ -295,6 +293,8 @@ def test_full_pipeline_sampled(name):
     rng = np.random.default_rng(5)
     ri = np.unique(np.r_[0, x16.shape[0] - 1, rng.choice(x16.shape[0], nr, replace=False)])
     ci = np.unique(np.r_[0, w16.shape[0] - 1, rng.choice(w16.shape[0], nc, replace=False)])
+    if name == "tiny":  # every row and column
+        ri, ci = np.arange(x16.shape[0]), np.arange(w16.shape[0])
     # the GEMM is exact on whatever codes it was given
     cx = oracle.unpack_int4(qx_h[ri])
     cw = oracle.unpack_int4(qw_h[ci])
@@ -302,10 +302,8 @@ def test_full_pipeline_sampled(name):
     # end to end against the oracle pipeline on the sampled rows and columns
     a = oracle.had_quant(x16[ri], signs, cfg.m)
     b = oracle.prep_weights(w16[ci], signs, cfg.m)
-    check_scales(sx_h[ri], a["scales"])
-    check_scales(sw_h[ci], b["scales"])
-    check_codes(cx, a["codes"])
-    check_codes(cw, b["codes"])
+    check_quant(cx, sx_h[ri], a["x_rot"], a["scales"])
+    check_quant(cw, sw_h[ci], b["x_rot"], b["scales"])
     _, y_ref = oracle.w4a4_reference(a["codes"], a["scales"], b["codes"], b["scales"])
     ys = y_h[np.ix_(ri, ci)]
     e = check_y_frobenius(ys, y_ref)
@@ -319,25 +317,56 @@ def test_full_pipeline_sampled(name):
 # KV cache path
 # ---------------------------------------------------------------------------
 def test_kv_workload():
+    # the full K/V launch, with the optional fp32 copy of every rotated group
     cfg = workloads.KV_CONFIG
     inp = workloads.make_kv_inputs(cfg)
     k16, v16, signs = inp["k"], inp["v"], inp["signs"]
     B, H, S, D = k16.shape
-    say(f"kv {cfg.name}: K/V {k16.shape}")
+    say(f"kv {cfg.name}: K/V {k16.shape} with rotated outputs")
     kq = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device="cuda")
     vq = torch.empty_like(kq)
     ks = torch.empty((B, H, S), dtype=torch.float16, device="cuda")
     vs = torch.empty_like(ks)
-    qr.kv_had_quant(dev(k16), dev(v16), dev(signs), kq, ks, vq, vs, pos0=0)
-    kq_h, vq_h, ks_h, vs_h = host(kq), host(vq), host(ks), host(vs)
+    kr = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
+    vr = torch.empty_like(kr)
+    qr.kv_had_quant(dev(k16), dev(v16), dev(signs), kq, ks, vq, vs, pos0=0, k_rot_out=kr,
+                    v_rot_out=vr)
     rng = np.random.default_rng(3)
-    flat = rng.choice(B * H * S, 4096, replace=False)
-    for t16, q_h, s_h, nm in ((k16, kq_h, ks_h, "K"), (v16, vq_h, vs_h, "V")):
+    flat = np.unique(np.r_[0, B * H * S - 1, rng.choice(B * H * S, 4096, replace=False)])
+    for t16, q_t, s_t, r_t, nm in ((k16, kq, ks, kr, "K"), (v16, vq, vs, vr, "V")):
+        q_h, s_h = host(q_t), host(s_t)
+        r_h = host(r_t).reshape(-1, D)[flat]
         rows = t16.reshape(-1, D)[flat]
         ref = oracle.had_quant(rows, signs, 1)
-        check_scales(s_h.reshape(-1)[flat], ref["scales"])
-        f = check_codes(oracle.unpack_int4(q_h.reshape(-1, D // 2)[flat]), ref["codes"])
-        say(f"  {nm}: 4096 groups sampled, code diff frac {f:.2e}")
+        e = check_rot(r_h, ref["x_rot"])
+        _, f = check_quant(oracle.unpack_int4(q_h.reshape(-1, D // 2)[flat]), s_h.reshape(-1)[flat],
+                           ref["x_rot"], ref["scales"])
+        say(f"  {nm}: {len(flat)} groups sampled, rot err {e:.2e}, code diff frac {f:.2e}")
+    del kr, vr
+
+
+def test_kv_append_single_position():
+    # decode-time append: S = 1 at pos0 = t writes cache position t only
+    rng = np.random.default_rng(23)
+    B, H, D, S_cache = 4, 8, 128, 96
+    for t in (0, 41, S_cache - 1):
+        k1 = rng.standard_normal((B, H, 1, D)).astype(np.float16)
+        v1 = rng.standard_normal((B, H, 1, D)).astype(np.float16)
+        signs = (1 - 2 * rng.integers(0, 2, D)).astype(np.int8)
+        say(f"kv append S=1 at pos0={t}")
+        kq = torch.full((B, H, S_cache, D // 2), 0x3C, dtype=torch.uint8, device="cuda")
+        vq = torch.full_like(kq, 0xC3)
+        ks = torch.full((B, H, S_cache), -1.0, dtype=torch.float16, device="cuda")
+        vs = torch.full_like(ks, -2.0)
+        qr.kv_had_quant(dev(k1), dev(v1), dev(signs), kq, ks, vq, vs, pos0=t)
+        for src, q_t, s_t, fq, fs in ((k1, kq, ks, 0x3C, -1.0), (v1, vq, vs, 0xC3, -2.0)):
+            q_h, s_h = host(q_t), host(s_t)
+            ref = oracle.had_quant(src.reshape(-1, D), signs, 1)
+            check_quant(oracle.unpack_int4(q_h[:, :, t].reshape(-1, D // 2)),
+                        s_h[:, :, t].reshape(-1), ref["x_rot"], ref["scales"])
+            keep = np.ones(S_cache, bool)
+            keep[t] = False
+            assert np.all(q_h[:, :, keep] == fq) and np.all(s_h[:, :, keep] == fs)
 
 
 def test_kv_positions_strides_and_per_head_signs():
@@ -363,8 +392,7 @@ def test_kv_positions_strides_and_per_head_signs():
             ref = oracle.had_quant(rows, signs[h], 1)
             got_q = q_h[:, h, pos0:pos0 + S].reshape(-1, D // 2)
             got_s = s_h[:, h, pos0:pos0 + S].reshape(-1)
-            check_scales(got_s, ref["scales"])
-            check_codes(oracle.unpack_int4(got_q), ref["codes"], frac=1e-2)
+            check_quant(oracle.unpack_int4(got_q), got_s, ref["x_rot"], ref["scales"])
         # cache entries outside [pos0, pos0 + S) untouched
         assert np.all(q_h[:, :, :pos0] == fill_q) and np.all(q_h[:, :, pos0 + S:] == fill_q)
         assert np.all(s_h[:, :, :pos0] == fill_s) and np.all(s_h[:, :, pos0 + S:] == fill_s)
@@ -381,8 +409,8 @@ def test_kv_single_tensor_and_head_dims():
         vs = torch.empty((B, H, S), dtype=torch.float16, device="cuda")
         qr.kv_had_quant(None, dev(v16), dev(signs), None, None, vq, vs)
         ref = oracle.had_quant(v16.reshape(-1, D), signs, 1)
-        check_scales(host(vs).reshape(-1), ref["scales"])
-        check_codes(oracle.unpack_int4(host(vq).reshape(-1, D // 2)), ref["codes"], frac=1e-2)
+        check_quant(oracle.unpack_int4(host(vq).reshape(-1, D // 2)), host(vs).reshape(-1),
+                    ref["x_rot"], ref["scales"])
 
 
 # ---------------------------------------------------------------------------
@@ -403,9 +431,42 @@ def test_had_quant_strided_rows_clip_and_zero_rows():
     ref = oracle.had_quant(buf[:, :d], signs, 1, 0.9)
     qh = host(qbuf)
     assert np.all(qh[:, d // 2:] == 0x5A)
-    check_scales(host(s), ref["scales"])
-    check_codes(oracle.unpack_int4(qh[:, : d // 2]), ref["codes"])
+    check_quant(oracle.unpack_int4(qh[:, : d // 2]), host(s), ref["x_rot"], ref["scales"])
     assert np.all(qh[3, : d // 2] == 0)
+
+
+@pytest.mark.parametrize("d", [256, 4096])
+def test_exact_ties_round_to_even(d):
+    # rows whose rotated values sit exactly on k + 1/2 steps of the scale.
+    # x~ is built first (entries (k + 1/2) S with S = 1/8 exactly, plus the
+    # row maximum 7 S), then x = s * (H x~) / sqrt(d), exactly representable
+    # in fp16; for d = 4^k the kernels' transform of x is then exact too, so
+    # every such element is an exact tie of x~ / S and must round to even.
+    rng = np.random.default_rng(d)
+    rows = 64
+    h = oracle.sylvester(d).astype(np.float64)
+    signs = (1 - 2 * rng.integers(0, 2, d)).astype(np.int8)
+    xt = np.zeros((rows, d))
+    for r in range(rows):
+        pos = rng.choice(d, 15, replace=False)
+        xt[r, pos[0]] = 7 * 0.125 * (1 - 2 * (r & 1))
+        xt[r, pos[1:]] = (rng.integers(-7, 7, 14) + 0.5) * 0.125
+    x = (xt @ h) / np.sqrt(d) * signs[None, :]
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x), "input not exact in fp16"
+    say(f"exact ties d={d}: {rows} rows x 14 ties")
+    q, s, xr = gpu_had_quant(x16, signs, 1)
+    ref = oracle.had_quant(x16, signs, 1)
+    np.testing.assert_allclose(ref["x_rot"], xt, rtol=0, atol=1e-15)
+    assert np.all(ref["scales"] == np.float16(0.125))
+    np.testing.assert_array_equal(xr, xt)          # the kernel's transform is exact
+    np.testing.assert_array_equal(s, ref["scales"])
+    codes = oracle.unpack_int4(q)
+    tie = np.abs(np.abs(xt / 0.125) % 1.0 - 0.5) == 0.0
+    away = int((codes[tie] != ref["codes"][tie]).sum())
+    say(f"  {int(tie.sum())} ties, {away} rounded away from even")
+    check_codes(codes, ref["codes"])
+    assert away == 0
 
 
 def test_had_quant_no_signs_single_row_and_determinism():
@@ -418,8 +479,7 @@ def test_had_quant_no_signs_single_row_and_determinism():
         np.testing.assert_array_equal(q1, q2)
         np.testing.assert_array_equal(s1, s2)
         ref = oracle.had_quant(x16, np.ones(d, np.int8), m)
-        check_scales(s1, ref["scales"])
-        check_codes(oracle.unpack_int4(q1), ref["codes"], frac=1e-2)
+        check_quant(oracle.unpack_int4(q1), s1, ref["x_rot"], ref["scales"])
 
 
 @pytest.mark.parametrize("m", [12, 28])
@@ -446,8 +506,7 @@ def test_had_quant_kron_rows_strided_grid_stride(m, clip):
     qh = host(qbuf)
     assert np.all(qh[:, d // 2:] == 0x5A)
     check_rot(host(xr), ref["x_rot"])
-    check_scales(host(s), ref["scales"])
-    check_codes(oracle.unpack_int4(qh[:, : d // 2]), ref["codes"])
+    check_quant(oracle.unpack_int4(qh[:, : d // 2]), host(s), ref["x_rot"], ref["scales"])
     assert np.all(qh[5, : d // 2] == 0)
 
 
@@ -537,8 +596,7 @@ def test_kv_asym_positions_heads_and_degenerate_groups(D, clip):
             codes, sc, zz = oracle.quantize_rows_asym(x_rot, clip)
             ref = {"scales": sc, "zeros": zz}
             check_asym(oracle.unpack_uint4(q_h[:, h, pos0:pos0 + S].reshape(-1, D // 2)),
-                       s_h[:, h, pos0:pos0 + S], z_h[:, h, pos0:pos0 + S], x_rot, ref, clip,
-                       group_frac=0.05, code_frac=1e-2)
+                       s_h[:, h, pos0:pos0 + S], z_h[:, h, pos0:pos0 + S], x_rot, ref, clip)
         assert np.all(q_h[:, :, :pos0] == 0x5A) and np.all(q_h[:, :, pos0 + S:] == 0x5A)
         assert np.all(s_h[:, :, :pos0] == -3.0) and np.all(z_h[:, :, pos0 + S:] == -5.0)
     # the zero and constant groups: scale from the 1e-5 floor, codes = the zero point
