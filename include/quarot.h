@@ -317,6 +317,35 @@ int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv
                                void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free variant of quarot_kv_decode_attention, for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, results and errors as quarot_kv_decode_attention without the
+ * workspace.  The per-split partials go to a scratch array inside the
+ * library: QUAROT_DECODE_SCRATCH_BYTES per GPU, a file-scope device array
+ * that each GPU the library runs on holds until the process ends.  A call
+ * whose sizes need more (quarot_kv_decode_workspace_bytes() above the limit)
+ * is rejected with QUAROT_ERR_UNSUPPORTED before any launch.  The call makes
+ * no allocation (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks up that device's scratch address.  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's contents
+ * (no call depends on them: every partial read is written first in the same
+ * call), so calls that overlap on one GPU (other streams, other threads)
+ * race: order them on one stream.
+ */
+#define QUAROT_DECODE_SCRATCH_BYTES (8 * 1024 * 1024)
+
+int quarot_kv_decode_attention_noalloc(const void* q, int64_t B, int64_t Hq, int64_t Hkv,
+                                       int64_t D, const int8_t* signs, int64_t signs_stride_h,
+                                       int32_t mode, const uint8_t* k_q, const void* k_scale,
+                                       const void* k_zero, const uint8_t* v_q,
+                                       const void* v_scale, const void* v_zero, int64_t S_cache,
+                                       int64_t max_len, const int32_t* lengths, float sm_scale,
+                                       int32_t cross_head, void* out, float* out_f32,
+                                       void* stream);
+
+/*
  * Host-only: bytes of workspace quarot_kv_decode_attention needs for these
  * sizes (per position split: the running max, softmax sum and unnormalised
  * output of every query head).  Returns a negative status for sizes the

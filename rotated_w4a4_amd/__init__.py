@@ -18,6 +18,8 @@ Calls (same names as the C entry points, without the ``quarot_`` prefix):
 * ``kv_had_quant(k, v, signs, k_cache, k_scale, v_cache, v_scale, pos0)``
 * ``kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len)``
   -> fp16 [B, Hq, 128] (one decode step over the int4 cache)
+* ``kv_decode_attention_noalloc(...)``     -> the same without a workspace (the
+  library's own scratch array; for callers that cannot allocate)
 * ``kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len)``
 * ``hadamard_factor(m)``                  -> the library's Paley H_m (numpy int8)
 
@@ -26,9 +28,9 @@ memory and streams only.
 """
 
 from ._lib import (QuarotError, cross_head_had_quant, had_quant, hadamard_factor,
-                   kv_decode_attention, kv_decode_workspace_bytes, kv_had_quant, lib,
-                   library_path, swiglu_had_quant, w4a4_gemm)
+                   kv_decode_attention, kv_decode_attention_noalloc, kv_decode_workspace_bytes,
+                   kv_had_quant, lib, library_path, swiglu_had_quant, w4a4_gemm)
 
 __all__ = ["QuarotError", "cross_head_had_quant", "had_quant", "hadamard_factor",
-           "kv_decode_attention", "kv_decode_workspace_bytes", "kv_had_quant", "lib",
-           "library_path", "swiglu_had_quant", "w4a4_gemm"]
+           "kv_decode_attention", "kv_decode_attention_noalloc", "kv_decode_workspace_bytes",
+           "kv_had_quant", "lib", "library_path", "swiglu_had_quant", "w4a4_gemm"]

@@ -32,6 +32,10 @@ _SIGNATURES = {
     "quarot_kv_decode_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32,
                                                   _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                                   _f32, _i32, _vp, _vp, _vp, _i64, _vp]),
+    "quarot_kv_decode_attention_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64,
+                                                          _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                          _i64, _i64, _vp, _f32, _i32, _vp, _vp,
+                                                          _vp]),
     "quarot_kv_decode_workspace_bytes": (ctypes.c_int64, [_i64, _i64, _i64, _i64, _i64]),
     "quarot_hadamard_factor": (ctypes.c_int, [_i32, _vp]),
     "quarot_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -323,16 +327,10 @@ def kv_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_len: int) -
     return n
 
 
-def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: int,
-                        lengths=None, mode: int = 0, k_zero=None, v_zero=None,
-                        sm_scale: Optional[float] = None, cross_head: bool = False,
-                        signs_stride_h: int = 0, out=None, out_f32=None, workspace=None,
-                        stream=None):
-    """One decode step: q fp16 [B, Hq, 128] against the int4 caches
-    [B, Hkv, S_cache, 64] (+ fp16 scales [B, Hkv, S_cache], and zero points in
-    mode 1).  Returns fp16 [B, Hq, 128] (``out``); ``out_f32`` optionally
-    receives an fp32 copy.  ``workspace`` (uint8, device) is allocated here
-    when not given."""
+def _decode_prepare(q, signs, k_cache, k_scale, v_cache, v_scale, lengths, mode, k_zero, v_zero,
+                    sm_scale, signs_stride_h, out, out_f32):
+    """Shared argument checks of the two decode calls; returns the sizes and
+    the (possibly allocated) outputs."""
     torch = _torch()
     _need(q, torch.float16, "q", 3)
     if not q.is_contiguous():
@@ -371,6 +369,23 @@ def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: i
         _need(out_f32, torch.float32, "out_f32", 3)
         if not out_f32.is_contiguous() or tuple(out_f32.shape) != (B, Hq, D):
             raise ValueError("out_f32 must be contiguous float32 [B, Hq, D]")
+    return B, Hq, Hkv, D, S_cache, float(sm_scale), out
+
+
+def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: int,
+                        lengths=None, mode: int = 0, k_zero=None, v_zero=None,
+                        sm_scale: Optional[float] = None, cross_head: bool = False,
+                        signs_stride_h: int = 0, out=None, out_f32=None, workspace=None,
+                        stream=None):
+    """One decode step: q fp16 [B, Hq, 128] against the int4 caches
+    [B, Hkv, S_cache, 64] (+ fp16 scales [B, Hkv, S_cache], and zero points in
+    mode 1).  Returns fp16 [B, Hq, 128] (``out``); ``out_f32`` optionally
+    receives an fp32 copy.  ``workspace`` (uint8, device) is allocated here
+    when not given."""
+    torch = _torch()
+    B, Hq, Hkv, D, S_cache, sm_scale, out = _decode_prepare(
+        q, signs, k_cache, k_scale, v_cache, v_scale, lengths, mode, k_zero, v_zero, sm_scale,
+        signs_stride_h, out, out_f32)
     need = kv_decode_workspace_bytes(B, Hq, Hkv, D, max_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -379,7 +394,27 @@ def kv_decode_attention(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: i
         _ptr(q), B, Hq, Hkv, D, _ptr(signs), int(signs_stride_h), int(mode),
         _ptr(k_cache), _ptr(k_scale), _ptr(k_zero) if mode == 1 else None,
         _ptr(v_cache), _ptr(v_scale), _ptr(v_zero) if mode == 1 else None,
-        S_cache, int(max_len), _ptr(lengths), float(sm_scale), int(bool(cross_head)),
+        S_cache, int(max_len), _ptr(lengths), sm_scale, int(bool(cross_head)),
         _ptr(out), _ptr(out_f32), _ptr(workspace), workspace.numel(), _stream(stream))
     _check("quarot_kv_decode_attention", st)
+    return out
+
+
+def kv_decode_attention_noalloc(q, signs, k_cache, k_scale, v_cache, v_scale, max_len: int,
+                                lengths=None, mode: int = 0, k_zero=None, v_zero=None,
+                                sm_scale: Optional[float] = None, cross_head: bool = False,
+                                signs_stride_h: int = 0, out=None, out_f32=None, stream=None):
+    """kv_decode_attention without a workspace: the partials go to the
+    library's own scratch array (QUAROT_DECODE_SCRATCH_BYTES per GPU).  With
+    ``out`` given, nothing is allocated."""
+    B, Hq, Hkv, D, S_cache, sm_scale, out = _decode_prepare(
+        q, signs, k_cache, k_scale, v_cache, v_scale, lengths, mode, k_zero, v_zero, sm_scale,
+        signs_stride_h, out, out_f32)
+    st = lib().quarot_kv_decode_attention_noalloc(
+        _ptr(q), B, Hq, Hkv, D, _ptr(signs), int(signs_stride_h), int(mode),
+        _ptr(k_cache), _ptr(k_scale), _ptr(k_zero) if mode == 1 else None,
+        _ptr(v_cache), _ptr(v_scale), _ptr(v_zero) if mode == 1 else None,
+        S_cache, int(max_len), _ptr(lengths), sm_scale, int(bool(cross_head)),
+        _ptr(out), _ptr(out_f32), _stream(stream))
+    _check("quarot_kv_decode_attention_noalloc", st)
     return out

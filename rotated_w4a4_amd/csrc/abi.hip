@@ -322,15 +322,17 @@ int64_t quarot_kv_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int
   return decode_workspace_bytes(B, Hq, Hkv, max_len);
 }
 
-int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
-                               const int8_t* signs, int64_t signs_stride_h, int32_t mode,
-                               const uint8_t* k_q, const void* k_scale, const void* k_zero,
-                               const uint8_t* v_q, const void* v_scale, const void* v_zero,
-                               int64_t S_cache, int64_t max_len, const int32_t* lengths,
-                               float sm_scale, int32_t cross_head,
-                               void* out, float* out_f32,
-                               void* workspace, int64_t workspace_bytes, void* stream) {
-  clear_error();
+namespace {
+
+// Shared validation and launch of both decode entry points.  noalloc: the
+// partials go to the library's scratch array instead of the workspace.
+int decode_checked(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                   const int8_t* signs, int64_t signs_stride_h, int32_t mode,
+                   const uint8_t* k_q, const void* k_scale, const void* k_zero,
+                   const uint8_t* v_q, const void* v_scale, const void* v_zero,
+                   int64_t S_cache, int64_t max_len, const int32_t* lengths, float sm_scale,
+                   int32_t cross_head, void* out, float* out_f32, void* workspace,
+                   int64_t workspace_bytes, bool noalloc, void* stream) {
   int st = decode_shape_ok(B, Hq, Hkv, D, max_len);
   if (st != QUAROT_OK) return st;
   QR_CHECK_ARG(mode == 0 || mode == 1, QUAROT_ERR_INVALID, "mode must be 0 or 1");
@@ -342,16 +344,24 @@ int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv
                (long long)max_len, (long long)S_cache);
   QR_CHECK_ARG(cross_head == 0 || (is_pow2(Hq) && Hq <= 256), QUAROT_ERR_UNSUPPORTED,
                "cross_head needs Hq a power of two <= 256 (Hq = %lld)", (long long)Hq);
+  const int64_t need = decode_workspace_bytes(B, Hq, Hkv, max_len);
+  QR_CHECK_ARG(!noalloc || need <= QUAROT_DECODE_SCRATCH_BYTES, QUAROT_ERR_UNSUPPORTED,
+               "these sizes need %lld bytes of partials; the allocation-free entry point holds "
+               "%lld (use quarot_kv_decode_attention with a workspace)",
+               (long long)need, (long long)QUAROT_DECODE_SCRATCH_BYTES);
   if (B == 0) return QUAROT_OK;
   QR_CHECK_ARG(q && k_q && k_scale && v_q && v_scale && out, QUAROT_ERR_INVALID,
                "q, k_q, k_scale, v_q, v_scale and out are required");
   QR_CHECK_ARG(mode == 0 || (k_zero && v_zero), QUAROT_ERR_INVALID, "mode 1 needs k_zero and v_zero");
-  const int64_t need = decode_workspace_bytes(B, Hq, Hkv, max_len);
-  QR_CHECK_ARG(workspace && workspace_bytes >= need, QUAROT_ERR_INVALID,
-               "workspace of %lld bytes needed, %lld given", (long long)need,
-               (long long)workspace_bytes);
-  QR_CHECK_ARG(aligned(q, 16) && aligned(k_q, 16) && aligned(v_q, 16) && aligned(workspace, 16),
-               QUAROT_ERR_MISALIGNED, "q, k_q, v_q and workspace must be 16-byte aligned");
+  if (!noalloc) {
+    QR_CHECK_ARG(workspace && workspace_bytes >= need, QUAROT_ERR_INVALID,
+                 "workspace of %lld bytes needed, %lld given", (long long)need,
+                 (long long)workspace_bytes);
+    QR_CHECK_ARG(aligned(workspace, 16), QUAROT_ERR_MISALIGNED,
+                 "workspace must be 16-byte aligned");
+  }
+  QR_CHECK_ARG(aligned(q, 16) && aligned(k_q, 16) && aligned(v_q, 16),
+               QUAROT_ERR_MISALIGNED, "q, k_q and v_q must be 16-byte aligned");
   QR_CHECK_ARG(aligned(k_scale, 2) && aligned(v_scale, 2) && aligned(out, 2) &&
                    (mode == 0 || (aligned(k_zero, 2) && aligned(v_zero, 2))),
                QUAROT_ERR_MISALIGNED, "fp16 buffers must be 2-byte aligned");
@@ -359,6 +369,10 @@ int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv
                "out_f32 must be 4-byte aligned");
   QR_CHECK_ARG(lengths == nullptr || aligned(lengths, 4), QUAROT_ERR_MISALIGNED,
                "lengths must be 4-byte aligned");
+  if (noalloc) {
+    st = decode_scratch(&workspace);
+    if (st != QUAROT_OK) return st;
+  }
   DecodeTensors t{};
   t.q = static_cast<const __half*>(q);
   t.signs = signs;
@@ -375,6 +389,36 @@ int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv
   t.workspace = workspace;
   return launch_kv_decode(t, B, Hq, Hkv, S_cache, max_len, sm_scale, int(mode), cross_head != 0,
                           static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+int quarot_kv_decode_attention(const void* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                               const int8_t* signs, int64_t signs_stride_h, int32_t mode,
+                               const uint8_t* k_q, const void* k_scale, const void* k_zero,
+                               const uint8_t* v_q, const void* v_scale, const void* v_zero,
+                               int64_t S_cache, int64_t max_len, const int32_t* lengths,
+                               float sm_scale, int32_t cross_head,
+                               void* out, float* out_f32,
+                               void* workspace, int64_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_checked(q, B, Hq, Hkv, D, signs, signs_stride_h, mode, k_q, k_scale, k_zero, v_q,
+                        v_scale, v_zero, S_cache, max_len, lengths, sm_scale, cross_head, out,
+                        out_f32, workspace, workspace_bytes, false, stream);
+}
+
+int quarot_kv_decode_attention_noalloc(const void* q, int64_t B, int64_t Hq, int64_t Hkv,
+                                       int64_t D, const int8_t* signs, int64_t signs_stride_h,
+                                       int32_t mode, const uint8_t* k_q, const void* k_scale,
+                                       const void* k_zero, const uint8_t* v_q,
+                                       const void* v_scale, const void* v_zero, int64_t S_cache,
+                                       int64_t max_len, const int32_t* lengths, float sm_scale,
+                                       int32_t cross_head, void* out, float* out_f32,
+                                       void* stream) {
+  clear_error();
+  return decode_checked(q, B, Hq, Hkv, D, signs, signs_stride_h, mode, k_q, k_scale, k_zero, v_q,
+                        v_scale, v_zero, S_cache, max_len, lengths, sm_scale, cross_head, out,
+                        out_f32, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -28,4 +28,9 @@ int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_l
 int launch_kv_decode(const DecodeTensors& t, int64_t B, int64_t Hq, int64_t Hkv, int64_t S_cache,
                      int64_t max_len, float sm_scale, int mode, bool cross, hipStream_t stream);
 
+// Device address of this device's copy of the allocation-free entry point's
+// scratch array (QUAROT_DECODE_SCRATCH_BYTES), fetched on the first call on
+// each device.  Allocates nothing.
+int decode_scratch(void** out);
+
 }  // namespace quarot

@@ -35,6 +35,9 @@
 // flipped to offset binary first) or 1024 + z (zero-point codes); both steps
 // are exact.  The 8 nibbles of a dword come out in the order
 // 0, 4, 1, 5, 2, 6, 3, 7, and the other operand uses the same order.
+#include <atomic>
+#include <mutex>
+
 #include "decode.h"
 #include "wave_rows.h"
 
@@ -615,6 +618,51 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the per-split partials live in
+// a file-scope device array of QUAROT_DECODE_SCRATCH_BYTES (each GPU the
+// library runs on holds its own copy until the process ends).  Host code
+// never passes the array's name to a kernel: its device address is fetched
+// once per device with hipGetSymbolAddress, with that device current, and
+// kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[QUAROT_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+int decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice: %s", hipGetErrorString(e));
+    return QUAROT_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device %d: the allocation-free entry point serves devices 0..%d", dev,
+              kMaxDevices - 1);
+    return QUAROT_ERR_UNSUPPORTED;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) {
+        set_error("hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        return QUAROT_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return QUAROT_OK;
+}
 
 // Workgroups of the split kernel resident at once on MI355X: 256 CUs x 4
 // (the kernel's register use allows four 4-wave groups per CU).

@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
     names = set(re.findall(r"\b(quarot_[a-z0-9_]+)\s*\(", text))
     assert {"quarot_had_quant", "quarot_w4a4_gemm", "quarot_kv_had_quant",
             "quarot_kv_decode_attention", "quarot_kv_decode_workspace_bytes",
-            "quarot_swiglu_had_quant", "quarot_cross_head_had_quant"} <= names
+            "quarot_swiglu_had_quant", "quarot_cross_head_had_quant",
+            "quarot_kv_decode_attention_noalloc"} <= names
     assert "quarot_rmsnorm_had_quant" not in names
     for name in names:
         assert hasattr(lib, name), name
@@ -284,6 +285,36 @@ def _dec(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, status):
     assert _dec(lib, **kw) == status
+
+
+def _dec_na(lib, **kw):
+    a = dict(q=FAKE, B=2, Hq=8, Hkv=2, D=128, signs=None, ssh=0, mode=0, kq=FAKE, ks=FAKE,
+             kz=None, vq=FAKE, vs=FAKE, vz=None, S_cache=512, max_len=300, lengths=None,
+             sm=0.088, cross=0, out=FAKE, o32=None)
+    a.update(kw)
+    return lib.quarot_kv_decode_attention_noalloc(
+        a["q"], a["B"], a["Hq"], a["Hkv"], a["D"], a["signs"], a["ssh"], a["mode"], a["kq"],
+        a["ks"], a["kz"], a["vq"], a["vs"], a["vz"], a["S_cache"], a["max_len"], a["lengths"],
+        a["sm"], a["cross"], a["out"], a["o32"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=256, Hq=64, Hkv=8, S_cache=4096, max_len=4096), UNSUPPORTED),  # past the scratch
+    (dict(D=64), UNSUPPORTED),
+    (dict(mode=3), INVALID),
+    (dict(q=None), INVALID),
+    (dict(max_len=600), INVALID),
+    (dict(q=FAKE + 8), MISALIGNED),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    assert _dec_na(lib, **kw) == status
+    assert lib.quarot_last_error()
+
+
+def test_decode_noalloc_scratch_limit_is_reported(lib):
+    assert _dec_na(lib, B=256, Hq=64, Hkv=8, S_cache=4096, max_len=4096) == UNSUPPORTED
+    assert b"allocation-free" in lib.quarot_last_error()
+    assert _dec_na(lib, B=0) == OK
 
 
 def test_decode_empty_batch_is_noop(lib):
