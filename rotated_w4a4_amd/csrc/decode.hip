@@ -527,8 +527,10 @@ constexpr int kCombineDims = 4;   // head dims per combine block
 // Block (b, kCombineDims-dim chunk): every query head's outputs in the
 // chunk, one per thread.  Each thread merges its head's splits (loads issued
 // kCombineBatch at a time, so a few memory round trips cover all splits).
-// With CROSS the Walsh-Hadamard transform over the head index runs in LDS
-// (Sylvester order, normalised by 1 / sqrt(Hq)).
+// With CROSS the Walsh-Hadamard transform over the head index (Sylvester
+// order, normalised by 1 / sqrt(Hq)) runs on lane shuffles for up to 64
+// query heads and in LDS, a barrier per stage, for 128 and 256 heads (the
+// dynamic LDS is allocated only then).
 template <bool CROSS>
 __global__ __launch_bounds__(1024) void decode_combine_kernel(CombineArgs p) {
   extern __shared__ float zs[];  // [Hq][kCombineDims]
@@ -732,7 +734,8 @@ int launch_kv_decode(const DecodeTensors& t, int64_t B, int64_t Hq, int64_t Hkv,
   CombineArgs c{p.part_o, p.part_ml, p.hkv, p.hq, p.group, p.splits, t.out, t.out_f32};
   const dim3 cgrid{unsigned(B), unsigned(kDecD / kCombineDims)};
   const unsigned cthreads = unsigned(std::min<int64_t>(Hq * kCombineDims, 1024));
-  const size_t lds = cross ? size_t(Hq) * kCombineDims * sizeof(float) : 0;
+  // LDS only for the transform of more than 64 heads (the lane path uses none)
+  const size_t lds = (cross && Hq > 64) ? size_t(Hq) * kCombineDims * sizeof(float) : 0;
   if (cross)
     hipLaunchKernelGGL(decode_combine_kernel<true>, cgrid, dim3(cthreads), lds, stream, c);
   else
