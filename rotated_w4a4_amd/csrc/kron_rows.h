@@ -152,8 +152,16 @@ struct KronCfg {
   static constexpr int TASKS = 64 * UNITS;  // phase-2 tasks per row
   static constexpr int HALVES = (M > 16) ? 2 : 1;
   static constexpr int LDS_BYTES = D * 4 + D / 2;  // fp32 row, then its codes
+  // Register-lean addressing for the gated product (two input streams):
+  // buffer loads over the row (one 32-bit lane offset instead of a 64-bit
+  // address per tile and stream) and phase-2 addresses recomputed per row
+  // from an opaque base.  The plain rows keep global loads and let the
+  // compiler hoist the addresses, which measured faster for m = 28 (m = 12,
+  // sixteen tiles per lane, needs the lean form not to spill).
+  static constexpr bool LEAN = SWIGLU || M == 12;
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
   static_assert(TASKS <= THREADS, "one phase-2 task per thread");
+  static_assert(8 * TILES >= 16 * BW, "phase 2 reuses the phase-1 registers");
 };
 
 // SWIGLU: x is the gate projection and up the up projection; the row is
@@ -236,14 +244,20 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   // sign left on this task's values by the phase-1 DPP stages
   const float sigma = (__builtin_popcount(combo & 7) & 1) ? -1.0f : 1.0f;
 
-  // loads of one row's phase-1 chunks (the up projection's too when gated):
-  // buffer loads over the row, so a lane keeps one 32-bit offset (tile t
-  // adds 32 m bytes) instead of a 64-bit address per tile and stream.
-  // (The lanes past m are masked at use: masking here would make the
-  // prefetch wait for its own data.)
+  // loads of one row's phase-1 chunks (the up projection's too when gated;
+  // LEAN: buffer loads, tile t at lane offset + 32 m bytes).  (The lanes past
+  // m are masked at use: masking here would make the prefetch wait for its
+  // own data.)
   constexpr int TU = SWIGLU ? TILES : 1;
   const int lane_off = 2 * ((AW * wave + n) * M + off16);
   auto load_row = [&](int64_t row, uint4 (&raw)[TILES], uint4 (&raw_u)[TU]) {
+    if constexpr (!C::LEAN) {
+      const __half* src = x + row * ld_x;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+        __builtin_memcpy(&raw[t], src + (AW * wave + 16 * t + n) * M + off16, 16);
+      return;
+    }
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(x + row * ld_x), 0, 2 * C::D,
                                           0x00020000);
@@ -262,12 +276,9 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
     }
   };
 
-  int64_t row = blockIdx.x;
-  uint4 raw[TILES], raw_u[TU];
-  if (row < rows) load_row(row, raw, raw_u);
-  for (; row < rows; row += gridDim.x) {
-    float v[8 * TILES];
-    // ---- phase 1: H_m on the matrix cores --------------------------------
+  // ---- phase 1: H_m on the matrix cores, then the butterflies over a4-a6
+  // (register bits) and a0, a1, a3 (lane bits, DPP) -------------------------
+  auto phase1 = [&](const uint4 (&raw)[TILES], const uint4 (&raw_u)[TU], float (&v)[8 * TILES]) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       uint4 mk;
@@ -334,9 +345,8 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
         v[8 * t + 4 + q] = d1[q];
       }
     }
-    // prefetch the next row
-    const int64_t nrow = row + gridDim.x;
-    if (nrow < rows) load_row(nrow, raw, raw_u);
+  };
+  auto butterflies1 = [&](float (&v)[8 * TILES]) {
     // a4-a6: register bits 3-5 (a7, a tile bit too with sixteen tiles, is
     // left to phase 2)
 #pragma unroll
@@ -354,7 +364,10 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
     dpp_fmac_stage<0, C::HALVES>(v, s_q1);
     dpp_fmac_stage<1, C::HALVES>(v, s_q2);
     dpp_fmac_stage<2, C::HALVES>(v, s_r8);
-    // valid outputs to LDS: b = 16 h + 4 g + (0..3), group a at row kron_row(a)
+  };
+  // valid phase-1 outputs to LDS: b = 16 h + 4 g + (0..3), group a at row
+  // kron_row(a)
+  auto write_row = [&](const float (&v)[8 * TILES]) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const int a = kron_row(AW * wave + 16 * t + n);
@@ -367,17 +380,19 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
                           v[8 * t + 4 * h + 3]);
       }
     }
-    __syncthreads();
-    // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
-    // register r = BW q + i holds b = BW unit + i of group a(q).  Group
-    // a(q) = abase + 4 (q & 1) + 128 (q >> 1); its LDS row kron_row(a(q))
-    // flips bit 2 when bit 4 of abase is set.  The per-thread base is made
-    // opaque per row, so the sixteen addresses are base + constant in the loop
-    // rather than sixteen registers kept across it.
-    constexpr int BW = C::BW;
+  };
+  // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
+  // register r = BW q + i holds b = BW unit + i of group a(q).  Group
+  // a(q) = abase + 4 (q & 1) + 128 (q >> 1); its LDS row kron_row(a(q))
+  // flips bit 2 when bit 4 of abase is set.  The per-thread base is made
+  // opaque per row, so the sixteen addresses are base + constant in the loop
+  // rather than sixteen registers kept across it.  Returns the task's
+  // largest |value| (0 for threads without a task).
+  constexpr int BW = C::BW;
+  auto phase2 = [&](float (&v)[16 * BW]) -> float {
     float amax = 0.0f;
     int tbase = abase * M + BW * unit;
-    asm volatile("" : "+v"(tbase));
+    if (C::LEAN) asm volatile("" : "+v"(tbase));
     const int flip4 = ((abase >> 4) & 1) ? 4 * M : 0;
     if (task_on) {
 #pragma unroll
@@ -407,10 +422,12 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
 #pragma unroll
       for (int r = 0; r < 16 * BW; ++r) amax = fmaxf(amax, fabsf(v[r]));
     }
-    amax = wave_max_dpp(amax);
-    if (lane == 0) red[wave] = amax;
-    __syncthreads();  // phase-2 reads of buf are done; red is complete
-    amax = red[0];
+    return amax;
+  };
+  // the row's scale from the per-wave maxima in red, then its codes to the
+  // LDS code area (and the optional fp32 copy)
+  auto quantize = [&](const float (&v)[16 * BW], int64_t row) -> __half {
+    float amax = red[0];
 #pragma unroll
     for (int w = 1; w < C::NWAVE; ++w) amax = fmaxf(amax, red[w]);
     const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
@@ -419,7 +436,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
     if (task_on) {
       // element offset of register q's run in the row (natural order)
       int ebase = abase * M + BW * unit;
-      asm volatile("" : "+v"(ebase));
+      if (C::LEAN) asm volatile("" : "+v"(ebase));
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int e = ebase + M * (4 * (q & 1) + 128 * (q >> 1));
@@ -449,9 +466,10 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
         }
       }
     }
-    __syncthreads();
-    // the row's codes: D / 2 bytes, 16-byte stores.  The codes have their
-    // own LDS area, so the next row's phase 1 may start while they leave.
+    return s16;
+  };
+  // the row's codes: D / 2 bytes from the LDS code area, 16-byte stores
+  auto store_codes = [&](int64_t row, __half s16) {
     uint8_t* qrow = q_out + row * ld_q;
     constexpr int kChunks = C::D / 32, kIter = (kChunks + C::THREADS - 1) / C::THREADS;
 #pragma unroll
@@ -461,6 +479,35 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
         *reinterpret_cast<uint4*>(qrow + 16 * c) = reinterpret_cast<const uint4*>(buf + C::D)[c];
     }
     if (tid == 0) scale_out[row] = s16;
+  };
+
+  int64_t row = blockIdx.x;
+  uint4 raw[TILES], raw_u[TU];
+  if (row >= rows) return;
+  load_row(row, raw, raw_u);
+  // One row at a time: phase 1, the next row's loads, LDS, phase 2, codes.
+  // (Running phase 1 of the next row inside phase 2 of this one, two rows in
+  // flight per workgroup, measured slower: the kernel is bound by VALU issue,
+  // not by the latency between phases.)
+  for (; row < rows; row += gridDim.x) {
+    float v[8 * TILES];
+    phase1(raw, raw_u, v);
+    const int64_t nrow = row + gridDim.x;
+    if (nrow < rows) load_row(nrow, raw, raw_u);  // prefetch
+    butterflies1(v);
+    write_row(v);
+    __syncthreads();
+    // phase 2 reuses the registers
+    float(&v2)[16 * BW] = *reinterpret_cast<float(*)[16 * BW]>(&v[0]);
+    float amax = phase2(v2);
+    amax = wave_max_dpp(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();  // phase-2 reads of buf are done; red is complete
+    const __half s16 = quantize(v2, row);
+    __syncthreads();
+    // the codes have their own LDS area, so the next row's phase 1 may start
+    // while they leave
+    store_codes(row, s16);
   }
 }
 
