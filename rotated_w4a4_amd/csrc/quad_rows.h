@@ -239,11 +239,16 @@ __device__ __forceinline__ void quad_row_asym(const uint4 (&raw)[D / 32],
   const float amin = clip_ratio * (vmin * kNorm);
   const float amax = clip_ratio * (vmax * kNorm);
   const float range = fmaxf(amax - amin, 1e-5f);
-  const __half s16 = __float2half_rn(range / 15.0f);
+  // range / 15 and x / S as products with reciprocals (v_rcp_f32, about one
+  // ulp): the three fp32 divisions were a fifth of the group's VALU work; a
+  // scale, zero point or code can then differ from the exact division's
+  // where the quotient sits within an ulp or two of a rounding boundary
+  const __half s16 = __float2half_rn(range * (1.0f / 15.0f));
   const float sf = __half2float(s16);
-  const float z = fminf(fmaxf(__builtin_rintf(-amin / sf), -1024.0f), 1024.0f);
+  const float rs = __builtin_amdgcn_rcpf(sf);
+  const float z = fminf(fmaxf(__builtin_rintf(-amin * rs), -1024.0f), 1024.0f);
   if (!active) return;
-  const float kq = (1.0f / sf) * kNorm * sigma;
+  const float kq = rs * kNorm * sigma;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     float t8[8];
