@@ -7,9 +7,8 @@
 // in fp32 from the two fp16 inputs as they arrive (the same page, section
 // 3.4 Stage 1b: the online Hadamard acts on that product).  The matrix cores
 // take fp16 operands, so c is split into hi = fp16(c) and
-// lo = fp16((c - hi) * 2^11); H_m hi and H_m lo are two MFMAs with their own
-// fp32 accumulators, joined as H_m hi + 2^-11 H_m lo, keeping about 22 bits
-// of c.
+// lo = fp16((c - hi) * 2^11); H_m hi and (2^-11 H_m) lo accumulate in fp32
+// (products exact), keeping about 22 bits of c.
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
@@ -65,27 +64,47 @@ __device__ __forceinline__ float silu_f32(float t) {
   return t * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Eight gated products c = SiLU(g) * u from one 16-byte chunk of each input,
+// Eight gated products c = SiLU(g) u from one 16-byte chunk of each input,
 // split for the matrix cores: hi = fp16(c), lo = fp16((c - hi) * 2^11).
-// c is made opaque once formed: otherwise the backend folds fp16(s * u) into
-// a single-rounding mixed-precision multiply for the residual while the
-// operand takes fp16 of the rounded product, and where the two disagree by an
-// fp16 ulp the low part no longer completes hi.
+// The element's random sign is already in u (its fp16 sign bit flipped).
+// c = (g u) / (1 + 2^(-g log2 e)): g u is exact in fp32 (two fp16 factors),
+// so c takes one rounding.  c is made opaque once formed, and the residual
+// c - hi (exact) is taken from the very fp16 pair that feeds the MFMA: the
+// backend would otherwise fold fp16(c) into a single-rounding multiply for
+// the residual while the operand takes fp16 of the rounded product, and
+// where the two disagree by an fp16 ulp the low part no longer completes hi.
 __device__ __forceinline__ void swiglu_split8(const uint4& g, const uint4& u, uint4& hi,
                                               uint4& lo) {
-  float gf[8], uf[8];
-  unpack_half8(g, gf);
-  unpack_half8(u, uf);
-  half8_t h, l;
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  const half8_t gh = __builtin_bit_cast(half8_t, g);
+  const half8_t uh = __builtin_bit_cast(half8_t, u);
+  uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float c = silu_f32(gf[j]) * uf[j];
-    asm volatile("" : "+v"(c));
-    h[j] = static_cast<_Float16>(c);
-    l[j] = static_cast<_Float16>((c - static_cast<float>(h[j])) * 2048.0f);
+  for (int k = 0; k < 4; ++k) {
+    float c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = 2 * k + i;
+      // (each product written as an fma of widened fp16 operands, so it runs
+      // as one mixed-precision fma with no separate conversions)
+      const float e = __builtin_amdgcn_exp2f(
+          __builtin_fmaf(static_cast<float>(gh[j]), -1.4426950408889634f, 0.0f));
+      const float p = __builtin_fmaf(static_cast<float>(gh[j]), static_cast<float>(uh[j]), 0.0f);
+      c[i] = p * __builtin_amdgcn_rcpf(1.0f + e);
+      asm volatile("" : "+v"(c[i]));
+    }
+    const half2_t hp = {static_cast<_Float16>(c[0]), static_cast<_Float16>(c[1])};
+    hw[k] = __builtin_bit_cast(uint32_t, hp);
+    // c - hi, exact, from the packed hi pair itself (one mixed fma per value)
+    float r0, r1;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(hw[k]), "v"(c[0]));
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r1) : "v"(hw[k]), "v"(c[1]));
+    const half2_t lp = {static_cast<_Float16>(r0 * 2048.0f), static_cast<_Float16>(r1 * 2048.0f)};
+    lw[k] = __builtin_bit_cast(uint32_t, lp);
   }
-  hi = __builtin_bit_cast(uint4, h);
-  lo = __builtin_bit_cast(uint4, l);
+  hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 }
 
 // LDS row of group a: a2 is flipped when a4 is set.  Phase 1 writes 16
@@ -135,16 +154,15 @@ struct KronCfg {
   // one 512-thread block of eight waves with eight tiles each.  The gated
   // product prefetches two inputs, which sixteen tiles per lane would not
   // hold: it always runs eight waves of eight tiles.
-  static constexpr bool TWO_BLOCKS = (M == 12) && !SWIGLU;
+  static constexpr bool TWO_BLOCKS = (M == 12);
   static constexpr int NWAVE = TWO_BLOCKS ? 4 : 8;
   static constexpr int THREADS = 64 * NWAVE;
   static constexpr int TILES = 1024 / (16 * NWAVE);
   static constexpr int BLOCKS_PER_CU = TWO_BLOCKS ? 2 : 1;
   // how the lane keeps its phase-1 signs across rows: 0 the fp16 sign-bit
   // masks (four registers per tile), 1 the int8 sign words (two per tile,
-  // expanded per row: sixteen tiles), 2 one bit per element (a byte per
-  // tile, four tiles per register: the gated product, whose second input
-  // stream needs the registers)
+  // expanded per row: sixteen tiles), 2 none (the gated product applies
+  // them to its compact chunks)
   static constexpr int SIGN_STORE = SWIGLU ? 2 : (TILES > 8 ? 1 : 0);
   // b per phase-2 task: 4 (m = 12: 192 tasks, m = 28: 448)
   static constexpr int BW = 4;
@@ -159,6 +177,14 @@ struct KronCfg {
   // compiler hoist the addresses, which measured faster for m = 28 (m = 12,
   // sixteen tiles per lane, needs the lean form not to spill).
   static constexpr bool LEAN = SWIGLU || M == 12;
+  // The gated product is formed on a compact layout: a wave's groups
+  // (1024 / NWAVE of them, contiguous in the row) are J 16-byte chunks per
+  // lane and stream, every element real, where the MFMA operand layout pads
+  // each group of m to 32 slots (m = 12: 24 of 64 slots per lane are real).
+  // The products' hi and lo parts go through the wave's own rows of the LDS
+  // row area and are read back in the operand layout.
+  static constexpr int J = SWIGLU ? (1024 / NWAVE) * M / 512 : 1;
+  static_assert(!SWIGLU || (1024 / NWAVE) * M % 512 == 0, "whole chunks per lane");
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
   static_assert(TASKS <= THREADS, "one phase-2 task per thread");
   static_assert(8 * TILES >= 16 * BW, "phase 2 reuses the phase-1 registers");
@@ -193,26 +219,41 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   const uint32_t keep_hi = cnt > 0 ? 0xFFFFFFFFu : 0u;
   // A operands: H_m rows n (and 16 + n) against the lane's K slots, zero
   // padded: slot j pairs with column 8 g + j, or 8 g + j - 4 for a half chunk.
-  const int shift = cnt == 4 ? 4 : 0;
+  const int shift = (cnt == 4 && !SWIGLU) ? 4 : 0;
   const uint32_t nz_lo = mask_row(hm.nz, n) >> (8 * g), neg_lo = mask_row(hm.neg, n) >> (8 * g);
   const uint32_t nz_hi = mask_row(hm.nz, n + 16) >> (8 * g);
   const uint32_t neg_hi = mask_row(hm.neg, n + 16) >> (8 * g);
-  half8_t h_lo, h_hi;
+  half8_t h_lo, h_hi, hs_lo, hs_hi;  // hs: H_m 2^-11 for the gated product's low parts
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bool in = j >= shift;
     h_lo[j] = in ? had_entry(nz_lo, neg_lo, j - shift) : _Float16(0.0f);
     h_hi[j] = in ? had_entry(nz_hi, neg_hi, j - shift) : _Float16(0.0f);
+    hs_lo[j] = h_lo[j] * _Float16(1.0f / 2048.0f);
+    hs_hi[j] = h_hi[j] * _Float16(1.0f / 2048.0f);
   }
   // signs of this lane's phase-1 elements (the same for every row): group
   // a = (1024 / NWAVE) wave + 16 t + n.  Either the fp16 sign-bit masks
   // or the int8 sign words, expanded per row.
-  constexpr int TILES = C::TILES, AW = 1024 / C::NWAVE;
+  constexpr int TILES = C::TILES, AW = 1024 / C::NWAVE, J = C::J;
   uint4 mask[C::SIGN_STORE == 0 ? TILES : 1];
   uint2 sw[C::SIGN_STORE == 1 ? TILES : 1];
-  uint32_t sbits[C::SIGN_STORE == 2 ? (TILES + 3) / 4 : 1] = {};
+  // gated product: the fp16 sign-bit masks of compact chunk j, XORed into up
+  uint4 cmask[SWIGLU ? J : 1];
+  if constexpr (SWIGLU) {
 #pragma unroll
-  for (int t = 0; t < TILES; ++t) {
+    for (int j = 0; j < J; ++j) {
+      uint32_t w0 = 0, w1 = 0;
+      if (signs) {
+        const int e = AW * wave * M + 512 * j + 8 * lane;
+        __builtin_memcpy(&w0, signs + e, 4);
+        __builtin_memcpy(&w1, signs + e + 4, 4);
+      }
+      cmask[j] = sign_masks8(w0, w1);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < (SWIGLU ? 0 : TILES); ++t) {
     uint32_t w0 = 0, w1 = 0;
     if (signs) {
       const int a = AW * wave + 16 * t + n;
@@ -221,17 +262,8 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
     }
     w0 &= keep_lo;
     w1 &= keep_hi;
-    if constexpr (C::SIGN_STORE == 0) {
-      mask[t] = sign_masks8(w0, w1);
-    } else if constexpr (C::SIGN_STORE == 1) {
-      sw[t] = make_uint2(w0, w1);
-    } else {
-      // bit j of the tile's byte: element j negative (bit 7 of its int8)
-      const uint32_t b = ((w0 >> 7) & 1u) | ((w0 >> 14) & 2u) | ((w0 >> 21) & 4u) |
-                         ((w0 >> 28) & 8u) | (((w1 >> 7) & 1u) << 4) | (((w1 >> 14) & 2u) << 4) |
-                         (((w1 >> 21) & 4u) << 4) | (((w1 >> 28) & 8u) << 4);
-      sbits[t >> 2] |= b << (8 * (t & 3));
-    }
+    if constexpr (C::SIGN_STORE == 0) mask[t] = sign_masks8(w0, w1);
+    else sw[t] = make_uint2(w0, w1);
   }
   const float s_q1 = (lane & 1) ? -1.0f : 1.0f;
   const float s_q2 = (lane & 2) ? -1.0f : 1.0f;
@@ -248,9 +280,24 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   // LEAN: buffer loads, tile t at lane offset + 32 m bytes).  (The lanes past
   // m are masked at use: masking here would make the prefetch wait for its
   // own data.)
-  constexpr int TU = SWIGLU ? TILES : 1;
-  const int lane_off = 2 * ((AW * wave + n) * M + off16);
-  auto load_row = [&](int64_t row, uint4 (&raw)[TILES], uint4 (&raw_u)[TU]) {
+  constexpr int NR = SWIGLU ? J : TILES, TU = SWIGLU ? J : 1;
+  const int lane_off =
+      SWIGLU ? 2 * (AW * wave * M + 8 * lane) : 2 * ((AW * wave + n) * M + off16);
+  // byte step between a lane's loads: compact chunks, or tiles of 16 groups
+  constexpr int LSTEP = SWIGLU ? 1024 : 32 * M;
+  // one compact chunk of both inputs of the gated product
+  auto load_chunk = [&](int64_t row, int j, uint4& r, uint4& ru) {
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(x + row * ld_x), 0, 2 * C::D,
+                                          0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(up + row * ld_up), 0, 2 * C::D,
+                                          0x00020000);
+    r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane_off + LSTEP * j, 0, 0));
+    ru = __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + LSTEP * j, 0, 0));
+  };
+  auto load_row = [&](int64_t row, uint4 (&raw)[NR], uint4 (&raw_u)[TU]) {
     if constexpr (!C::LEAN) {
       const __half* src = x + row * ld_x;
 #pragma unroll
@@ -262,23 +309,47 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
         __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(x + row * ld_x), 0, 2 * C::D,
                                           0x00020000);
 #pragma unroll
-    for (int t = 0; t < TILES; ++t)
+    for (int t = 0; t < NR; ++t)
       raw[t] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane_off + 32 * M * t, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane_off + LSTEP * t, 0, 0));
     if constexpr (SWIGLU) {
       const __amdgpu_buffer_rsrc_t ru =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<__half*>(up + row * ld_up), 0, 2 * C::D,
                                             0x00020000);
 #pragma unroll
-      for (int t = 0; t < TILES; ++t)
+      for (int t = 0; t < J; ++t)
         raw_u[t] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(ru, lane_off + 32 * M * t, 0, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ru, lane_off + LSTEP * t, 0, 0));
     }
   };
 
   // ---- phase 1: H_m on the matrix cores, then the butterflies over a4-a6
   // (register bits) and a0, a1, a3 (lane bits, DPP) -------------------------
-  auto phase1 = [&](const uint4 (&raw)[TILES], const uint4 (&raw_u)[TU], float (&v)[8 * TILES]) {
+  // (gated product: nrow < rows issues the next row's loads chunk by chunk
+  // as soon as each chunk's registers are free, so they overlap the long
+  // product phase instead of following it)
+  auto phase1 = [&](uint4 (&raw)[NR], uint4 (&raw_u)[TU], float (&v)[8 * TILES],
+                    int64_t nrow) {
+    if constexpr (SWIGLU) {
+      // products, signs and the hi / lo split on the compact chunks, staged
+      // in this wave's rows of the LDS row area: hi parts, then lo parts
+      _Float16* shi = reinterpret_cast<_Float16*>(buf + AW * wave * M);
+      _Float16* slo = shi + AW * M;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const uint4 um = make_uint4(raw_u[j].x ^ cmask[j].x, raw_u[j].y ^ cmask[j].y,
+                                    raw_u[j].z ^ cmask[j].z, raw_u[j].w ^ cmask[j].w);
+        uint4 hi, lo;
+        swiglu_split8(raw[j], um, hi, lo);
+        if (nrow < rows) load_chunk(nrow, j, raw[j], raw_u[j]);
+        *reinterpret_cast<uint4*>(shi + 512 * j + 8 * lane) = hi;
+        *reinterpret_cast<uint4*>(slo + 512 * j + 8 * lane) = lo;
+      }
+      // the wave reads back what its own lanes wrote: LDS completes a wave's
+      // accesses in order once they have all been issued and counted
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       uint4 mk;
@@ -290,41 +361,34 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
         asm volatile("" : "+v"(s0), "+v"(s1));
         mk = sign_masks8(s0, s1);
       } else {
-        uint32_t b = sbits[t >> 2];
-        asm volatile("" : "+v"(b));
-        b >>= 8 * (t & 3);
-        // element 2i to bit 15, element 2i + 1 to bit 31 of word i
-        mk.x = ((b & 1u) << 15) | ((b & 2u) << 30);
-        mk.y = ((b & 4u) << 13) | ((b & 8u) << 28);
-        mk.z = ((b & 16u) << 11) | ((b & 32u) << 26);
-        mk.w = ((b & 64u) << 9) | ((b & 128u) << 24);
+        mk = make_uint4(0, 0, 0, 0);  // the gated product's signs are applied on the compact chunks
       }
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       float4_t d0, d1 = zero;
       if constexpr (SWIGLU) {
+        // operand slots j < cnt hold b = 8 g + j of group 16 t + n (read as
+        // two 8-byte halves; slots past cnt are zeroed)
+        const _Float16* shi = reinterpret_cast<const _Float16*>(buf + AW * wave * M);
+        const _Float16* slo = shi + AW * M;
+        const int e = (16 * t + n) * M + (cnt > 0 ? 8 * g : 0);
         uint4 hi, lo;
-        swiglu_split8(raw[t], raw_u[t], hi, lo);
-        hi.x = (hi.x & keep_lo) ^ mk.x;
-        hi.y = (hi.y & keep_lo) ^ mk.y;
-        hi.z = (hi.z & keep_hi) ^ mk.z;
-        hi.w = (hi.w & keep_hi) ^ mk.w;
-        lo.x = (lo.x & keep_lo) ^ mk.x;
-        lo.y = (lo.y & keep_lo) ^ mk.y;
-        lo.z = (lo.z & keep_hi) ^ mk.z;
-        lo.w = (lo.w & keep_hi) ^ mk.w;
+        const uint2 h0 = *reinterpret_cast<const uint2*>(shi + e);
+        const uint2 h1 = *reinterpret_cast<const uint2*>(shi + e + 4);
+        const uint2 q0 = *reinterpret_cast<const uint2*>(slo + e);
+        const uint2 q1 = *reinterpret_cast<const uint2*>(slo + e + 4);
+        const uint32_t k_lo = cnt > 0 ? 0xFFFFFFFFu : 0u;   // slots 0-3
+        const uint32_t k_hi = cnt == 8 ? 0xFFFFFFFFu : 0u;  // slots 4-7
+        hi = make_uint4(h0.x & k_lo, h0.y & k_lo, h1.x & k_hi, h1.y & k_hi);
+        lo = make_uint4(q0.x & k_lo, q0.y & k_lo, q1.x & k_hi, q1.y & k_hi);
+        (void)mk;
         const half8_t bh = __builtin_bit_cast(half8_t, hi);
         const half8_t bl = __builtin_bit_cast(half8_t, lo);
-        // the low parts get their own accumulator: added on top of the high
-        // parts' sum inside one MFMA they kept only part of their bits
+        // H_m hi, then 2^-11 H_m lo accumulated onto it (exact products)
         d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bh, zero, 0, 0, 0);
-        const float4_t l0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bl, zero, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) d0[q] = fmaf(l0[q], 1.0f / 2048.0f, d0[q]);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hs_lo, bl, d0, 0, 0, 0);
         if (C::HALVES == 2) {
           d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bh, zero, 0, 0, 0);
-          const float4_t l1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bl, zero, 0, 0, 0);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) d1[q] = fmaf(l1[q], 1.0f / 2048.0f, d1[q]);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hs_hi, bl, d1, 0, 0, 0);
         }
         // one tile's products at a time: interleaving the tiles' conversions
         // would hold several tiles' temporaries at once and spill
@@ -482,7 +546,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   };
 
   int64_t row = blockIdx.x;
-  uint4 raw[TILES], raw_u[TU];
+  uint4 raw[NR], raw_u[TU];
   if (row >= rows) return;
   load_row(row, raw, raw_u);
   // One row at a time: phase 1, the next row's loads, LDS, phase 2, codes.
@@ -491,9 +555,9 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   // not by the latency between phases.)
   for (; row < rows; row += gridDim.x) {
     float v[8 * TILES];
-    phase1(raw, raw_u, v);
     const int64_t nrow = row + gridDim.x;
-    if (nrow < rows) load_row(nrow, raw, raw_u);  // prefetch
+    phase1(raw, raw_u, v, nrow);
+    if (!SWIGLU && nrow < rows) load_row(nrow, raw, raw_u);  // prefetch
     butterflies1(v);
     write_row(v);
     __syncthreads();
