@@ -33,6 +33,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -142,7 +143,8 @@ def us_stats(t: dict) -> dict:
 
 
 # The source file each timed kernel is compiled from.
-KERNEL_FILES = {"had_quant": "had_quant.hip", "w4a4_gemm": "gemm.hip",
+KERNEL_FILES = {"had_quant": "had_quant.hip", "swiglu_had_quant": "had_quant.hip",
+                "w4a4_gemm": "gemm.hip",
                 "kv_had_quant": "kv.hip", "kv_decode": "decode.hip",
                 "cross_head": "cross_head.hip"}
 
@@ -151,7 +153,6 @@ def source_digest(kernel: str) -> str:
     """sha256 over a kernel's source file and the local headers it includes,
     transitively (the public header holds declarations only)."""
     import hashlib
-    import re
 
     seen, todo = [], [KERNEL_FILES[kernel]]
     while todo:
@@ -414,7 +415,7 @@ def bench_swiglu(args, torch, qr) -> dict:
         "speedup_vs_unfused": round(tu["mean"] / tf["mean"], 3),
         "roofline": {"kernel": "swiglu_had_quant", "bound": "hbm", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name + "_swiglu", "had_quant"),
+                     "traffic": measured_traffic(cfg.name + "_swiglu", "swiglu_had_quant"),
                      "algorithmic_bytes": fused_bytes},
     }
     if not args.no_cpu_baseline:
@@ -741,6 +742,17 @@ def counter_means(path: str, counter: str, min_dispatches: int = 3) -> dict:
 KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant": "kv_had_quant",
                "decode_split": "kv_decode", "decode_combine": "kv_decode",
                "cross_head_quant": "cross_head"}
+# instantiations of the rotate+quant kernels that form the gated product first
+GATED_KERNEL = re.compile(r"had_quant_kron<\d+, (?:true|false), true>|had_quant_lds<true>")
+
+
+def kernel_key(kname: str):
+    """Traffic key of a demangled kernel name, or None for kernels not tracked."""
+    if "kv_had_quant" in kname:
+        return "kv_had_quant"
+    if "had_quant" in kname and GATED_KERNEL.search(kname):
+        return "swiglu_had_quant"
+    return next((v for k, v in KERNEL_KEYS.items() if k in kname), None)
 
 
 def summarize_counters(args) -> dict:
@@ -766,8 +778,7 @@ def summarize_counters(args) -> dict:
         w = counter_means(wpath, "WRITE_SIZE")
         ent = {}
         for kname, fv in f.items():
-            key = next((v for k, v in KERNEL_KEYS.items() if k in kname and
-                        not (k == "had_quant" and "kv_had_quant" in kname)), None)
+            key = kernel_key(kname)
             if key is None or kname not in w:
                 continue
             e = ent.setdefault(key, {"kernel": "", "source_sha256": source_digest(key),
