@@ -191,8 +191,11 @@ def host_cpus() -> int:
         return os.cpu_count() or 1
 
 
-# Token rows of the CPU oracle sample per workload: about 10-30 s of host work.
-CPU_ROWS = {"tiny": 16, "llama7b_proj": 2048, "down_12288": 1024, "llama70b_down": 512}
+# Token rows the CPU oracle times per workload: every token (each whole
+# workload stays under about 10 s of host work on 16 cores).
+CPU_ROWS = {"tiny": 16, "llama7b_proj": 2048, "down_12288": 2048, "llama70b_down": 4096}
+# batch entries of the K/V cache write that the CPU oracle times (all of them)
+KV_CPU_BATCH = 16
 
 
 def cpu_baseline_act(cfg, inp, rows: int) -> dict:
@@ -481,7 +484,7 @@ def bench_kv(args, torch, qr) -> dict:
     nbytes = per_set
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"kv {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
-    return {
+    out = {
         "metric": "KV rotate+quant GB/s (% HBM peak)" + (" [asymmetric, zero point]" if asym else ""),
         "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -500,6 +503,24 @@ def bench_kv(args, torch, qr) -> dict:
                                                  "kv_had_quant"),
                      "algorithmic_bytes": nbytes},
     }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        nb = min(KV_CPU_BATCH, B)
+        log("timing the CPU oracle on a sample")
+        t0 = time.perf_counter()
+        for t in (inp["k"][:nb], inp["v"][:nb]):
+            if asym:
+                oracle.kv_had_quant_asym(t, inp["signs"], 0.95)
+            else:
+                oracle.kv_had_quant(t, inp["signs"])
+        sec = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": per_set * nb / B / sec / 1e9, "unit": "GB/s",
+                               "seconds": sec, "cores": blas_threads(),
+                               "host_cpus": host_cpus(), "kind": "oracle",
+                               "sample": f"K and V of {nb} of the {B} batch entries "
+                                         f"(float64 H_{D} rotation, rint)"}
+    return out
 
 
 def cpu_baseline_cross_head(cfg, z16, rows=None) -> dict:
@@ -572,13 +593,15 @@ def bench_cross_head(args, torch, qr) -> dict:
     return out
 
 
-def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows: int = 4) -> dict:
-    """The oracle, as it stands, on `rows` batch rows of the decode step (its
-    cache built by the oracle's KV quantiser, untimed)."""
+def cpu_baseline_decode(dcfg, inp, q16, mode: int, cross: bool, rows=None) -> dict:
+    """The oracle, as it stands, on `rows` batch rows of the decode step
+    (default: all of them; its cache built by the oracle's KV quantiser,
+    untimed)."""
     import oracle
     from oracle.attention import decode_attention
 
     cfg = dcfg.kv
+    rows = cfg.batch if rows is None else rows
     S = cfg.positions
     quant = oracle.kv_had_quant if mode == 0 else (
         lambda t, s: oracle.kv_had_quant_asym(t, s, 0.95))
