@@ -16,7 +16,8 @@
 //   * had_quant_4096_split  d = 4096, m = 1: two waves per row, one LDS
 //                         exchange (split_rows.h).
 //   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
-//                         on the matrix cores, one LDS exchange
+//                         (plain d = 12288: H_2 (x) H_12 over 512 groups of
+//                         24) on the matrix cores, one LDS exchange
 //                         (kron_rows.h); also the gated product.
 //   * had_quant_lds       any supported d (<= 32768) and m: one workgroup per
 //                         row, the row staged in LDS as fp32; H_m applied per
@@ -208,21 +209,35 @@ int sm_count_cached() {
 }
 
 // Raise the dynamic LDS limit of the Kronecker kernel instantiation once.
-template <int M, bool CLAMP, bool SWIGLU>
+template <int M, bool CLAMP, bool SWIGLU, int NP>
 bool kron_attr_ok() {
   static const bool ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<M, CLAMP, SWIGLU>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kron<M, CLAMP, SWIGLU, NP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                          KronCfg<M, SWIGLU>::LDS_BYTES) == hipSuccess;
+                          KronCfg<M, SWIGLU, NP>::LDS_BYTES) == hipSuccess;
   return ok;
 }
 
-template <int M, bool CLAMP, bool SWIGLU>
+// Masks of H_2 (x) H_m (rows and columns i = i0 m + ib, entry
+// (-1)^(i0 j0) H_m[ib][jb]) from those of H_m: the Sylvester H_{2^n} is
+// H_{2^(n-1)} (x) H_2, so H_{2^n} (x) H_m = H_{2^(n-1)} (x) (H_2 (x) H_m).
+HadMasks kron2_masks(const HadMasks& h, int m) {
+  HadMasks o{};
+  for (int r = 0; r < 2 * m; ++r) {
+    const int rb = r % m;
+    const uint32_t nz = h.nz[rb], neg = h.neg[rb];
+    o.nz[r] = nz | (nz << m);
+    o.neg[r] = neg | ((r >= m ? neg ^ nz : neg) << m);
+  }
+  return o;
+}
+
+template <int M, bool CLAMP, bool SWIGLU, int NP>
 int launch_kron(const RowSource& src, int64_t rows, const HadMasks& hm, const int8_t* signs,
                 float clip_ratio, uint8_t* q_out, int64_t ld_q, __half* scale_out,
                 float* x_rot_out, int cus, hipStream_t stream) {
-  using C = KronCfg<M, SWIGLU>;
-  if (!kron_attr_ok<M, CLAMP, SWIGLU>()) {
+  using C = KronCfg<M, SWIGLU, NP>;
+  if (!kron_attr_ok<M, CLAMP, SWIGLU, NP>()) {
     set_error("could not raise the dynamic LDS limit for d = %d", C::D);
     return QUAROT_ERR_HIP;
   }
@@ -230,22 +245,22 @@ int launch_kron(const RowSource& src, int64_t rows, const HadMasks& hm, const in
   const int64_t cap = int64_t(cus) * C::BLOCKS_PER_CU;
   const int64_t blocks = rows < cap ? rows : cap;
   const float norm = 1.0f / sqrtf(float(C::D));
-  hipLaunchKernelGGL((had_quant_kron<M, CLAMP, SWIGLU>), dim3(unsigned(blocks)),
+  hipLaunchKernelGGL((had_quant_kron<M, CLAMP, SWIGLU, NP>), dim3(unsigned(blocks)),
                      dim3(unsigned(C::THREADS)), C::LDS_BYTES, stream, src.x, src.ld_x, src.up,
                      src.ld_up, rows, signs, hm, clip_ratio, q_out, ld_q, scale_out, x_rot_out,
                      norm);
   return check_launch("had_quant_kron");
 }
 
-template <int M, bool SWIGLU>
+template <int M, bool SWIGLU, int NP = 1024>
 int launch_kron_clip(const RowSource& src, int64_t rows, const HadMasks& hm,
                      const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
                      __half* scale_out, float* x_rot_out, int cus, hipStream_t stream) {
   if (clip_ratio != 1.0f)
-    return launch_kron<M, true, SWIGLU>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
-                                        x_rot_out, cus, stream);
-  return launch_kron<M, false, SWIGLU>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
-                                       x_rot_out, cus, stream);
+    return launch_kron<M, true, SWIGLU, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                            scale_out, x_rot_out, cus, stream);
+  return launch_kron<M, false, SWIGLU, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                           scale_out, x_rot_out, cus, stream);
 }
 
 }  // namespace
@@ -293,10 +308,12 @@ int launch_had_quant(const RowSource& src, int64_t rows, int d, int n, int m,
     return check_launch("had_quant_4096_split");
   }
   if (m == 12 && d == 1024 * 12) {
+    // plain rows: 512 groups of 24 under H_2 (x) H_12
     return gated ? launch_kron_clip<12, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
                                               scale_out, x_rot_out, cus, stream)
-                 : launch_kron_clip<12, false>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
-                                               scale_out, x_rot_out, cus, stream);
+                 : launch_kron_clip<24, false, 512>(src, rows, kron2_masks(hm, 12), signs,
+                                                    clip_ratio, q_out, ld_q, scale_out,
+                                                    x_rot_out, cus, stream);
   }
   if (m == 28 && d == 1024 * 28) {
     return gated ? launch_kron_clip<28, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,

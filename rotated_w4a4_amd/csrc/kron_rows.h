@@ -1,14 +1,17 @@
-// Rotate+quant of rows of d = 1024 * m, m = 12 or 28 (H_1024 (x) H_m):
-// one workgroup owns one row (m = 28: 512 threads, one per CU; m = 12: 256
+// Rotate+quant of rows of d = NP * m (H_NP (x) H_m, NP = 2^n): one
+// workgroup owns one row (d = 28672: 512 threads, one per CU; d = 12288: 256
 // threads, two per CU, so two rows are in flight per CU).  H_m is the
-// caller's matrix, handed in as bit masks.
+// caller's matrix, handed in as bit masks.  The plain d = 12288 row runs as
+// NP = 512 groups of m = 24 under H_2 (x) H_12 (built on the host from the
+// caller's H_12); d = 28672 as 1024 groups of 28.
 //
 // With SWIGLU the row is the gated FFN product c = SiLU(gate) * up, formed
 // in fp32 from the two fp16 inputs as they arrive (the same page, section
 // 3.4 Stage 1b: the online Hadamard acts on that product).  The matrix cores
 // take fp16 operands, so c is split into hi = fp16(c) and
 // lo = fp16((c - hi) * 2^11); H_m hi and (2^-11 H_m) lo accumulate in fp32
-// (products exact), keeping about 22 bits of c.
+// (products exact), keeping about 22 bits of c.  (The gated rows keep
+// NP = 1024 groups of m.)
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
@@ -17,24 +20,24 @@
 // LLaMA2-70B down-projection input, d = 12288 the Qwen3-8B one, which the
 // QuaRot paper-viz explainer builds with a Paley-12 block).
 //
-// Element e = a * m + b, a = 0..1023 (the power-of-two index), b = 0..m-1.
-//   phase 1  wave w (of W = 8 or 4), lane l = n + 16 g, tile t (of 1024 /
-//            (16 W)) hold group a = (1024 / W) w + 16 t + n.  The lane loads
+// Element e = a * m + b, a = 0..NP-1 (the power-of-two index), b = 0..m-1.
+//   phase 1  wave w (of W = 8 or 4), lane l = n + 16 g, tile t (of NP /
+//            (16 W)) hold group a = (NP / W) w + 16 t + n.  The lane loads
 //            elements b = 8 g .. 8 g + 7 of its group (zero past m) with one
 //            16-byte load inside the group: the B operand of
-//            v_mfma_f32_16x16x32_f16.  H_m (rows 0-15 and, for m = 28,
+//            v_mfma_f32_16x16x32_f16.  H_m (rows 0-15 and, for m > 16,
 //            16-31; zero padded to 32 x 32) is the A operand, so the dense
 //            H_m factor runs on the matrix cores on the raw sign-flipped fp16
 //            input (products with +-1 are exact, sums fp32).  The output
 //            lands as b = 4 g + (0..3) and 16 + 4 g + (0..3).  Butterflies
 //            over a4-a6 (tile t) run in registers, over a0, a1, a3 (lane bits
 //            0, 1, 3) through DPP.  Valid outputs go to LDS as fp32.
-//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of four
-//            consecutive b.  The task reads the 16 values of a2, a7, a8, a9
-//            (a float4 each), runs those
-//            four butterfly stages in registers, joins the workgroup maximum,
-//            quantises and writes 16- or 8-bit code units to LDS; the row's
-//            codes then leave in 16-byte stores.
+//   phase 2  task (c, u): c fixes a0, a1, a3, a4, a5, a6, u a run of BW
+//            consecutive b.  The task reads its BW values of each of the
+//            QN = NP / 64 groups that differ in a2 and a7 up (float4 reads),
+//            runs those butterfly stages in registers, joins the workgroup
+//            maximum, quantises and writes 16- or 32-bit code units to LDS;
+//            the row's codes then leave in 16-byte stores.
 #pragma once
 
 #include "wave_rows.h"
@@ -145,60 +148,70 @@ __device__ __forceinline__ void dpp_fmac_stage(float (&v)[N], float c) {
 #undef QR_FMAC_DPP
 }
 
-template <int M, bool SWIGLU = false>
+// A row of d = NP m elements: NP = 2^n groups of m.  The plain d = 12288 row
+// is taken as 512 groups of 24 under H_24 = H_2 (x) H_12 (the Sylvester
+// H_1024 is H_512 (x) H_2, so H_1024 (x) H_12 = H_512 (x) H_24): the
+// matrix cores then apply 24 of their 32 K slots instead of 12.
+template <int M, bool SWIGLU = false, int NP = 1024>
 struct KronCfg {
-  static constexpr int D = 1024 * M;
-  // m = 12: 256-thread blocks (four waves, sixteen phase-1 tiles each), two
-  // blocks per CU, so two rows are in flight per CU with their own barriers
-  // and prefetches; m = 28 rows (112 KiB of fp32 in LDS) take the whole CU:
-  // one 512-thread block of eight waves with eight tiles each.  The gated
-  // product prefetches two inputs, which sixteen tiles per lane would not
-  // hold: it always runs eight waves of eight tiles.
-  static constexpr bool TWO_BLOCKS = (M == 12);
+  static constexpr int D = NP * M;
+  // d = 12288: 256-thread blocks (four waves), two blocks per CU, so two
+  // rows are in flight per CU with their own barriers and prefetches;
+  // d = 28672 rows (112 KiB of fp32 in LDS) take the whole CU: one
+  // 512-thread block of eight waves.
+  static constexpr bool TWO_BLOCKS = (D == 12288);
   static constexpr int NWAVE = TWO_BLOCKS ? 4 : 8;
   static constexpr int THREADS = 64 * NWAVE;
-  static constexpr int TILES = 1024 / (16 * NWAVE);
+  static constexpr int AW = NP / NWAVE;  // groups per wave in phase 1
+  static constexpr int TILES = AW / 16;
   static constexpr int BLOCKS_PER_CU = TWO_BLOCKS ? 2 : 1;
   // how the lane keeps its phase-1 signs across rows: 0 the fp16 sign-bit
   // masks (four registers per tile), 1 the int8 sign words (two per tile,
   // expanded per row: sixteen tiles), 2 none (the gated product applies
   // them to its compact chunks)
   static constexpr int SIGN_STORE = SWIGLU ? 2 : (TILES > 8 ? 1 : 0);
-  // b per phase-2 task: 4 (m = 12: 192 tasks, m = 28: 448)
-  static constexpr int BW = 4;
+  // phase 2: a task owns QN groups (the group bits left after phase 1) and
+  // a run of BW consecutive b of each: 64 values
+  static constexpr int QN = NP / 64;
+  static constexpr int BW = 64 / QN;
   static constexpr int UNITS = M / BW;      // runs of BW consecutive b per group
   static constexpr int TASKS = 64 * UNITS;  // phase-2 tasks per row
   static constexpr int HALVES = (M > 16) ? 2 : 1;
-  static constexpr int LDS_BYTES = D * 4 + D / 2;  // fp32 row, then its codes
-  // Register-lean addressing for the gated product (two input streams):
-  // buffer loads over the row (one 32-bit lane offset instead of a 64-bit
-  // address per tile and stream) and phase-2 addresses recomputed per row
-  // from an opaque base.  The plain rows keep global loads and let the
-  // compiler hoist the addresses, which measured faster for m = 28 (m = 12,
-  // sixteen tiles per lane, needs the lean form not to spill).
-  static constexpr bool LEAN = SWIGLU || M == 12;
-  // The gated product is formed on a compact layout: a wave's groups
-  // (1024 / NWAVE of them, contiguous in the row) are J 16-byte chunks per
-  // lane and stream, every element real, where the MFMA operand layout pads
-  // each group of m to 32 slots (m = 12: 24 of 64 slots per lane are real).
-  // The products' hi and lo parts go through the wave's own rows of the LDS
-  // row area and are read back in the operand layout.
-  static constexpr int J = SWIGLU ? (1024 / NWAVE) * M / 512 : 1;
-  static_assert(!SWIGLU || (1024 / NWAVE) * M % 512 == 0, "whole chunks per lane");
+  // LDS row stride in floats: an odd number of float4 slots, so that both
+  // exchange patterns hit 16 distinct bank slots (m = 24 is padded to 28)
+  static constexpr int RS = ((M / 4) % 2 == 1) ? M : M + 4;
+  static constexpr int CODE_OFF = NP * RS;  // the codes follow the fp32 row
+  static constexpr int LDS_BYTES = CODE_OFF * 4 + D / 2;
+  // Register-lean addressing for the gated product (two input streams) and
+  // for sixteen tiles per lane: buffer loads over the row (one 32-bit lane
+  // offset instead of a 64-bit address per tile and stream) and phase-2
+  // addresses recomputed per row from an opaque base.  Eight tiles of one
+  // stream keep global loads and let the compiler hoist the addresses,
+  // which measured faster for m = 28.
+  static constexpr bool LEAN = SWIGLU || TILES > 8;
+  // The gated product is formed on a compact layout: a wave's groups (AW of
+  // them, contiguous in the row) are J 16-byte chunks per lane and stream,
+  // every element real, where the MFMA operand layout pads each group of m
+  // to 32 slots (m = 12: 24 of 64 slots per lane are real).  The products'
+  // hi and lo parts go through the wave's own rows of the LDS row area and
+  // are read back in the operand layout.
+  static constexpr int J = SWIGLU ? AW * M / 512 : 1;
+  static_assert(!SWIGLU || AW * M % 512 == 0, "whole chunks per lane");
+  static_assert(!SWIGLU || RS == M, "the gated staging uses unpadded rows");
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
+  static_assert(AW == 128 || AW == 256, "phase 2 takes a2 and the bits from a7 up");
   static_assert(TASKS <= THREADS, "one phase-2 task per thread");
-  static_assert(8 * TILES >= 16 * BW, "phase 2 reuses the phase-1 registers");
 };
 
 // SWIGLU: x is the gate projection and up the up projection; the row is
 // SiLU(x) * up.  Otherwise up is unused and the row is x.
-template <int M, bool CLAMP, bool SWIGLU>
-__global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kron(
+template <int M, bool CLAMP, bool SWIGLU, int NP>
+__global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quant_kron(
     const __half* __restrict__ x, int64_t ld_x, const __half* __restrict__ up, int64_t ld_up,
     int64_t rows, const int8_t* __restrict__ signs, HadMasks hm, float clip_ratio,
     uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
     float* __restrict__ x_rot, float norm) {
-  using C = KronCfg<M, SWIGLU>;
+  using C = KronCfg<M, SWIGLU, NP>;
   extern __shared__ float4 kron_lds[];  // the row in fp32 (phase 1 -> phase 2), then its codes
   float* buf = reinterpret_cast<float*>(kron_lds);
   __shared__ float red[C::NWAVE];
@@ -207,13 +220,15 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   const int n = lane & 15, g = lane >> 4;
 
   // valid elements of this lane's chunk of a group: b = 8 g .. 8 g + cnt - 1
-  // (cnt is 8, 4 or 0 for m = 12 and 28)
+  // (cnt is 8, 4 or 0 for m = 12, 24 and 28)
   const int cnt = min(8, max(0, M - 8 * g));
   // Each lane loads 16 bytes (8 elements) of its group in one instruction,
   // always inside the group: a full chunk (cnt = 8) at b = 8 g; a half chunk
   // (cnt = 4, the group's last four elements) at b = 8 g - 4, so the wanted
-  // values sit in the upper half; lanes past m at the group start.  Halves
-  // that are not wanted are zeroed before the MFMA.
+  // values sit in the upper half; lanes past m at the group start.  The
+  // slots that are not wanted meet zero columns of the A operand: they hold
+  // other elements of the same group, so with finite inputs they add exact
+  // zeros (a non-finite input spoils its group's outputs either way).
   const int off16 = cnt == 8 ? 8 * g : (cnt == 4 ? 8 * g - 4 : 0);
   const uint32_t keep_lo = cnt == 8 ? 0xFFFFFFFFu : 0u;
   const uint32_t keep_hi = cnt > 0 ? 0xFFFFFFFFu : 0u;
@@ -235,7 +250,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
   // signs of this lane's phase-1 elements (the same for every row): group
   // a = (1024 / NWAVE) wave + 16 t + n.  Either the fp16 sign-bit masks
   // or the int8 sign words, expanded per row.
-  constexpr int TILES = C::TILES, AW = 1024 / C::NWAVE, J = C::J;
+  constexpr int TILES = C::TILES, AW = C::AW, J = C::J, RS = C::RS;
   uint4 mask[C::SIGN_STORE == 0 ? TILES : 1];
   uint2 sw[C::SIGN_STORE == 1 ? TILES : 1];
   // gated product: the fp16 sign-bit masks of compact chunk j, XORed into up
@@ -394,11 +409,8 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
         // would hold several tiles' temporaries at once and spill
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        uint4 r = raw[t];
-        r.x = (r.x & keep_lo) ^ mk.x;
-        r.y = (r.y & keep_lo) ^ mk.y;
-        r.z = (r.z & keep_hi) ^ mk.z;
-        r.w = (r.w & keep_hi) ^ mk.w;
+        const uint4 r = make_uint4(raw[t].x ^ mk.x, raw[t].y ^ mk.y, raw[t].z ^ mk.z,
+                                   raw[t].w ^ mk.w);
         const half8_t bop = __builtin_bit_cast(half8_t, r);
         d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
         if (C::HALVES == 2) d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bop, zero, 0, 0, 0);
@@ -439,95 +451,92 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
       for (int h = 0; h < C::HALVES; ++h) {
         const int b0 = 16 * h + 4 * g;
         if (b0 < M)
-          *reinterpret_cast<float4*>(buf + a * M + b0) =
+          *reinterpret_cast<float4*>(buf + a * RS + b0) =
               make_float4(v[8 * t + 4 * h], v[8 * t + 4 * h + 1], v[8 * t + 4 * h + 2],
                           v[8 * t + 4 * h + 3]);
       }
     }
   };
-  // ---- phase 2: a2, a7, a8, a9 in registers ------------------------------
-  // register r = BW q + i holds b = BW unit + i of group a(q).  Group
-  // a(q) = abase + 4 (q & 1) + 128 (q >> 1); its LDS row kron_row(a(q))
-  // flips bit 2 when bit 4 of abase is set.  The per-thread base is made
-  // opaque per row, so the sixteen addresses are base + constant in the loop
-  // rather than sixteen registers kept across it.  Returns the task's
-  // largest |value| (0 for threads without a task).
-  constexpr int BW = C::BW;
-  auto phase2 = [&](float (&v)[16 * BW]) -> float {
+  // ---- phase 2: a2 and the group bits from a7 up, in registers ----------
+  // register r = BW q + i holds b = BW unit + i of group a(q), q < QN.
+  // Group a(q) = abase + 4 (q & 1) + 128 (q >> 1); its LDS row
+  // kron_row(a(q)) flips bit 2 when bit 4 of abase is set.  With LEAN the
+  // per-thread base is made opaque per row, so the addresses are base +
+  // constant in the loop rather than registers kept across it.  Returns the
+  // task's largest |value| (0 for threads without a task).
+  constexpr int BW = C::BW, QN = C::QN, NV = QN * BW;
+  auto phase2 = [&](float (&v)[NV]) -> float {
     float amax = 0.0f;
-    int tbase = abase * M + BW * unit;
+    int tbase = abase * RS + BW * unit;
     if (C::LEAN) asm volatile("" : "+v"(tbase));
-    const int flip4 = ((abase >> 4) & 1) ? 4 * M : 0;
+    const int flip4 = ((abase >> 4) & 1) ? 4 * RS : 0;
     if (task_on) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int a_off = ((q & 1) ? 4 * M - flip4 : flip4) + 128 * M * (q >> 1);
-        if (BW == 4) {
-          const float4 f = *reinterpret_cast<const float4*>(buf + tbase + a_off);
-          v[4 * q] = f.x;
-          v[4 * q + 1] = f.y;
-          v[4 * q + 2] = f.z;
-          v[4 * q + 3] = f.w;
-        } else {
-          const float2 f = *reinterpret_cast<const float2*>(buf + tbase + a_off);
-          v[2 * q] = f.x;
-          v[2 * q + 1] = f.y;
+      for (int q = 0; q < QN; ++q) {
+        const int a_off = ((q & 1) ? 4 * RS - flip4 : flip4) + 128 * RS * (q >> 1);
+#pragma unroll
+        for (int k = 0; k < BW; k += 4) {
+          const float4 f = *reinterpret_cast<const float4*>(buf + tbase + a_off + k);
+          v[BW * q + k] = f.x;
+          v[BW * q + k + 1] = f.y;
+          v[BW * q + k + 2] = f.z;
+          v[BW * q + k + 3] = f.w;
         }
       }
 #pragma unroll
-      for (int h = BW; h < 16 * BW; h <<= 1)
+      for (int h = BW; h < NV; h <<= 1)
 #pragma unroll
-        for (int r = 0; r < 16 * BW; ++r)
+        for (int r = 0; r < NV; ++r)
           if ((r & h) == 0) {
             const float a = v[r], b = v[r + h];
             v[r] = a + b;
             v[r + h] = a - b;
           }
 #pragma unroll
-      for (int r = 0; r < 16 * BW; ++r) amax = fmaxf(amax, fabsf(v[r]));
+      for (int r = 0; r < NV; ++r) amax = fmaxf(amax, fabsf(v[r]));
     }
     return amax;
   };
   // the row's scale from the per-wave maxima in red, then its codes to the
-  // LDS code area (and the optional fp32 copy)
-  auto quantize = [&](const float (&v)[16 * BW], int64_t row) -> __half {
+  // LDS code area (BW codes per unit: 16 or 32 bits), and the optional fp32
+  // copy.  The element offset of register q's run in the row (natural
+  // order) is ebase + M (4 (q & 1) + 128 (q >> 1)), a multiple of BW.
+  auto quantize = [&](const float (&v)[NV], int64_t row) -> __half {
     float amax = red[0];
 #pragma unroll
     for (int w = 1; w < C::NWAVE; ++w) amax = fmaxf(amax, red[w]);
     const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
     const float kq = inv_scale(s16) * norm * sigma;
-    const float xnorm = norm * sigma;
     if (task_on) {
-      // element offset of register q's run in the row (natural order)
-      int ebase = abase * M + BW * unit;
-      if (C::LEAN) asm volatile("" : "+v"(ebase));
+      int cbase = abase * (M / BW) + unit;  // code unit of register 0's run
+      if (C::LEAN) asm volatile("" : "+v"(cbase));
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int e = ebase + M * (4 * (q & 1) + 128 * (q >> 1));
-        if (BW == 4) {
-          uint16_t* codes = reinterpret_cast<uint16_t*>(buf + C::D);  // 4 codes per unit
-          const float t0 = magic_code<CLAMP>(v[4 * q], kq), t1 = magic_code<CLAMP>(v[4 * q + 1], kq);
-          const float t2 = magic_code<CLAMP>(v[4 * q + 2], kq), t3 = magic_code<CLAMP>(v[4 * q + 3], kq);
-          const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t2),
-                                                    __builtin_bit_cast(uint32_t, t0), 0x0c0c0400u);
-          const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t3),
-                                                    __builtin_bit_cast(uint32_t, t1), 0x0c0c0400u);
-          codes[e >> 2] = uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
-          if (x_rot) {
-            float4* dst = reinterpret_cast<float4*>(x_rot + row * int64_t(C::D) + e);
-            *dst = make_float4(v[4 * q] * xnorm, v[4 * q + 1] * xnorm, v[4 * q + 2] * xnorm,
-                               v[4 * q + 3] * xnorm);
-          }
+      for (int q = 0; q < QN; ++q) {
+        const int cu = cbase + (M / BW) * (4 * (q & 1) + 128 * (q >> 1));
+        float t[BW];
+#pragma unroll
+        for (int i = 0; i < BW; ++i) t[i] = magic_code<CLAMP>(v[BW * q + i], kq);
+        if constexpr (BW == 8) {
+          reinterpret_cast<uint32_t*>(buf + C::CODE_OFF)[cu] = pack8_magic(t);
         } else {
-          uint8_t* codes = reinterpret_cast<uint8_t*>(buf + C::D);  // 2 codes per unit
-          const uint32_t t0 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * q], kq));
-          const uint32_t t1 = __builtin_bit_cast(uint32_t, magic_code<CLAMP>(v[2 * q + 1], kq));
-          codes[e >> 1] = uint8_t(((t1 << 4) | (t0 & 0xFu)) ^ 0x88u);
-          if (x_rot) {
-            float2* dst = reinterpret_cast<float2*>(x_rot + row * int64_t(C::D) + e);
-            *dst = make_float2(v[2 * q] * xnorm, v[2 * q + 1] * xnorm);
-          }
+          const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t[2]),
+                                                    __builtin_bit_cast(uint32_t, t[0]), 0x0c0c0400u);
+          const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t[3]),
+                                                    __builtin_bit_cast(uint32_t, t[1]), 0x0c0c0400u);
+          reinterpret_cast<uint16_t*>(buf + C::CODE_OFF)[cu] =
+              uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
         }
+      }
+      if (x_rot) {
+        const float xnorm = norm * sigma;
+        float* xr = x_rot + row * int64_t(C::D) + BW * cbase;
+#pragma unroll
+        for (int q = 0; q < QN; ++q)
+#pragma unroll
+          for (int k = 0; k < BW; k += 4)
+            *reinterpret_cast<float4*>(xr + M * (4 * (q & 1) + 128 * (q >> 1)) + k) =
+                make_float4(v[BW * q + k] * xnorm, v[BW * q + k + 1] * xnorm,
+                            v[BW * q + k + 2] * xnorm, v[BW * q + k + 3] * xnorm);
       }
     }
     return s16;
@@ -540,7 +549,8 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
     for (int i = 0; i < kIter; ++i) {
       const int c = tid + C::THREADS * i;
       if (i + 1 < kIter || c < kChunks)
-        *reinterpret_cast<uint4*>(qrow + 16 * c) = reinterpret_cast<const uint4*>(buf + C::D)[c];
+        *reinterpret_cast<uint4*>(qrow + 16 * c) =
+            reinterpret_cast<const uint4*>(buf + C::CODE_OFF)[c];
     }
     if (tid == 0) scale_out[row] = s16;
   };
@@ -562,7 +572,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU>::THREADS), 2) void had_quant_kr
     write_row(v);
     __syncthreads();
     // phase 2 reuses the registers
-    float(&v2)[16 * BW] = *reinterpret_cast<float(*)[16 * BW]>(&v[0]);
+    float(&v2)[NV] = *reinterpret_cast<float(*)[NV]>(&v[0]);
     float amax = phase2(v2);
     amax = wave_max_dpp(amax);
     if (lane == 0) red[wave] = amax;
