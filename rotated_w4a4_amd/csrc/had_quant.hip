@@ -308,12 +308,12 @@ int launch_had_quant(const RowSource& src, int64_t rows, int d, int n, int m,
     return check_launch("had_quant_4096_split");
   }
   if (m == 12 && d == 1024 * 12) {
-    // plain rows: 512 groups of 24 under H_2 (x) H_12
-    return gated ? launch_kron_clip<12, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
-                                              scale_out, x_rot_out, cus, stream)
-                 : launch_kron_clip<24, false, 512>(src, rows, kron2_masks(hm, 12), signs,
-                                                    clip_ratio, q_out, ld_q, scale_out,
-                                                    x_rot_out, cus, stream);
+    // 512 groups of 24 under H_2 (x) H_12
+    const HadMasks h24 = kron2_masks(hm, 12);
+    return gated ? launch_kron_clip<24, true, 512>(src, rows, h24, signs, clip_ratio, q_out,
+                                                   ld_q, scale_out, x_rot_out, cus, stream)
+                 : launch_kron_clip<24, false, 512>(src, rows, h24, signs, clip_ratio, q_out,
+                                                    ld_q, scale_out, x_rot_out, cus, stream);
   }
   if (m == 28 && d == 1024 * 28) {
     return gated ? launch_kron_clip<28, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,

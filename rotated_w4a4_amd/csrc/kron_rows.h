@@ -197,7 +197,6 @@ struct KronCfg {
   // are read back in the operand layout.
   static constexpr int J = SWIGLU ? AW * M / 512 : 1;
   static_assert(!SWIGLU || AW * M % 512 == 0, "whole chunks per lane");
-  static_assert(!SWIGLU || RS == M, "the gated staging uses unpadded rows");
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
   static_assert(AW == 128 || AW == 256, "phase 2 takes a2 and the bits from a7 up");
   static_assert(TASKS <= THREADS, "one phase-2 task per thread");
@@ -348,7 +347,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
     if constexpr (SWIGLU) {
       // products, signs and the hi / lo split on the compact chunks, staged
       // in this wave's rows of the LDS row area: hi parts, then lo parts
-      _Float16* shi = reinterpret_cast<_Float16*>(buf + AW * wave * M);
+      _Float16* shi = reinterpret_cast<_Float16*>(buf + AW * wave * RS);
       _Float16* slo = shi + AW * M;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
@@ -381,20 +380,29 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       float4_t d0, d1 = zero;
       if constexpr (SWIGLU) {
-        // operand slots j < cnt hold b = 8 g + j of group 16 t + n (read as
-        // two 8-byte halves; slots past cnt are zeroed)
-        const _Float16* shi = reinterpret_cast<const _Float16*>(buf + AW * wave * M);
+        // operand slots j < cnt hold b = 8 g + j of group 16 t + n
+        const _Float16* shi = reinterpret_cast<const _Float16*>(buf + AW * wave * RS);
         const _Float16* slo = shi + AW * M;
         const int e = (16 * t + n) * M + (cnt > 0 ? 8 * g : 0);
         uint4 hi, lo;
-        const uint2 h0 = *reinterpret_cast<const uint2*>(shi + e);
-        const uint2 h1 = *reinterpret_cast<const uint2*>(shi + e + 4);
-        const uint2 q0 = *reinterpret_cast<const uint2*>(slo + e);
-        const uint2 q1 = *reinterpret_cast<const uint2*>(slo + e + 4);
-        const uint32_t k_lo = cnt > 0 ? 0xFFFFFFFFu : 0u;   // slots 0-3
-        const uint32_t k_hi = cnt == 8 ? 0xFFFFFFFFu : 0u;  // slots 4-7
-        hi = make_uint4(h0.x & k_lo, h0.y & k_lo, h1.x & k_hi, h1.y & k_hi);
-        lo = make_uint4(q0.x & k_lo, q0.y & k_lo, q1.x & k_hi, q1.y & k_hi);
+        if constexpr (M % 8 == 0) {
+          // whole chunks (16-byte aligned); lanes past m read their group's
+          // first chunk, against zero columns of H
+          hi = *reinterpret_cast<const uint4*>(shi + e);
+          lo = *reinterpret_cast<const uint4*>(slo + e);
+        } else {
+          // two 8-byte halves; slots past cnt are zeroed (a half chunk's
+          // upper slots would reach the next group, or past the wave's
+          // staging rows)
+          const uint2 h0 = *reinterpret_cast<const uint2*>(shi + e);
+          const uint2 h1 = *reinterpret_cast<const uint2*>(shi + e + 4);
+          const uint2 q0 = *reinterpret_cast<const uint2*>(slo + e);
+          const uint2 q1 = *reinterpret_cast<const uint2*>(slo + e + 4);
+          const uint32_t k_lo = cnt > 0 ? 0xFFFFFFFFu : 0u;   // slots 0-3
+          const uint32_t k_hi = cnt == 8 ? 0xFFFFFFFFu : 0u;  // slots 4-7
+          hi = make_uint4(h0.x & k_lo, h0.y & k_lo, h1.x & k_hi, h1.y & k_hi);
+          lo = make_uint4(q0.x & k_lo, q0.y & k_lo, q1.x & k_hi, q1.y & k_hi);
+        }
         (void)mk;
         const half8_t bh = __builtin_bit_cast(half8_t, hi);
         const half8_t bl = __builtin_bit_cast(half8_t, lo);
