@@ -155,21 +155,17 @@ __device__ __forceinline__ void dpp_fmac_stage(float (&v)[N], float c) {
 template <int M, bool SWIGLU = false, int NP = 1024>
 struct KronCfg {
   static constexpr int D = NP * M;
-  // d = 12288: 256-thread blocks (four waves), two blocks per CU, so two
-  // rows are in flight per CU with their own barriers and prefetches;
-  // d = 28672 rows (112 KiB of fp32 in LDS) take the whole CU: one
+  // A wave owns 128 groups in phase 1 (eight tiles of 16 per lane).  NP =
+  // 512 (d = 12288): 256-thread blocks (four waves), two blocks per CU, so
+  // two rows are in flight per CU with their own barriers and prefetches;
+  // NP = 1024 (d = 28672: 112 KiB of fp32 in LDS) takes the whole CU: one
   // 512-thread block of eight waves.
-  static constexpr bool TWO_BLOCKS = (D == 12288);
-  static constexpr int NWAVE = TWO_BLOCKS ? 4 : 8;
-  static constexpr int THREADS = 64 * NWAVE;
-  static constexpr int AW = NP / NWAVE;  // groups per wave in phase 1
+  static constexpr int AW = 128;  // groups per wave in phase 1
   static constexpr int TILES = AW / 16;
+  static constexpr int NWAVE = NP / AW;
+  static constexpr bool TWO_BLOCKS = NWAVE == 4;
+  static constexpr int THREADS = 64 * NWAVE;
   static constexpr int BLOCKS_PER_CU = TWO_BLOCKS ? 2 : 1;
-  // how the lane keeps its phase-1 signs across rows: 0 the fp16 sign-bit
-  // masks (four registers per tile), 1 the int8 sign words (two per tile,
-  // expanded per row: sixteen tiles), 2 none (the gated product applies
-  // them to its compact chunks)
-  static constexpr int SIGN_STORE = SWIGLU ? 2 : (TILES > 8 ? 1 : 0);
   // phase 2: a task owns QN groups (the group bits left after phase 1) and
   // a run of BW consecutive b of each: 64 values
   static constexpr int QN = NP / 64;
@@ -182,13 +178,12 @@ struct KronCfg {
   static constexpr int RS = ((M / 4) % 2 == 1) ? M : M + 4;
   static constexpr int CODE_OFF = NP * RS;  // the codes follow the fp32 row
   static constexpr int LDS_BYTES = CODE_OFF * 4 + D / 2;
-  // Register-lean addressing for the gated product (two input streams) and
-  // for sixteen tiles per lane: buffer loads over the row (one 32-bit lane
-  // offset instead of a 64-bit address per tile and stream) and phase-2
-  // addresses recomputed per row from an opaque base.  Eight tiles of one
-  // stream keep global loads and let the compiler hoist the addresses,
-  // which measured faster for m = 28.
-  static constexpr bool LEAN = SWIGLU || TILES > 8;
+  // Register-lean addressing for the gated product (two input streams):
+  // buffer loads over the row (one 32-bit lane offset instead of a 64-bit
+  // address per tile and stream) and phase-2 addresses recomputed per row
+  // from an opaque base.  The plain rows keep global loads and let the
+  // compiler hoist the addresses, which measured faster for m = 28.
+  static constexpr bool LEAN = SWIGLU;
   // The gated product is formed on a compact layout: a wave's groups (AW of
   // them, contiguous in the row) are J 16-byte chunks per lane and stream,
   // every element real, where the MFMA operand layout pads each group of m
@@ -198,7 +193,7 @@ struct KronCfg {
   static constexpr int J = SWIGLU ? AW * M / 512 : 1;
   static_assert(!SWIGLU || AW * M % 512 == 0, "whole chunks per lane");
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
-  static_assert(AW == 128 || AW == 256, "phase 2 takes a2 and the bits from a7 up");
+  static_assert(NP == 512 || NP == 1024, "four or eight waves per row");
   static_assert(TASKS <= THREADS, "one phase-2 task per thread");
 };
 
@@ -229,8 +224,6 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
   // other elements of the same group, so with finite inputs they add exact
   // zeros (a non-finite input spoils its group's outputs either way).
   const int off16 = cnt == 8 ? 8 * g : (cnt == 4 ? 8 * g - 4 : 0);
-  const uint32_t keep_lo = cnt == 8 ? 0xFFFFFFFFu : 0u;
-  const uint32_t keep_hi = cnt > 0 ? 0xFFFFFFFFu : 0u;
   // A operands: H_m rows n (and 16 + n) against the lane's K slots, zero
   // padded: slot j pairs with column 8 g + j, or 8 g + j - 4 for a half chunk.
   const int shift = (cnt == 4 && !SWIGLU) ? 4 : 0;
@@ -246,12 +239,10 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
     hs_lo[j] = h_lo[j] * _Float16(1.0f / 2048.0f);
     hs_hi[j] = h_hi[j] * _Float16(1.0f / 2048.0f);
   }
-  // signs of this lane's phase-1 elements (the same for every row): group
-  // a = (1024 / NWAVE) wave + 16 t + n.  Either the fp16 sign-bit masks
-  // or the int8 sign words, expanded per row.
+  // signs of this lane's phase-1 elements (the same for every row), as fp16
+  // sign-bit masks: group a = 128 wave + 16 t + n
   constexpr int TILES = C::TILES, AW = C::AW, J = C::J, RS = C::RS;
-  uint4 mask[C::SIGN_STORE == 0 ? TILES : 1];
-  uint2 sw[C::SIGN_STORE == 1 ? TILES : 1];
+  uint4 mask[SWIGLU ? 1 : TILES];
   // gated product: the fp16 sign-bit masks of compact chunk j, XORed into up
   uint4 cmask[SWIGLU ? J : 1];
   if constexpr (SWIGLU) {
@@ -274,10 +265,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
       __builtin_memcpy(&w0, signs + a * M + off16, 4);
       __builtin_memcpy(&w1, signs + a * M + off16 + 4, 4);
     }
-    w0 &= keep_lo;
-    w1 &= keep_hi;
-    if constexpr (C::SIGN_STORE == 0) mask[t] = sign_masks8(w0, w1);
-    else sw[t] = make_uint2(w0, w1);
+    mask[t] = sign_masks8(w0, w1);
   }
   const float s_q1 = (lane & 1) ? -1.0f : 1.0f;
   const float s_q2 = (lane & 2) ? -1.0f : 1.0f;
@@ -366,17 +354,6 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
     }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      uint4 mk;
-      if constexpr (C::SIGN_STORE == 0) {
-        mk = mask[t];
-      } else if constexpr (C::SIGN_STORE == 1) {
-        // (opaque per row, so the expansion is not hoisted out of the row loop)
-        uint32_t s0 = sw[t].x, s1 = sw[t].y;
-        asm volatile("" : "+v"(s0), "+v"(s1));
-        mk = sign_masks8(s0, s1);
-      } else {
-        mk = make_uint4(0, 0, 0, 0);  // the gated product's signs are applied on the compact chunks
-      }
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
       float4_t d0, d1 = zero;
       if constexpr (SWIGLU) {
@@ -403,7 +380,6 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
           hi = make_uint4(h0.x & k_lo, h0.y & k_lo, h1.x & k_hi, h1.y & k_hi);
           lo = make_uint4(q0.x & k_lo, q0.y & k_lo, q1.x & k_hi, q1.y & k_hi);
         }
-        (void)mk;
         const half8_t bh = __builtin_bit_cast(half8_t, hi);
         const half8_t bl = __builtin_bit_cast(half8_t, lo);
         // H_m hi, then 2^-11 H_m lo accumulated onto it (exact products)
@@ -417,8 +393,9 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
         // would hold several tiles' temporaries at once and spill
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        const uint4 r = make_uint4(raw[t].x ^ mk.x, raw[t].y ^ mk.y, raw[t].z ^ mk.z,
-                                   raw[t].w ^ mk.w);
+        // (the gated product's signs are applied on its compact chunks)
+        const uint4 r = make_uint4(raw[t].x ^ mask[t].x, raw[t].y ^ mask[t].y,
+                                   raw[t].z ^ mask[t].z, raw[t].w ^ mask[t].w);
         const half8_t bop = __builtin_bit_cast(half8_t, r);
         d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_lo, bop, zero, 0, 0, 0);
         if (C::HALVES == 2) d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h_hi, bop, zero, 0, 0, 0);
@@ -431,8 +408,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
     }
   };
   auto butterflies1 = [&](float (&v)[8 * TILES]) {
-    // a4-a6: register bits 3-5 (a7, a tile bit too with sixteen tiles, is
-    // left to phase 2)
+    // a4-a6: register bits 3-5
 #pragma unroll
     for (int h = 8; h < 64; h <<= 1)
 #pragma unroll
