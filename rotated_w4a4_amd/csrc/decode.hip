@@ -666,9 +666,13 @@ int decode_scratch(void** out) {
   return QUAROT_OK;
 }
 
-// Workgroups of the split kernel resident at once on MI355X: 256 CUs x 4
-// (the kernel's register use allows four 4-wave groups per CU).
-constexpr int64_t kDecResident = 1024;
+// Split workgroups planned per round on MI355X: 256 CUs x 2.  The kernel's
+// register use would allow four 4-wave groups per CU, but two (two waves per
+// SIMD) already keep the step loop at the VALU's rate, while every further
+// group adds its dispatch, its query rotation and its partials to merge
+// (70B shape: 4 splits of 1024 positions ran 23.1 us against 24.7 us for 8
+// splits of 512).
+constexpr int64_t kDecResident = 512;
 
 void decode_plan(int64_t B, int64_t Hkv, int64_t max_len, int& splits, int& split_len) {
   // Choose the split count that minimises (rounds of resident workgroups) x
