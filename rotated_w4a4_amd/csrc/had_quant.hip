@@ -16,9 +16,9 @@
 //   * had_quant_4096_split  d = 4096, m = 1: two waves per row, one LDS
 //                         exchange (split_rows.h).
 //   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
-//                         (plain d = 12288: H_2 (x) H_12 over 512 groups of
-//                         24) on the matrix cores, one LDS exchange
-//                         (kron_rows.h); also the gated product.
+//                         (d = 12288: H_2 (x) H_12 over 512 groups of 24) on
+//                         the matrix cores, one LDS exchange (kron_rows.h);
+//                         also the gated product.
 //   * had_quant_lds       any supported d (<= 32768) and m: one workgroup per
 //                         row, the row staged in LDS as fp32; H_m applied per
 //                         contiguous group, then radix-32 FWHT passes over

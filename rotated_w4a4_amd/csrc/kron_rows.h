@@ -1,7 +1,7 @@
 // Rotate+quant of rows of d = NP * m (H_NP (x) H_m, NP = 2^n): one
 // workgroup owns one row (d = 28672: 512 threads, one per CU; d = 12288: 256
 // threads, two per CU, so two rows are in flight per CU).  H_m is the
-// caller's matrix, handed in as bit masks.  The plain d = 12288 row runs as
+// caller's matrix, handed in as bit masks.  The d = 12288 row runs as
 // NP = 512 groups of m = 24 under H_2 (x) H_12 (built on the host from the
 // caller's H_12); d = 28672 as 1024 groups of 28.
 //
@@ -10,8 +10,7 @@
 // 3.4 Stage 1b: the online Hadamard acts on that product).  The matrix cores
 // take fp16 operands, so c is split into hi = fp16(c) and
 // lo = fp16((c - hi) * 2^11); H_m hi and (2^-11 H_m) lo accumulate in fp32
-// (products exact), keeping about 22 bits of c.  (The gated rows keep
-// NP = 1024 groups of m.)
+// (products exact), keeping about 22 bits of c.
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
@@ -187,9 +186,9 @@ struct KronCfg {
   // The gated product is formed on a compact layout: a wave's groups (AW of
   // them, contiguous in the row) are J 16-byte chunks per lane and stream,
   // every element real, where the MFMA operand layout pads each group of m
-  // to 32 slots (m = 12: 24 of 64 slots per lane are real).  The products'
-  // hi and lo parts go through the wave's own rows of the LDS row area and
-  // are read back in the operand layout.
+  // to 32 slots (m = 24: 24 of 32, m = 28: 28 of 32).  The products' hi and
+  // lo parts go through the wave's own rows of the LDS row area and are
+  // read back in the operand layout.
   static constexpr int J = SWIGLU ? AW * M / 512 : 1;
   static_assert(!SWIGLU || AW * M % 512 == 0, "whole chunks per lane");
   static_assert(M % 4 == 0 && M <= 32 && M % BW == 0, "m must be a multiple of 4 up to 32");
@@ -214,7 +213,7 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
   const int n = lane & 15, g = lane >> 4;
 
   // valid elements of this lane's chunk of a group: b = 8 g .. 8 g + cnt - 1
-  // (cnt is 8, 4 or 0 for m = 12, 24 and 28)
+  // (cnt is 8 or 0 for m = 24; 8 or 4 for m = 28)
   const int cnt = min(8, max(0, M - 8 * g));
   // Each lane loads 16 bytes (8 elements) of its group in one instruction,
   // always inside the group: a full chunk (cnt = 8) at b = 8 g; a half chunk
