@@ -543,9 +543,17 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
   if (row >= rows) return;
   load_row(row, raw, raw_u);
   // One row at a time: phase 1, the next row's loads, LDS, phase 2, codes.
+  // Two barriers per row.  A row's codes leave after the next row's first
+  // barrier (or after the loop): every thread has written them by then, and
+  // every thread has read them before it reaches the next row's second
+  // barrier, after which that row's codes overwrite the area.  red is safe
+  // the same way: it is read between a row's second barrier and the next
+  // row's first, written between those two.
   // (Running phase 1 of the next row inside phase 2 of this one, two rows in
   // flight per workgroup, measured slower: the kernel is bound by VALU issue,
   // not by the latency between phases.)
+  int64_t prev = -1;  // the row whose codes wait in the LDS code area
+  __half prev_s16 = __half(0.0f);
   for (; row < rows; row += gridDim.x) {
     float v[8 * TILES];
     const int64_t nrow = row + gridDim.x;
@@ -554,18 +562,18 @@ __global__ __launch_bounds__((KronCfg<M, SWIGLU, NP>::THREADS), 2) void had_quan
     butterflies1(v);
     write_row(v);
     __syncthreads();
+    if (prev >= 0) store_codes(prev, prev_s16);
     // phase 2 reuses the registers
     float(&v2)[NV] = *reinterpret_cast<float(*)[NV]>(&v[0]);
     float amax = phase2(v2);
     amax = wave_max_dpp(amax);
     if (lane == 0) red[wave] = amax;
     __syncthreads();  // phase-2 reads of buf are done; red is complete
-    const __half s16 = quantize(v2, row);
-    __syncthreads();
-    // the codes have their own LDS area, so the next row's phase 1 may start
-    // while they leave
-    store_codes(row, s16);
+    prev_s16 = quantize(v2, row);
+    prev = row;
   }
+  __syncthreads();
+  store_codes(prev, prev_s16);
 }
 
 }  // namespace quarot
