@@ -398,6 +398,47 @@ def test_kv_positions_strides_and_per_head_signs():
         assert np.all(s_h[:, :, :pos0] == fill_s) and np.all(s_h[:, :, pos0 + S:] == fill_s)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_kv_block_aligned_strides_positions_and_per_head_signs(mode):
+    # S a multiple of 128: each block's groups share (b, h), taken once per
+    # block; strided [B, S, H, D] sources, a cache offset and per-head signs
+    rng = np.random.default_rng(31 + mode)
+    B, H, S, D, S_cache, pos0 = 2, 3, 256, 128, 300, 29
+    k_bshd = rng.standard_normal((B, S, H, D)).astype(np.float16)
+    v_bshd = (rng.standard_normal((B, S, H, D)) + 0.5).astype(np.float16)
+    signs = (1 - 2 * rng.integers(0, 2, (H, D))).astype(np.int8)
+    say(f"kv block-aligned S={S} mode={mode}")
+    k_t = dev(k_bshd).permute(0, 2, 1, 3)
+    v_t = dev(v_bshd).permute(0, 2, 1, 3)
+    if mode == 1:
+        out = gpu_kv_asym(k_bshd.transpose(0, 2, 1, 3), v_bshd.transpose(0, 2, 1, 3), signs,
+                          0.95, S_cache=S_cache, pos0=pos0, signs_stride_h=D, k_t=k_t, v_t=v_t)
+    else:
+        kq = torch.full((B, H, S_cache, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+        vq = torch.full_like(kq, 0x5A)
+        ks = torch.full((B, H, S_cache), -3.0, dtype=torch.float16, device="cuda")
+        vs = torch.full_like(ks, -3.0)
+        qr.kv_had_quant(k_t, v_t, dev(signs), kq, ks, vq, vs, pos0=pos0, signs_stride_h=D)
+        out = {"k": (host(kq), host(ks), None), "v": (host(vq), host(vs), None)}
+    for src, nm in ((k_bshd, "k"), (v_bshd, "v")):
+        q_h, s_h, z_h = out[nm]
+        for h in range(H):
+            rows = src[:, :, h, :].reshape(-1, D)
+            got_q = q_h[:, h, pos0:pos0 + S].reshape(-1, D // 2)
+            if mode == 1:
+                x_rot = oracle.rotate_rows(rows, signs[h], 1)
+                _, sc, zz = oracle.quantize_rows_asym(x_rot, 0.95)
+                check_asym(oracle.unpack_uint4(got_q), s_h[:, h, pos0:pos0 + S],
+                           z_h[:, h, pos0:pos0 + S], x_rot, {"scales": sc, "zeros": zz}, 0.95)
+            else:
+                ref = oracle.had_quant(rows, signs[h], 1)
+                check_quant(oracle.unpack_int4(got_q), s_h[:, h, pos0:pos0 + S].reshape(-1),
+                            ref["x_rot"], ref["scales"])
+        # cache entries outside [pos0, pos0 + S) untouched
+        assert np.all(q_h[:, :, :pos0] == 0x5A) and np.all(q_h[:, :, pos0 + S:] == 0x5A)
+        assert np.all(s_h[:, :, :pos0] == -3.0) and np.all(s_h[:, :, pos0 + S:] == -3.0)
+
+
 def test_kv_single_tensor_and_head_dims():
     rng = np.random.default_rng(4)
     for D in (32, 64, 128, 256):
