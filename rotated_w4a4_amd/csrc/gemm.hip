@@ -42,18 +42,24 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int GROUP_M = 8;
 
 // LDS holds one K tile per buffer, row-major with BKB-byte rows (no
-// padding).  The LDS has 64 four-byte banks and serves a 128-bit read for 16
-// lanes per cycle, so the 16 rows a fragment read touches (same logical
-// 16-byte chunk) must land in 16 different 16-byte slots of a 256-byte bank
-// period.  Chunk c of row r is stored at chunk slot c ^ swz(r); with 64-byte
-// rows (4 chunks) swz(r) = ((r >> 1) ^ (r >> 3)) & 3, with 128-byte rows
-// (8 chunks) swz(r) = (r >> 1) & 7.  The cooperative stores write whole rows
-// and stay conflict-free.
+// padding).  The LDS has 64 four-byte banks, a 256-byte period.  Chunk c of
+// row r is stored at chunk slot c ^ swz(r), where swz(r) is the index of the
+// row's 256-byte period, taken modulo the chunks per row: (r >> 2) & 3 for
+// 64-byte rows (4 chunks), (r >> 1) & 7 for 128-byte rows (8 chunks).  A
+// fragment read (32 consecutive rows, one logical chunk per 32 lanes) then
+// counts no bank-conflict cycles with either row length (SQ_LDS_BANK_CONFLICT
+// on a read-only probe of each pattern; the 64-byte swizzle
+// ((r >> 1) ^ (r >> 3)) & 3 counted 1.33 cycles per read).  The cooperative
+// stores write whole rows and stay conflict-free.
+template <int CPR>
+__device__ __forceinline__ int lds_swz(int r) {
+  static_assert(CPR == 4 || CPR == 8, "64- or 128-byte rows");
+  return CPR == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+
 template <int BKB>
 __device__ __forceinline__ int lds_off(int r, int c) {
-  constexpr int CPR = BKB / 16;
-  const int sw = (CPR == 4) ? (((r >> 1) ^ (r >> 3)) & 3) : ((r >> 1) & (CPR - 1));
-  return r * BKB + ((c ^ sw) << 4);
+  return r * BKB + ((c ^ lds_swz<BKB / 16>(r)) << 4);
 }
 
 __device__ __forceinline__ void widen(const uint4& p, v4i& lo, v4i& hi) {
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   for (int i = 0; i < CH; ++i) {
     const int rb = NW * i + wave;
     const int r = 8 * rb + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int c = (lane & 7) ^ lds_swz<8>(r);
     src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * c
                       : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb + 16 * c;
   }
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_big_kernel(
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int r = 16 * (NW * i + wave) + (lane >> 2);
-    const int ch = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    const int ch = (lane & 3) ^ lds_swz<4>(r);
     src[i] = (r < BM) ? a_q + int64_t(min(m0 + r, M - 1)) * lda + 16 * ch
                       : b_q + int64_t(min(n0 + r - BM, N - 1)) * ldb + 16 * ch;
   }
