@@ -32,12 +32,28 @@ namespace quarot {
 
 constexpr int kSplitBlock = 128;  // two waves, one row
 
-// Float4 slot of chunk c (= element / 4) in the row's LDS copy: bits 0-2
-// are XORed with bits 4-6.  Over GF(2) the low four slot bits are then a
-// bijection of chunk bits 3-6 (the phase-1 writes: chunks 8 n + const for
-// the 16 lanes of a cycle) and of chunk bits 1-4 (the phase-2 reads: chunks
-// 2 j + const), so both patterns hit 16 distinct 16-byte bank slots.
-__device__ __forceinline__ int split_slot(int c) { return c ^ ((c >> 4) & 7); }
+// Float4 slot of chunk c (= element / 4) in the row's LDS copy: c with bits
+// 0-2 XORed with parities of higher bits (bit 0 with c5 ^ c6, bit 1 with
+// c3 ^ c4 ^ c7, bit 2 with c3 ^ c6 ^ c8), a bijection since the higher bits
+// stay.  Neither the phase-1 writes (chunks 128 (4 w + t) + 8 n + 4 h + g)
+// nor the phase-2 reads (chunks 2 (lane & 15) + 64 (lane >> 4) + const)
+// count bank-conflict cycles with it: a read/write probe of both patterns
+// (SQ_LDS_BANK_CONFLICT) found it among random swizzles of this form.  The
+// earlier c ^ ((c >> 4) & 7), chosen on a model of 16 lanes per 128-bit LDS
+// cycle, left the writes heavily conflicted.
+__device__ __forceinline__ constexpr int split_slot(int c) {
+  return c ^ ((((c >> 5) ^ (c >> 6)) & 1) | ((((c >> 3) ^ (c >> 4) ^ (c >> 7)) & 1) << 1) |
+              ((((c >> 3) ^ (c >> 6) ^ (c >> 8)) & 1) << 2));
+}
+// An access's chunk is c = a + b with a lane part a (computed once) and a
+// part b fixed at compile time (the unrolled register index), their bits
+// disjoint.  The XOR term is linear over GF(2) in bits 3-8 and lands in bits
+// 0-2, so split_slot(a + b) = (split_slot(a) ^ (split_slot(b) & 7)) +
+// (b & ~7): one XOR with a constant per access, and the add folds into the
+// LDS instruction's offset.
+__device__ __forceinline__ int split_slot_at(int slot_a, int b) {
+  return (slot_a ^ (split_slot(b) & 7)) + (b & ~7);
+}
 
 // One DPP butterfly stage over lane bit 0, 1 or 3 (STAGE 0, 1, 2) on 32
 // registers, as v + partner * c in one v_fmac_f32 with DPP (c = +1 on the
@@ -83,6 +99,10 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
   // the DPP stages left the sign (-1)^(e5 + e6 + e8) on every value of the lane
   const int e2 = 8 * (lane & 15) + 256 * (lane >> 4) + 1024 * wave;
   const float sigma = ((((lane >> 2) ^ (lane >> 3) ^ (lane >> 4)) & 1) != 0) ? -1.0f : 1.0f;
+  // LDS slots of the lane parts of the phase-1 chunks (512 w + 8 n + g) and
+  // of the phase-2 chunks (e2 / 4); the register index adds the fixed part
+  const int slot_w = split_slot(512 * wave + 8 * n + g);
+  const int slot_r = split_slot(e2 >> 2);
 
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const __half* src = x + row * ld_x + e_in;
@@ -144,8 +164,8 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = 128 * (4 * wave + t) + 8 * n + 4 * h + g;
-        lds[split_slot(c)] = make_float4(v[8 * t + 4 * h], v[8 * t + 4 * h + 1],
+        // chunk 128 (4 w + t) + 8 n + 4 h + g
+        lds[split_slot_at(slot_w, 128 * t + 4 * h)] = make_float4(v[8 * t + 4 * h], v[8 * t + 4 * h + 1],
                                          v[8 * t + 4 * h + 2], v[8 * t + 4 * h + 3]);
       }
     __syncthreads();
@@ -154,8 +174,8 @@ __global__ __launch_bounds__(kSplitBlock, 4) void had_quant_4096_split(
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int u = k >> 1;
-      const int e = e2 + 128 * (u & 1) + 2048 * (u >> 1) + 4 * (k & 1);
-      const float4 f = lds[split_slot(e >> 2)];
+      // element e2 + 128 (u & 1) + 2048 (u >> 1) + 4 (k & 1)
+      const float4 f = lds[split_slot_at(slot_r, 32 * (u & 1) + 512 * (u >> 1) + (k & 1))];
       v[4 * k] = f.x;
       v[4 * k + 1] = f.y;
       v[4 * k + 2] = f.z;
