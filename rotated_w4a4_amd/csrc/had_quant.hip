@@ -15,10 +15,13 @@
 //                         (quad_rows.h).
 //   * had_quant_4096_split  d = 4096, m = 1: two waves per row, one LDS
 //                         exchange (split_rows.h).
-//   * had_quant_kron<M>   d = 1024 m, m = 12 or 28: a workgroup per row, H_m
-//                         (d = 12288: H_2 (x) H_12 over 512 groups of 24) on
-//                         the matrix cores, one LDS exchange (kron_rows.h);
-//                         also the gated product.
+//   * had_quant_kront<M>  d = 12288, plain rows: a workgroup per row, H_2 (x)
+//                         H_12 over 512 groups of 24 on the matrix cores,
+//                         every butterfly in registers, one b-major LDS
+//                         exchange (kront_rows.h).
+//   * had_quant_kron<M>   d = 1024 m, m = 12 or 28, for d = 28672 and the
+//                         gated product: DPP butterflies over lane bits, one
+//                         LDS exchange (kron_rows.h).
 //   * had_quant_lds       any supported d (<= 32768) and m: one workgroup per
 //                         row, the row staged in LDS as fp32; H_m applied per
 //                         contiguous group, then radix-32 FWHT passes over
@@ -26,6 +29,7 @@
 #include "quad_rows.h"
 #include "wave_rows.h"
 #include "kron_rows.h"
+#include "kront_rows.h"
 #include "split_rows.h"
 
 namespace quarot {
@@ -218,6 +222,16 @@ bool kron_attr_ok() {
   return ok;
 }
 
+// The same for the register-butterfly kernel of plain rows.
+template <int M, bool CLAMP, int NP>
+bool kront_attr_ok() {
+  static const bool ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kront<M, CLAMP, NP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          KronTCfg<M, NP>::LDS_BYTES) == hipSuccess;
+  return ok;
+}
+
 // Masks of H_2 (x) H_m (rows and columns i = i0 m + ib, entry
 // (-1)^(i0 j0) H_m[ib][jb]) from those of H_m: the Sylvester H_{2^n} is
 // H_{2^(n-1)} (x) H_2, so H_{2^n} (x) H_m = H_{2^(n-1)} (x) (H_2 (x) H_m).
@@ -252,6 +266,25 @@ int launch_kron(const RowSource& src, int64_t rows, const HadMasks& hm, const in
   return check_launch("had_quant_kron");
 }
 
+template <int M, bool CLAMP, int NP>
+int launch_kront(const RowSource& src, int64_t rows, const HadMasks& hm, const int8_t* signs,
+                 float clip_ratio, uint8_t* q_out, int64_t ld_q, __half* scale_out,
+                 float* x_rot_out, int cus, hipStream_t stream) {
+  using C = KronTCfg<M, NP>;
+  if (!kront_attr_ok<M, CLAMP, NP>()) {
+    set_error("could not raise the dynamic LDS limit for d = %d", C::D);
+    return QUAROT_ERR_HIP;
+  }
+  // two waves per SIMD (up to 256 VGPRs): one or two blocks per CU
+  const int64_t cap = int64_t(cus) * C::BLOCKS_PER_CU;
+  const int64_t blocks = rows < cap ? rows : cap;
+  const float norm = 1.0f / sqrtf(float(C::D));
+  hipLaunchKernelGGL((had_quant_kront<M, CLAMP, NP>), dim3(unsigned(blocks)),
+                     dim3(unsigned(C::THREADS)), C::LDS_BYTES, stream, src.x, src.ld_x, rows,
+                     signs, hm, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm);
+  return check_launch("had_quant_kront");
+}
+
 template <int M, bool SWIGLU, int NP = 1024>
 int launch_kron_clip(const RowSource& src, int64_t rows, const HadMasks& hm,
                      const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
@@ -261,6 +294,24 @@ int launch_kron_clip(const RowSource& src, int64_t rows, const HadMasks& hm,
                                             scale_out, x_rot_out, cus, stream);
   return launch_kron<M, false, SWIGLU, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
                                            scale_out, x_rot_out, cus, stream);
+}
+
+// Plain rows of 512 groups: the register-butterfly kernel; the gated product
+// and the 1024-group rows: had_quant_kron.
+template <int M, bool SWIGLU, int NP = 1024>
+int launch_kron_any(const RowSource& src, int64_t rows, const HadMasks& hm,
+                    const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
+                    __half* scale_out, float* x_rot_out, int cus, hipStream_t stream) {
+  if constexpr (SWIGLU || NP != 512) {
+    return launch_kron_clip<M, SWIGLU, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                           scale_out, x_rot_out, cus, stream);
+  } else {
+    if (clip_ratio != 1.0f)
+      return launch_kront<M, true, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
+                                       x_rot_out, cus, stream);
+    return launch_kront<M, false, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
+                                      x_rot_out, cus, stream);
+  }
 }
 
 }  // namespace
@@ -310,16 +361,16 @@ int launch_had_quant(const RowSource& src, int64_t rows, int d, int n, int m,
   if (m == 12 && d == 1024 * 12) {
     // 512 groups of 24 under H_2 (x) H_12
     const HadMasks h24 = kron2_masks(hm, 12);
-    return gated ? launch_kron_clip<24, true, 512>(src, rows, h24, signs, clip_ratio, q_out,
-                                                   ld_q, scale_out, x_rot_out, cus, stream)
-                 : launch_kron_clip<24, false, 512>(src, rows, h24, signs, clip_ratio, q_out,
-                                                    ld_q, scale_out, x_rot_out, cus, stream);
+    return gated ? launch_kron_any<24, true, 512>(src, rows, h24, signs, clip_ratio, q_out,
+                                                  ld_q, scale_out, x_rot_out, cus, stream)
+                 : launch_kron_any<24, false, 512>(src, rows, h24, signs, clip_ratio, q_out,
+                                                   ld_q, scale_out, x_rot_out, cus, stream);
   }
   if (m == 28 && d == 1024 * 28) {
-    return gated ? launch_kron_clip<28, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
-                                              scale_out, x_rot_out, cus, stream)
-                 : launch_kron_clip<28, false>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
-                                               scale_out, x_rot_out, cus, stream);
+    return gated ? launch_kron_any<28, true>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                             scale_out, x_rot_out, cus, stream)
+                 : launch_kron_any<28, false>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                              scale_out, x_rot_out, cus, stream);
   }
   const size_t lds = size_t(d + d / 32) * sizeof(float);
   // the generic kernel stages up to 32768 + 1024 floats (132 KiB) in LDS

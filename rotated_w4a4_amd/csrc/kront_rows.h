@@ -1,0 +1,300 @@
+// Rotate+quant of plain rows of d = 512 m (H_512 (x) H_m; d = 12288 runs as
+// 512 groups of 24 under H_2 (x) H_12) with every butterfly stage in
+// registers.  One 256-thread workgroup owns one row, two per CU.  H_m is the
+// caller's matrix, handed in as bit masks.  The gated product and the
+// d = 28672 rows keep had_quant_kron: there (1024 groups) phase 2 would take
+// five stages over 32 groups with one-byte code units, which measured 3-4%
+// slower than the DPP butterflies it saves (77-81 against 74-77 us).
+//
+// "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
+// summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
+// H_{2^n} (x) H_m with a known H_m, computable in O(d (m + n)); Stage 1b:
+// the online Hadamard before the down-projection.
+//
+// Element e = a * m + b, a = 0..NP-1 (the power-of-two index, bits a0 ..),
+// b = 0..m-1.  The DPP butterflies of a lane-major layout cost about twice a
+// register butterfly on this chip (a v_fmac_f32_dpp issues at about half the
+// rate of a v_fmac_f32), so the layout keeps every stage in registers:
+//   phase 1  wave w, lane l = n + 16 g, tile t (of 8) load the 16-byte chunk
+//            b = 8 g .. 8 g + 7 of group a = 128 w + 16 t + n, as now the A
+//            operand of v_mfma_f32_16x16x32_f16; H_m (rows 0-15 and 16-31)
+//            is the B operand.  D = X^T H_m^T then holds, in lane n + 16 g,
+//            b' = n (and 16 + n) of the four groups 128 w + 16 t + 4 g + i,
+//            i = 0..3 in its registers.  Butterflies over a0, a1 (i) and
+//            a4, a5, a6 (t), all in registers; the row goes to LDS b-major
+//            (row b', group a), four consecutive groups per 16-byte store.
+//   phase 2  task (c, u): c fixes a0, a1, a4, a5, a6 (32 combos), u a run
+//            of four consecutive b.  It reads its four values of each of the
+//            16 groups that differ in a2, a3, a7, a8, runs those stages in
+//            registers, joins the workgroup maximum, quantises and writes
+//            16-bit code units to LDS; the row's codes then leave in 16-byte
+//            stores.
+#pragma once
+
+#include "kron_rows.h"
+
+namespace quarot {
+
+template <int M, int NP>
+struct KronTCfg {
+  static constexpr int D = NP * M;
+  static constexpr int AW = 128;  // groups per wave in phase 1
+  static constexpr int TILES = AW / 16;
+  static constexpr int NWAVE = NP / AW;
+  static constexpr int THREADS = 64 * NWAVE;
+  static constexpr int BLOCKS_PER_CU = NWAVE == 4 ? 2 : 1;
+  static constexpr int QN = NP / 32;  // phase-2 groups: a2, a3, a7, a8
+  static constexpr int BW = 64 / QN;  // b per task: 4
+  static constexpr int UNITS = M / BW;
+  static constexpr int TASKS = 32 * UNITS;
+  static constexpr int HALVES = (M > 16) ? 2 : 1;
+  // LDS row of one b: the NP groups plus a pad of four floats.  Group a of
+  // a row sits at column a ^ kront_swz(a) (bits 2, 3 XOR a5, a6).  4-byte
+  // LDS accesses go through 32 banks, half a wave per cycle; the phase-2
+  // reads of a half wave (32 combos: a0, a1, a4, a5, a6) then hit 32
+  // distinct banks, and the phase-1 16-byte writes stay conflict-free with
+  // this pad (SQ_LDS_BANK_CONFLICT on a probe of both patterns: none).
+  static constexpr int AP = NP + 4;
+  static constexpr int CODE_OFF = M * AP;  // the codes follow the fp32 row
+  static constexpr int LDS_BYTES = CODE_OFF * 4 + D / 2;
+  static_assert(M % 4 == 0 && M > 16 && M <= 32 && M % BW == 0, "m = 20 .. 32, a multiple of 4");
+  static_assert(NP == 512, "four waves per row");
+  static_assert(TASKS <= THREADS && TASKS % 64 == 0, "whole waves of phase-2 tasks");
+};
+
+// column offset of group a within its LDS row: a ^ kront_swz(a)
+__device__ __forceinline__ constexpr int kront_swz(int a) {
+  return (((a >> 5) & 1) << 2) | (((a >> 6) & 1) << 3);
+}
+
+template <int M, bool CLAMP, int NP>
+__global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront(
+    const __half* __restrict__ x, int64_t ld_x, int64_t rows, const int8_t* __restrict__ signs,
+    HadMasks hm, float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q,
+    __half* __restrict__ scale_out, float* __restrict__ x_rot, float norm) {
+  using C = KronTCfg<M, NP>;
+  extern __shared__ float4 kront_lds[];  // the row in fp32 (b-major), then its codes
+  float* buf = reinterpret_cast<float*>(kront_lds);
+  __shared__ float red[C::NWAVE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  constexpr int TILES = C::TILES, AW = C::AW, AP = C::AP, BW = C::BW, QN = C::QN;
+
+  // valid elements of this lane's chunk: b = 8 g .. 8 g + cnt - 1 (cnt 8 or
+  // 0 for m = 24; 8 or 4 for m = 28).  The lane loads 16 bytes inside its
+  // group: a full chunk at b = 8 g, a half chunk (the group's last four) at
+  // b = 8 g - 4 so the wanted values sit in the upper half, lanes past m at
+  // the group start.  Unwanted slots meet zero rows of the B operand.
+  const int cnt = min(8, max(0, M - 8 * g));
+  const int off16 = cnt == 8 ? 8 * g : (cnt == 4 ? 8 * g - 4 : 0);
+  // B operands: B[k][b'] = H_m[b'][k] for b' = n (and 16 + n), k = the
+  // lane's K slots, zero padded: slot j pairs with column 8 g + j, or
+  // 8 g + j - 4 for a half chunk.  (The same registers as the A operand of
+  // the lane-major layout: the two operands share one lane layout.)
+  const int shift = cnt == 4 ? 4 : 0;
+  const uint32_t nz_lo = mask_row(hm.nz, n) >> (8 * g), neg_lo = mask_row(hm.neg, n) >> (8 * g);
+  const uint32_t nz_hi = mask_row(hm.nz, n + 16) >> (8 * g);
+  const uint32_t neg_hi = mask_row(hm.neg, n + 16) >> (8 * g);
+  half8_t h_lo, h_hi;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool in = j >= shift;
+    h_lo[j] = in ? had_entry(nz_lo, neg_lo, j - shift) : _Float16(0.0f);
+    h_hi[j] = in ? had_entry(nz_hi, neg_hi, j - shift) : _Float16(0.0f);
+  }
+  // signs of this lane's phase-1 elements (the same for every row), as fp16
+  // sign-bit masks: group a = 128 wave + 16 t + n
+  uint4 mask[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
+    uint32_t w0 = 0, w1 = 0;
+    if (signs) {
+      const int a = AW * wave + 16 * t + n;
+      __builtin_memcpy(&w0, signs + a * M + off16, 4);
+      __builtin_memcpy(&w1, signs + a * M + off16 + 4, 4);
+    }
+    mask[t] = sign_masks8(w0, w1);
+  }
+
+  // phase-2 task of this thread: combo c (a0, a1 = c bits 0, 1; a4, a5, a6 =
+  // c bits 2-4), run u of BW b.  A wave takes units 2 w and 2 w + 1 of all
+  // 32 combos.
+  const bool task_on = tid < C::TASKS;
+  const int combo = tid & 31, unit = tid >> 5;
+  const int abase = (combo & 3) + ((combo >> 2) << 4);
+
+  auto load_row = [&](int64_t row, uint4 (&raw)[TILES]) {
+    const __half* src = x + row * ld_x;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+      __builtin_memcpy(&raw[t], src + (AW * wave + 16 * t + n) * M + off16, 16);
+  };
+
+  // ---- phase 1: H_m on the matrix cores (D = X^T H_m^T), then the
+  // butterflies over a0, a1 (register bits 0, 1) and a4-a6 (bits 3-5) ------
+  // register r = 8 t + 4 h + i: b' = 16 h + n of group 128 w + 16 t + 4 g + i
+  auto phase1 = [&](const uint4 (&raw)[TILES], float (&v)[8 * TILES]) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const uint4 r = make_uint4(raw[t].x ^ mask[t].x, raw[t].y ^ mask[t].y,
+                                 raw[t].z ^ mask[t].z, raw[t].w ^ mask[t].w);
+      const half8_t aop = __builtin_bit_cast(half8_t, r);
+      const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, h_lo, zero, 0, 0, 0);
+      const float4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, h_hi, zero, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[8 * t + q] = d0[q];
+        v[8 * t + 4 + q] = d1[q];
+      }
+    }
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      if (h == 4) continue;  // register bit 2 is the MFMA half (b')
+#pragma unroll
+      for (int r = 0; r < 8 * TILES; ++r)
+        if ((r & h) == 0) {
+          const float a = v[r], b = v[r + h];
+          v[r] = a + b;
+          v[r + h] = a - b;
+        }
+    }
+  };
+  // to LDS, b-major: element (a, b') at b' AP + (a ^ kront_swz(a)); four
+  // consecutive groups per store (a5, a6 are bits 1, 2 of t, so the swizzle
+  // of a tile is a constant XOR on the lane's 4 g)
+  auto write_row = [&](const float (&v)[8 * TILES]) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int h = 0; h < C::HALVES; ++h) {
+        const int bp = 16 * h + n;
+        if (bp < M)
+          *reinterpret_cast<float4*>(buf + bp * AP + AW * wave + 16 * t +
+                                     ((4 * g) ^ kront_swz(16 * t))) =
+              make_float4(v[8 * t + 4 * h], v[8 * t + 4 * h + 1], v[8 * t + 4 * h + 2],
+                          v[8 * t + 4 * h + 3]);
+      }
+  };
+  // ---- phase 2: a2, a3 and the group bits from a7 up, in registers ------
+  // register BW q + k holds b = BW unit + k of group a(q) = abase +
+  // 4 (q & 3) + 128 (q >> 2).  Returns the task's largest |value|.
+  constexpr int NV = QN * BW;
+  auto phase2 = [&](float (&v)[NV]) -> float {
+    float amax = 0.0f;
+    if (task_on) {
+      // column of a(q) = abase + ((4 (q & 3)) ^ swz) + 128 (q >> 2): the
+      // swizzle comes from abase's a5, a6 only
+      const int swz = kront_swz(abase);
+      const float* src = buf + BW * unit * AP + abase;
+      int col[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) col[j] = (4 * j) ^ swz;
+#pragma unroll
+      for (int k = 0; k < BW; ++k)
+#pragma unroll
+        for (int q = 0; q < QN; ++q)
+          v[BW * q + k] = src[k * AP + col[q & 3] + 128 * (q >> 2)];
+#pragma unroll
+      for (int h = 1; h < QN; h <<= 1)
+#pragma unroll
+        for (int q = 0; q < QN; ++q)
+          if ((q & h) == 0)
+#pragma unroll
+            for (int k = 0; k < BW; ++k) {
+              const float a = v[BW * q + k], b = v[BW * (q + h) + k];
+              v[BW * q + k] = a + b;
+              v[BW * (q + h) + k] = a - b;
+            }
+#pragma unroll
+      for (int r = 0; r < NV; ++r) amax = fmaxf(amax, fabsf(v[r]));
+    }
+    return amax;
+  };
+  // the row's scale from the per-wave maxima, then its codes to the LDS code
+  // area (four codes per 16-bit unit) and the optional fp32 copy.  Group
+  // a(q)'s run starts at element a(q) M + 4 unit: code unit a(q) (M / 4) +
+  // unit.
+  auto quantize = [&](const float (&v)[NV], int64_t row) -> __half {
+    float amax = red[0];
+#pragma unroll
+    for (int w = 1; w < C::NWAVE; ++w) amax = fmaxf(amax, red[w]);
+    const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
+    const float kq = inv_scale(s16) * norm;
+    if (task_on) {
+      const int cbase = abase * (M / BW) + unit;
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        const int cu = cbase + (M / BW) * (4 * (q & 3) + 128 * (q >> 2));
+        float t[BW];
+#pragma unroll
+        for (int k = 0; k < BW; ++k) t[k] = magic_code<CLAMP>(v[BW * q + k], kq);
+        // byte 0 of each magic word is q + 8 (four bits); xor 8 gives the
+        // two's complement nibble
+        const uint32_t ev = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t[2]),
+                                                  __builtin_bit_cast(uint32_t, t[0]), 0x0c0c0400u);
+        const uint32_t od = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, t[3]),
+                                                  __builtin_bit_cast(uint32_t, t[1]), 0x0c0c0400u);
+        reinterpret_cast<uint16_t*>(buf + C::CODE_OFF)[cu] =
+            uint16_t((((od << 4) | ev) ^ 0x8888u) & 0xFFFFu);
+      }
+      if (x_rot) {
+        float* xr = x_rot + row * int64_t(C::D) + abase * M + BW * unit;
+#pragma unroll
+        for (int q = 0; q < QN; ++q)
+#pragma unroll
+          for (int k = 0; k < BW; ++k)
+            xr[M * (4 * (q & 3) + 128 * (q >> 2)) + k] = v[BW * q + k] * norm;
+      }
+    }
+    return s16;
+  };
+  // the row's codes: D / 2 bytes from the LDS code area, 16-byte stores
+  auto store_codes = [&](int64_t row, __half s16) {
+    uint8_t* qrow = q_out + row * ld_q;
+    constexpr int kChunks = C::D / 32, kIter = (kChunks + C::THREADS - 1) / C::THREADS;
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int c = tid + C::THREADS * i;
+      if (i + 1 < kIter || c < kChunks)
+        *reinterpret_cast<uint4*>(qrow + 16 * c) =
+            reinterpret_cast<const uint4*>(buf + C::CODE_OFF)[c];
+    }
+    if (tid == 0) scale_out[row] = s16;
+  };
+
+  int64_t row = blockIdx.x;
+  uint4 raw[TILES];
+  if (row >= rows) return;
+  load_row(row, raw);
+  // One row at a time, two barriers per row.  A row's codes leave after the
+  // next row's first barrier (or after the loop): every thread has written
+  // them by then, and every thread has read them before it reaches the next
+  // row's second barrier, after which that row's codes take the area.  red
+  // is read between a row's second barrier and the next row's first, and
+  // written between those two.
+  int64_t prev = -1;  // the row whose codes wait in the LDS code area
+  __half prev_s16 = __half(0.0f);
+  for (; row < rows; row += gridDim.x) {
+    float v[8 * TILES];
+    const int64_t nrow = row + gridDim.x;
+    phase1(raw, v);
+    if (nrow < rows) load_row(nrow, raw);  // prefetch
+    write_row(v);
+    __syncthreads();
+    if (prev >= 0) store_codes(prev, prev_s16);
+    // phase 2 reuses the registers
+    float(&v2)[NV] = *reinterpret_cast<float(*)[NV]>(&v[0]);
+    float amax = phase2(v2);
+    amax = wave_max_dpp(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();  // phase-2 reads of buf are done; red is complete
+    prev_s16 = quantize(v2, row);
+    prev = row;
+  }
+  __syncthreads();
+  store_codes(prev, prev_s16);
+}
+
+}  // namespace quarot
