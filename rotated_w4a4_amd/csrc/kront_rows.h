@@ -56,8 +56,19 @@ struct KronTCfg {
   // this pad (SQ_LDS_BANK_CONFLICT on a probe of both patterns: none).
   static constexpr int AP = NP + 4;
   static constexpr int CODE_OFF = M * AP;  // the codes follow the fp32 row
-  static constexpr int LDS_BYTES = CODE_OFF * 4 + D / 2;
-  static_assert(M % 4 == 0 && M > 16 && M <= 32 && M % BW == 0, "m = 20 .. 32, a multiple of 4");
+  // Code area: the row's D / 32 16-byte chunks with one chunk of pad after
+  // every CODE_BLK.  A half wave's 16-bit code writes (32 combos, a stride
+  // of M / 4 units) step by multiples of 32 dwords over a5 and a6, so at
+  // m = 24 they would share 8 banks; the pad moves each 96-dword block by 4
+  // banks, and a model of every (unit, q) write then finds 32 distinct
+  // banks.
+  static constexpr int CODE_CHUNKS = D / 32;
+  static constexpr int CODE_BLK = 24;
+  static constexpr int QSTEP = (M / BW) * 128;  // code units between q and q + 4
+  static constexpr int LDS_BYTES =
+      CODE_OFF * 4 + 16 * (CODE_CHUNKS + (CODE_CHUNKS + CODE_BLK - 1) / CODE_BLK);
+  static_assert(M == 24, "the code-area pad is laid out for m = 24");
+  static_assert(QSTEP % (8 * CODE_BLK) == 0, "q + 4 keeps a unit's place in its pad block");
   static_assert(NP == 512, "four waves per row");
   static_assert(TASKS <= THREADS && TASKS % 64 == 0, "whole waves of phase-2 tasks");
 };
@@ -215,7 +226,7 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
   // the row's scale from the per-wave maxima, then its codes to the LDS code
   // area (four codes per 16-bit unit) and the optional fp32 copy.  Group
   // a(q)'s run starts at element a(q) M + 4 unit: code unit a(q) (M / 4) +
-  // unit.
+  // unit, placed past the pad chunks before it.
   auto quantize = [&](const float (&v)[NV], int64_t row) -> __half {
     float amax = red[0];
 #pragma unroll
@@ -223,10 +234,17 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
     const __half s16 = row_scale_fp16(amax * norm, clip_ratio);
     const float kq = inv_scale(s16) * norm;
     if (task_on) {
-      const int cbase = abase * (M / BW) + unit;
+      // unit index u lives at u + 8 (u / (8 CODE_BLK)): 8 units a chunk
+      int cpad[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = abase * (M / BW) + unit + (M / BW) * 4 * j;
+        cpad[j] = c + 8 * (c / (8 * C::CODE_BLK));
+      }
+      constexpr int kQStepPad = C::QSTEP + 8 * (C::QSTEP / (8 * C::CODE_BLK));
 #pragma unroll
       for (int q = 0; q < QN; ++q) {
-        const int cu = cbase + (M / BW) * (4 * (q & 3) + 128 * (q >> 2));
+        const int cu = cpad[q & 3] + kQStepPad * (q >> 2);
         float t[BW];
 #pragma unroll
         for (int k = 0; k < BW; ++k) t[k] = magic_code<CLAMP>(v[BW * q + k], kq);
@@ -259,7 +277,7 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
       const int c = tid + C::THREADS * i;
       if (i + 1 < kIter || c < kChunks)
         *reinterpret_cast<uint4*>(qrow + 16 * c) =
-            reinterpret_cast<const uint4*>(buf + C::CODE_OFF)[c];
+            reinterpret_cast<const uint4*>(buf + C::CODE_OFF)[c + c / C::CODE_BLK];
     }
     if (tid == 0) scale_out[row] = s16;
   };
