@@ -318,9 +318,14 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   // consecutive columns of one row: 16-byte output stores instead of 2-byte
   // ones.  32x32 block layout: lane holds column (lane & 31); register r
   // holds row 8 * (r / 4) + 4 * (lane / 32) + (r % 4).  Each wave owns a
-  // [WM][WN + 8] int32 staging tile (the 8-word pad puts the rows r and r + 4
-  // written by one instruction on opposite bank halves).
-  constexpr int WM = C::WM, WN = C::WN, LDS_ROW = WN + 8;
+  // [WM][WN] int32 staging tile.  The writes (32 consecutive words of a row
+  // per half wave) are conflict-free.  On the read side the 8 lanes of a row
+  // fetch every other 16-byte piece of it with one ds_read_b128, so lane
+  // (cg, r0) takes the half (cg ^ r0) & 1 of its 8 columns first: the pieces
+  // of rows r0 and r0 + 1 then interleave.  SQ_LDS_BANK_CONFLICT on a probe
+  // of this read pattern: none, against 8 cycles per read with the earlier
+  // [WN + 8] rows and fixed order (the kernel's whole 262,144 per launch).
+  constexpr int WM = C::WM, WN = C::WN, LDS_ROW = WN;
   static_assert(C::WAVES_M * C::WAVES_N * WM * LDS_ROW * 4 <= 3 * C::STAGE,
                 "staging tiles must fit in the pipeline's LDS");
   __syncthreads();  // every wave is done reading the last K tile
@@ -337,7 +342,9 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
   __syncthreads();
   // lane -> columns 8 cg .. 8 cg + 7 of the wave tile, rows lane / 8 + 8 s
   constexpr int CG = WN / 8, RSTEP = 64 / CG;
+  static_assert(CG == 8 && RSTEP % 2 == 0, "the read order below pairs rows r0 and r0 + 1");
   const int cg = lane % CG, r0 = lane / CG;
+  const int first = (cg ^ r0) & 1;  // half of the 8 columns read first
   const int col0 = n0 + wn + 8 * cg;
   float sw[8];
 #pragma unroll
@@ -352,8 +359,10 @@ __global__ __launch_bounds__(C::THREADS) void w4a4_gemm_kernel(
     const int row = m0 + wm + lrow_;
     if (row >= M) continue;
     const float sx = __half2float(a_scale[row]);
-    const int4 v0 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg);
-    const int4 v1 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg + 4);
+    const int4 u0 = *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg + 4 * first);
+    const int4 u1 =
+        *reinterpret_cast<const int4*>(stg + lrow_ * LDS_ROW + 8 * cg + 4 * (1 - first));
+    const int4 v0 = first ? u1 : u0, v1 = first ? u0 : u1;
     const int v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     __half h[8];
 #pragma unroll
