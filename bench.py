@@ -61,7 +61,7 @@ def log(msg: str) -> None:
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama70b_down", choices=sorted(workloads.ACT_CONFIGS))
     p.add_argument("--kv", action="store_true", help="benchmark the K/V cache write instead")
