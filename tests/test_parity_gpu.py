@@ -171,6 +171,57 @@ def test_gemm_extreme_codes():
     assert np.all(host(acc) == 64 * K)
 
 
+# The largest K the entry point takes (65536): 256 * |acc| reaches 2^30 for an
+# all -8 row against an all -8 column, the widened accumulator's limit.  Ragged
+# M and N on the eight-wave kernel, with extreme rows and columns among random
+# ones; expected values from the oracle's integer GEMM.
+def test_gemm_max_k_extreme_rows_ragged():
+    M, N, K = 96, 300, 65536
+    rng = np.random.default_rng(65536)
+    qa = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qb = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    qa[0] = -8
+    qa[1] = 7
+    qa[2, 0::2], qa[2, 1::2] = -8, 7
+    qb[0] = -8
+    qb[1] = 7
+    qb[N - 1] = -8
+    sa = rng.uniform(0.01, 1.0, M).astype(np.float16)
+    sb = rng.uniform(0.001, 0.01, N).astype(np.float16)
+    acc_ref, y_ref = oracle.w4a4_reference(qa, sa, qb, sb)
+    assert acc_ref[0, 0] == 64 * K and acc_ref[1, 0] == -56 * K
+    say(f"gemm max K M={M} N={N} K={K}")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(dev(oracle.pack_int4(qa)), dev(sa), dev(oracle.pack_int4(qb)), dev(sb), K,
+                     acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    check_y_elementwise(host(y), y_ref)
+
+
+def test_gemm_large_tile_max_k_closed_form():
+    # Large-tile kernel at K = 65536.  Rows of A and B are all -8, all 7, or
+    # -8 at even and 7 at odd K, by index mod 3, so every accumulator has a
+    # closed form: K/2 times 128, -112, 98, 8, -7 or 113 (the row types' dot
+    # products over one even/odd pair).  Packed bytes follow the pages' layout
+    # (even element in the low nibble): 0x88, 0x77 and 0x78.
+    M, N, K = 4096, 4096, 65536
+    pair = np.array([[128, -112, 8], [-112, 98, -7], [8, -7, 113]], np.int64)
+    packed = np.array([0x88, 0x77, 0x78], np.uint8)
+    ta, tb = np.arange(M) % 3, (np.arange(N) * 7 + 1) % 3
+    a_q = np.repeat(packed[ta][:, None], K // 2, axis=1)
+    b_q = np.repeat(packed[tb][:, None], K // 2, axis=1)
+    acc_ref = pair[ta][:, tb] * (K // 2)
+    assert acc_ref.max() == 64 * K and acc_ref.min() == -56 * K
+    # scales 2^-8: y = acc / 2^16, every value exact in fp16
+    sa = np.full(M, 2.0 ** -8, np.float16)
+    sb = np.full(N, 2.0 ** -8, np.float16)
+    say(f"gemm large tiles max K M={M} N={N} K={K}")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = qr.w4a4_gemm(dev(a_q), dev(sa), dev(b_q), dev(sb), K, acc_out=acc)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    np.testing.assert_array_equal(host(y).astype(np.float64), acc_ref / 65536.0)
+
+
 # Shapes with at least 256 output tiles of 256 x 256 run the large-tile kernel
 # (one wave per SIMD, 64-byte K tiles in a four-stage LDS ring): ragged M and
 # N edges, a partial last K tile (K % 128 != 0) and an aligned case.
