@@ -103,3 +103,22 @@ def test_planted_reducible_modulus_is_caught(monkeypatch):
     monkeypatch.setattr(had_mod, "_field_for", lambda q: GF(3, 3, modulus_low=(1, 0, 0)))
     h = had_mod.paley1(27).astype(np.int64)
     assert not np.array_equal(h @ h.T, 28 * np.eye(28, dtype=np.int64))
+
+
+@pytest.mark.parametrize("a,b", [(2, 64), (16, 128), (32, 32), (256, 16)])
+def test_sylvester_factors_as_kronecker_product(a, b):
+    # (-1)^popcount(i & j) splits over the high and low index bits, so the
+    # Sylvester matrix of order a b is H_a (x) H_b in natural order (the GPU
+    # tests of large power-of-two rows take the oracle's rotation in this form)
+    np.testing.assert_array_equal(np.kron(sylvester(a), sylvester(b)), sylvester(a * b))
+
+
+def test_power_of_two_rotation_equals_its_kronecker_form():
+    from oracle import rotate_rows
+
+    rng = np.random.default_rng(3)
+    d = 4096
+    x = rng.standard_normal((5, d))
+    s = (1 - 2 * rng.integers(0, 2, d)).astype(np.int8)
+    np.testing.assert_allclose(rotate_rows(x, s, 128, hm=sylvester(128)), rotate_rows(x, s, 1),
+                               rtol=0, atol=1e-12)

@@ -527,6 +527,26 @@ def test_had_quant_strided_rows_clip_and_zero_rows():
     assert np.all(qh[3, : d // 2] == 0)
 
 
+# Power-of-two rows past the d = 4096 kernel run the generic kernel, with up
+# to 15 butterfly stages.  The oracle's rotation is taken in its Kronecker
+# form: the Sylvester H_d equals H_{d/128} (x) H_128 in natural order, so
+# m = 128 with the Sylvester H_128 as the small factor is the same rotation,
+# built from small matrices (pinned on the CPU).
+@pytest.mark.parametrize("d", [8192, 16384, 32768])
+def test_had_quant_large_power_of_two(d):
+    rng = np.random.default_rng(d)
+    rows = 37
+    x16 = rng.standard_normal((rows, d)).astype(np.float16)
+    ch = rng.choice(d, max(1, d // 1000), replace=False)
+    x16[:, ch] *= 40
+    signs = (1 - 2 * rng.integers(0, 2, d)).astype(np.int8)
+    say(f"had_quant power of two d={d} rows={rows}")
+    q, s, xr = gpu_had_quant(x16, signs, 1)
+    ref = oracle.had_quant(x16, signs, 128, 1.0, hm=oracle.sylvester(128))
+    check_rot(xr, ref["x_rot"])
+    check_quant(oracle.unpack_int4(q), s, ref["x_rot"], ref["scales"])
+
+
 @pytest.mark.parametrize("d", [256, 4096])
 def test_exact_ties_round_to_even(d):
     # rows whose rotated values sit exactly on k + 1/2 steps of the scale.
