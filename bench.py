@@ -766,7 +766,8 @@ KERNEL_KEYS = {"w4a4_gemm": "w4a4_gemm", "had_quant": "had_quant", "kv_had_quant
                "decode_split": "kv_decode", "decode_combine": "kv_decode",
                "cross_head_quant": "cross_head"}
 # instantiations of the rotate+quant kernels that form the gated product first
-GATED_KERNEL = re.compile(r"had_quant_kron<\d+, (?:true|false), true\b|had_quant_lds<true>")
+GATED_KERNEL = re.compile(r"had_quant_kron<\d+, (?:true|false), true\b|"
+                          r"had_quant_kront<\d+, (?:true|false), \d+, true\b|had_quant_lds<true>")
 
 
 def kernel_key(kname: str):

@@ -222,11 +222,11 @@ bool kron_attr_ok() {
   return ok;
 }
 
-// The same for the register-butterfly kernel of plain rows.
-template <int M, bool CLAMP, int NP>
+// The same for the register-butterfly kernel.
+template <int M, bool CLAMP, int NP, bool SWIGLU>
 bool kront_attr_ok() {
   static const bool ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kront<M, CLAMP, NP>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(had_quant_kront<M, CLAMP, NP, SWIGLU>),
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           KronTCfg<M, NP>::LDS_BYTES) == hipSuccess;
   return ok;
@@ -266,12 +266,12 @@ int launch_kron(const RowSource& src, int64_t rows, const HadMasks& hm, const in
   return check_launch("had_quant_kron");
 }
 
-template <int M, bool CLAMP, int NP>
+template <int M, bool CLAMP, int NP, bool SWIGLU>
 int launch_kront(const RowSource& src, int64_t rows, const HadMasks& hm, const int8_t* signs,
                  float clip_ratio, uint8_t* q_out, int64_t ld_q, __half* scale_out,
                  float* x_rot_out, int cus, hipStream_t stream) {
   using C = KronTCfg<M, NP>;
-  if (!kront_attr_ok<M, CLAMP, NP>()) {
+  if (!kront_attr_ok<M, CLAMP, NP, SWIGLU>()) {
     set_error("could not raise the dynamic LDS limit for d = %d", C::D);
     return QUAROT_ERR_HIP;
   }
@@ -279,9 +279,10 @@ int launch_kront(const RowSource& src, int64_t rows, const HadMasks& hm, const i
   const int64_t cap = int64_t(cus) * C::BLOCKS_PER_CU;
   const int64_t blocks = rows < cap ? rows : cap;
   const float norm = 1.0f / sqrtf(float(C::D));
-  hipLaunchKernelGGL((had_quant_kront<M, CLAMP, NP>), dim3(unsigned(blocks)),
-                     dim3(unsigned(C::THREADS)), C::LDS_BYTES, stream, src.x, src.ld_x, rows,
-                     signs, hm, clip_ratio, q_out, ld_q, scale_out, x_rot_out, norm);
+  hipLaunchKernelGGL((had_quant_kront<M, CLAMP, NP, SWIGLU>), dim3(unsigned(blocks)),
+                     dim3(unsigned(C::THREADS)), C::LDS_BYTES, stream, src.x, src.ld_x, src.up,
+                     src.ld_up, rows, signs, hm, clip_ratio, q_out, ld_q, scale_out, x_rot_out,
+                     norm);
   return check_launch("had_quant_kront");
 }
 
@@ -296,21 +297,21 @@ int launch_kron_clip(const RowSource& src, int64_t rows, const HadMasks& hm,
                                            scale_out, x_rot_out, cus, stream);
 }
 
-// Plain rows of 512 groups: the register-butterfly kernel; the gated product
-// and the 1024-group rows: had_quant_kron.
+// Rows of 512 groups (plain or gated): the register-butterfly kernel; the
+// 1024-group rows: had_quant_kron.
 template <int M, bool SWIGLU, int NP = 1024>
 int launch_kron_any(const RowSource& src, int64_t rows, const HadMasks& hm,
                     const int8_t* signs, float clip_ratio, uint8_t* q_out, int64_t ld_q,
                     __half* scale_out, float* x_rot_out, int cus, hipStream_t stream) {
-  if constexpr (SWIGLU || NP != 512) {
+  if constexpr (NP != 512) {
     return launch_kron_clip<M, SWIGLU, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
                                            scale_out, x_rot_out, cus, stream);
   } else {
     if (clip_ratio != 1.0f)
-      return launch_kront<M, true, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
-                                       x_rot_out, cus, stream);
-    return launch_kront<M, false, NP>(src, rows, hm, signs, clip_ratio, q_out, ld_q, scale_out,
-                                      x_rot_out, cus, stream);
+      return launch_kront<M, true, NP, SWIGLU>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                               scale_out, x_rot_out, cus, stream);
+    return launch_kront<M, false, NP, SWIGLU>(src, rows, hm, signs, clip_ratio, q_out, ld_q,
+                                              scale_out, x_rot_out, cus, stream);
   }
 }
 

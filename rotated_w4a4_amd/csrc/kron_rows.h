@@ -1,9 +1,11 @@
 // Rotate+quant of rows of d = NP * m (H_NP (x) H_m, NP = 2^n): one
-// workgroup owns one row (d = 28672: 512 threads, one per CU; d = 12288: 256
+// workgroup owns one row (NP = 1024: 512 threads, one per CU; NP = 512: 256
 // threads, two per CU, so two rows are in flight per CU).  H_m is the
-// caller's matrix, handed in as bit masks.  The d = 12288 row runs as
-// NP = 512 groups of m = 24 under H_2 (x) H_12 (built on the host from the
-// caller's H_12); d = 28672 as 1024 groups of 28.
+// caller's matrix, handed in as bit masks.  d = 28672 (plain and gated) runs
+// here as 1024 groups of 28.  The rows of 512 groups (d = 12288 as groups of
+// 24 under H_2 (x) H_12) are dispatched to had_quant_kront, which keeps every
+// butterfly in registers; the NP = 512 configuration below is the layout
+// that kernel replaced.
 //
 // With SWIGLU the row is the gated FFN product c = SiLU(gate) * up, formed
 // in fp32 from the two fp16 inputs as they arrive (the same page, section

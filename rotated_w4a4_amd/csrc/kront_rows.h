@@ -1,10 +1,14 @@
 // Rotate+quant of plain rows of d = 512 m (H_512 (x) H_m; d = 12288 runs as
 // 512 groups of 24 under H_2 (x) H_12) with every butterfly stage in
 // registers.  One 256-thread workgroup owns one row, two per CU.  H_m is the
-// caller's matrix, handed in as bit masks.  The gated product and the
-// d = 28672 rows keep had_quant_kron: there (1024 groups) phase 2 would take
-// five stages over 32 groups with one-byte code units, which measured 3-4%
-// slower than the DPP butterflies it saves (77-81 against 74-77 us).
+// caller's matrix, handed in as bit masks.  With SWIGLU the row is the gated
+// FFN product c = SiLU(gate) * up (section 3.4 Stage 1b of the same page),
+// formed in fp32 on compact 16-byte chunks and split as in had_quant_kron:
+// hi = fp16(c), lo = fp16((c - hi) 2^11), staged in the wave's own slice of
+// the LDS row area and fed to the matrix cores against H_m and 2^-11 H_m.
+// The d = 28672 rows keep had_quant_kron: there (1024 groups) phase 2 would
+// take five stages over 32 groups with one-byte code units, which measured
+// 3-4% slower than the DPP butterflies it saves (77-81 against 74-77 us).
 //
 // "QuaRot: Outlier-Free 4-Bit Inference in Rotated LLMs" (paper-graph-ui
 // summary), section 3.4 Stage 1a: for d = 2^n m the Hadamard is
@@ -78,11 +82,14 @@ __device__ __forceinline__ constexpr int kront_swz(int a) {
   return (((a >> 5) & 1) << 2) | (((a >> 6) & 1) << 3);
 }
 
-template <int M, bool CLAMP, int NP>
+// SWIGLU: x is the gate projection and up the up projection; the row is
+// SiLU(x) * up.  Otherwise up is unused and the row is x.
+template <int M, bool CLAMP, int NP, bool SWIGLU>
 __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront(
-    const __half* __restrict__ x, int64_t ld_x, int64_t rows, const int8_t* __restrict__ signs,
-    HadMasks hm, float clip_ratio, uint8_t* __restrict__ q_out, int64_t ld_q,
-    __half* __restrict__ scale_out, float* __restrict__ x_rot, float norm) {
+    const __half* __restrict__ x, int64_t ld_x, const __half* __restrict__ up, int64_t ld_up,
+    int64_t rows, const int8_t* __restrict__ signs, HadMasks hm, float clip_ratio,
+    uint8_t* __restrict__ q_out, int64_t ld_q, __half* __restrict__ scale_out,
+    float* __restrict__ x_rot, float norm) {
   using C = KronTCfg<M, NP>;
   extern __shared__ float4 kront_lds[];  // the row in fp32 (b-major), then its codes
   float* buf = reinterpret_cast<float*>(kront_lds);
@@ -107,18 +114,38 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
   const uint32_t nz_lo = mask_row(hm.nz, n) >> (8 * g), neg_lo = mask_row(hm.neg, n) >> (8 * g);
   const uint32_t nz_hi = mask_row(hm.nz, n + 16) >> (8 * g);
   const uint32_t neg_hi = mask_row(hm.neg, n + 16) >> (8 * g);
-  half8_t h_lo, h_hi;
+  half8_t h_lo, h_hi, hs_lo, hs_hi;  // hs: H_m 2^-11 for the gated product's low parts
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bool in = j >= shift;
     h_lo[j] = in ? had_entry(nz_lo, neg_lo, j - shift) : _Float16(0.0f);
     h_hi[j] = in ? had_entry(nz_hi, neg_hi, j - shift) : _Float16(0.0f);
+    hs_lo[j] = h_lo[j] * _Float16(1.0f / 2048.0f);
+    hs_hi[j] = h_hi[j] * _Float16(1.0f / 2048.0f);
+  }
+  // The gated product is formed on a compact layout: the wave's AW groups
+  // (contiguous in the row) are J 16-byte chunks per lane and stream, every
+  // element real.  Its fp16 sign-bit masks are XORed into up.
+  constexpr int J = AW * M / 512;
+  static_assert(!SWIGLU || AW * M % 512 == 0, "whole compact chunks per lane");
+  uint4 cmask[SWIGLU ? J : 1];
+  if constexpr (SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      uint32_t w0 = 0, w1 = 0;
+      if (signs) {
+        const int e = AW * wave * M + 512 * j + 8 * lane;
+        __builtin_memcpy(&w0, signs + e, 4);
+        __builtin_memcpy(&w1, signs + e + 4, 4);
+      }
+      cmask[j] = sign_masks8(w0, w1);
+    }
   }
   // signs of this lane's phase-1 elements (the same for every row), as fp16
   // sign-bit masks: group a = 128 wave + 16 t + n
-  uint4 mask[TILES];
+  uint4 mask[SWIGLU ? 1 : TILES];
 #pragma unroll
-  for (int t = 0; t < TILES; ++t) {
+  for (int t = 0; t < (SWIGLU ? 0 : TILES); ++t) {
     uint32_t w0 = 0, w1 = 0;
     if (signs) {
       const int a = AW * wave + 16 * t + n;
@@ -135,25 +162,87 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
   const int combo = tid & 31, unit = tid >> 5;
   const int abase = (combo & 3) + ((combo >> 2) << 4);
 
-  auto load_row = [&](int64_t row, uint4 (&raw)[TILES]) {
-    const __half* src = x + row * ld_x;
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-      __builtin_memcpy(&raw[t], src + (AW * wave + 16 * t + n) * M + off16, 16);
+  // one row's loads: tiles of 16 groups, or (gated) J compact chunks of both
+  // inputs as buffer loads (one 32-bit lane offset for every chunk)
+  constexpr int NR = SWIGLU ? J : TILES, TU = SWIGLU ? J : 1;
+  const int lane_off = 2 * (AW * wave * M + 8 * lane);
+  auto load_chunk = [&](int64_t row, int j, uint4& r, uint4& ru) {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__half*>(x + row * ld_x), 0, 2 * C::D, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__half*>(up + row * ld_up), 0, 2 * C::D, 0x00020000);
+    r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane_off + 1024 * j, 0, 0));
+    ru = __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + 1024 * j, 0, 0));
   };
+  auto load_row = [&](int64_t row, uint4 (&raw)[NR], uint4 (&raw_u)[TU]) {
+    if constexpr (SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) load_chunk(row, j, raw[j], raw_u[j]);
+    } else {
+      const __half* src = x + row * ld_x;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+        __builtin_memcpy(&raw[t], src + (AW * wave + 16 * t + n) * M + off16, 16);
+    }
+  };
+  // Gated product staging: float f (< 24 AW) of the wave's staging area lives
+  // in the wave's own slice of the b-major row area (rows of AW floats at
+  // column AW wave), which only this wave writes in write_row, after it has
+  // read the staged parts back.  hi parts take floats 0 .. AW M / 2 - 1, lo
+  // parts the rest (AW M floats in all: the slice's M rows).
+  static_assert(!SWIGLU || M == 24, "the staging area is the wave's 24 rows of AW floats");
+  auto stage = [&](int f) -> float* { return buf + (f >> 7) * AP + AW * wave + (f & 127); };
 
   // ---- phase 1: H_m on the matrix cores (D = X^T H_m^T), then the
   // butterflies over a0, a1 (register bits 0, 1) and a4-a6 (bits 3-5) ------
   // register r = 8 t + 4 h + i: b' = 16 h + n of group 128 w + 16 t + 4 g + i
-  auto phase1 = [&](const uint4 (&raw)[TILES], float (&v)[8 * TILES]) {
+  // (gated product: nrow < rows issues the next row's loads chunk by chunk
+  // as soon as each chunk's registers are free, so they overlap the product
+  // phase instead of following it)
+  auto phase1 = [&](uint4 (&raw)[NR], uint4 (&raw_u)[TU], float (&v)[8 * TILES],
+                    int64_t nrow) {
+    constexpr int kLo = AW * M / 2;  // float offset of the lo parts (after AW M / 2 of hi)
+    if constexpr (SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const uint4 um = make_uint4(raw_u[j].x ^ cmask[j].x, raw_u[j].y ^ cmask[j].y,
+                                    raw_u[j].z ^ cmask[j].z, raw_u[j].w ^ cmask[j].w);
+        uint4 hi, lo;
+        swiglu_split8(raw[j], um, hi, lo);
+        if (nrow < rows) load_chunk(nrow, j, raw[j], raw_u[j]);
+        *reinterpret_cast<uint4*>(stage(256 * j + 4 * lane)) = hi;
+        *reinterpret_cast<uint4*>(stage(kLo + 256 * j + 4 * lane)) = lo;
+      }
+      // the wave reads back what its own lanes wrote: LDS completes a wave's
+      // accesses in order once they have all been issued and counted
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      const uint4 r = make_uint4(raw[t].x ^ mask[t].x, raw[t].y ^ mask[t].y,
-                                 raw[t].z ^ mask[t].z, raw[t].w ^ mask[t].w);
-      const half8_t aop = __builtin_bit_cast(half8_t, r);
       const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const float4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, h_lo, zero, 0, 0, 0);
-      const float4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, h_hi, zero, 0, 0, 0);
+      float4_t d0, d1;
+      if constexpr (SWIGLU) {
+        // chunk b = 8 g .. 8 g + 7 of group 16 t + n (lanes past m read the
+        // group's first chunk, against zero rows of H): element e = (16 t +
+        // n) m + 8 g is float e / 2 of the staged parts
+        const int f = ((16 * t + n) * M + (cnt > 0 ? 8 * g : 0)) >> 1;
+        const half8_t ah = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(stage(f)));
+        const half8_t al =
+            __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(stage(kLo + f)));
+        // X hi against H_m, then X lo against 2^-11 H_m onto it (exact products)
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, h_lo, zero, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, hs_lo, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, h_hi, zero, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, hs_hi, d1, 0, 0, 0);
+      } else {
+        const uint4 r = make_uint4(raw[t].x ^ mask[t].x, raw[t].y ^ mask[t].y,
+                                   raw[t].z ^ mask[t].z, raw[t].w ^ mask[t].w);
+        const half8_t aop = __builtin_bit_cast(half8_t, r);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, h_lo, zero, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, h_hi, zero, 0, 0, 0);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[8 * t + q] = d0[q];
@@ -283,9 +372,9 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
   };
 
   int64_t row = blockIdx.x;
-  uint4 raw[TILES];
+  uint4 raw[NR], raw_u[TU];
   if (row >= rows) return;
-  load_row(row, raw);
+  load_row(row, raw, raw_u);
   // One row at a time, two barriers per row.  A row's codes leave after the
   // next row's first barrier (or after the loop): every thread has written
   // them by then, and every thread has read them before it reaches the next
@@ -297,8 +386,8 @@ __global__ __launch_bounds__((KronTCfg<M, NP>::THREADS), 2) void had_quant_kront
   for (; row < rows; row += gridDim.x) {
     float v[8 * TILES];
     const int64_t nrow = row + gridDim.x;
-    phase1(raw, v);
-    if (nrow < rows) load_row(nrow, raw);  // prefetch
+    phase1(raw, raw_u, v, nrow);
+    if (!SWIGLU && nrow < rows) load_row(nrow, raw, raw_u);  // prefetch
     write_row(v);
     __syncthreads();
     if (prev >= 0) store_codes(prev, prev_s16);

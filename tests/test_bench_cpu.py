@@ -26,8 +26,10 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("name,key", [
-    ("void quarot::had_quant_kront<24, false, 512>(__half const*, long)", "had_quant"),
-    ("void quarot::had_quant_kront<24, true, 512>(__half const*, long)", "had_quant"),
+    ("void quarot::had_quant_kront<24, false, 512, false>(__half const*, long)", "had_quant"),
+    ("void quarot::had_quant_kront<24, true, 512, false>(__half const*, long)", "had_quant"),
+    ("void quarot::had_quant_kront<24, false, 512, true>(__half const*, long)", "swiglu_had_quant"),
+    ("void quarot::had_quant_kront<24, true, 512, true>(__half const*, long)", "swiglu_had_quant"),
     ("void quarot::had_quant_kron<28, false, false, 1024>(__half const*)", "had_quant"),
     ("void quarot::had_quant_kron<24, true, false, 512>(__half const*)", "had_quant"),
     ("void quarot::had_quant_kron<24, false, true, 512>(__half const*)", "swiglu_had_quant"),
